@@ -1,0 +1,151 @@
+"""Seeded synthetic inputs for the KDA mixer core.
+
+This module only draws random numbers and rounds them to the io dtype; it holds none of
+the method's arithmetic.  Both the HIP path and the oracle take their inputs from here.
+
+Workloads (all head_dim 128, short-conv kernel 4, lower bound -5):
+
+* ``tiny_prefill_fp32``   -- 1 sequence x 64 tokens, 2 heads, fp32 io, zero state and ring;
+* ``decode_b256_h32``     -- 256 sequences x 1 token, 32 heads, bf16 io, fp32 state
+  ~ N(0, 0.02) and rings ~ N(0, 1), run as 128 consecutive steps;
+* ``prefill_t4096_h32``   -- 1 sequence x 4096 tokens, 32 heads, bf16 io;
+* ``prefill_2x8192_h96``  -- 2 sequences x 8192 tokens, 96 heads, bf16 io, final states;
+* ``varlen16_h64``        -- 16 sequences with lengths ~ U[512, 16384], 64 heads, bf16 io,
+  initial state ~ N(0, 0.02) and ring ~ N(0, 1), then 32 decode steps.
+
+Distributions: raw q/k/v, decay pre-activation z and output-gate pre-activation ~ N(0, 1);
+raw beta ~ N(0, 1); conv weights ~ U(-0.5, 0.5); dt_bias ~ N(0, 0.1); A_log = log U(1, 16)
+per head; RMSNorm weight = 1 + N(0, 0.02).  N(0, s) means standard deviation s.  Values
+are drawn in fp32 by torch's generator on the requested device and rounded once (round to
+nearest even) to the io dtype.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+HEAD_DIM = 128
+CONV_KERNEL = 4
+LOWER_BOUND = -5.0
+L2_EPS = 1e-6
+RMS_EPS = 1e-5
+
+
+@dataclass
+class Workload:
+    name: str
+    kind: str                      # "prefill" or "decode"
+    io: str                        # "f32" or "bf16"
+    heads: int
+    seqlens: list = field(default_factory=list)   # prefill sequence lengths
+    batch: int = 0                 # decode batch
+    steps: int = 0                 # decode steps
+    init_state: bool = False
+    init_ring: bool = False
+    decode_after: int = 0          # decode steps that continue a prefill
+    seed: int = 0
+
+    @property
+    def total_tokens(self) -> int:
+        return sum(self.seqlens) if self.kind == "prefill" else self.batch * self.steps
+
+
+def _varlen_lengths(seed: int, n: int = 16, lo: int = 512, hi: int = 16384) -> list:
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return [int(x) for x in torch.randint(lo, hi + 1, (n,), generator=g)]
+
+
+WORKLOADS = {
+    "tiny_prefill_fp32": Workload("tiny_prefill_fp32", "prefill", "f32", 2, [64], seed=20260),
+    "decode_b256_h32": Workload("decode_b256_h32", "decode", "bf16", 32, batch=256, steps=128,
+                                init_state=True, init_ring=True, seed=20261),
+    "prefill_t4096_h32": Workload("prefill_t4096_h32", "prefill", "bf16", 32, [4096], seed=20262),
+    "prefill_2x8192_h96": Workload("prefill_2x8192_h96", "prefill", "bf16", 96, [8192, 8192],
+                                   seed=20263),
+    "varlen16_h64": Workload("varlen16_h64", "prefill", "bf16", 64, _varlen_lengths(20264 + 7),
+                             init_state=True, init_ring=True, decode_after=32, seed=20264),
+}
+
+
+def torch_io_dtype(io: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[io]
+
+
+def gen(seed: int, device="cpu") -> torch.Generator:
+    return torch.Generator(device=device).manual_seed(int(seed))
+
+
+def layer_params(H: int, g: torch.Generator, device="cpu", d: int = HEAD_DIM,
+                 kconv: int = CONV_KERNEL) -> dict:
+    """conv_w [3*H*d, kconv] ~ U(-0.5, 0.5); dt_bias [H*d] ~ N(0, 0.1);
+    A_log [H] = log U(1, 16); norm_w [d] = 1 + N(0, 0.02); all fp32."""
+    Hd = H * d
+    conv_w = torch.rand(3 * Hd, kconv, generator=g, device=device) - 0.5
+    dt_bias = torch.randn(Hd, generator=g, device=device) * 0.1
+    A_log = torch.log(torch.rand(H, generator=g, device=device) * 15.0 + 1.0)
+    norm_w = 1.0 + 0.02 * torch.randn(d, generator=g, device=device)
+    return dict(num_heads=H, head_dim=d, conv_kernel=kconv, lower_bound=LOWER_BOUND,
+                l2_eps=L2_EPS, rms_eps=RMS_EPS, conv_w=conv_w.contiguous(),
+                dt_bias=dt_bias.contiguous(), A_log=A_log.contiguous(), norm_w=norm_w.contiguous())
+
+
+def activations(T: int, H: int, io: str, g: torch.Generator, device="cpu", d: int = HEAD_DIM,
+                lead=()) -> dict:
+    """Raw q, k, v, z, gate [*lead, T, H*d] and raw beta [*lead, T, H] ~ N(0, 1) in io dtype."""
+    dt = torch_io_dtype(io)
+    shp = tuple(lead) + (T, H * d)
+    out = {}
+    for name in ("q", "k", "v", "z", "gate"):
+        out[name] = torch.randn(shp, generator=g, device=device).to(dt)
+    out["beta"] = torch.randn(tuple(lead) + (T, H), generator=g, device=device).to(dt)
+    return out
+
+
+def initial_state(N: int, H: int, g: torch.Generator, device="cpu", d: int = HEAD_DIM,
+                  std: float = 0.02) -> torch.Tensor:
+    return torch.randn(N, H, d, d, generator=g, device=device) * std
+
+
+def initial_ring(N: int, H: int, g: torch.Generator, device="cpu", d: int = HEAD_DIM,
+                 kconv: int = CONV_KERNEL, std: float = 1.0) -> torch.Tensor:
+    return torch.randn(N, 3 * H * d, kconv - 1, generator=g, device=device) * std
+
+
+def cu_seqlens(seqlens) -> torch.Tensor:
+    cu = [0]
+    for L in seqlens:
+        cu.append(cu[-1] + int(L))
+    return torch.tensor(cu, dtype=torch.int32)
+
+
+def make_prefill(seqlens, H: int, io: str, seed: int, device="cpu", init_state=False,
+                 init_ring=False, d: int = HEAD_DIM) -> dict:
+    """A packed varlen prefill problem.  Draw order: layer params, activations, state, ring."""
+    g = gen(seed, device)
+    p = layer_params(H, g, device, d)
+    T = int(sum(seqlens))
+    a = activations(T, H, io, g, device, d)
+    N = len(seqlens)
+    st = initial_state(N, H, g, device, d) if init_state else None
+    rg = initial_ring(N, H, g, device, d) if init_ring else None
+    return dict(layer=p, io=io, seqlens=list(map(int, seqlens)), cu_seqlens=cu_seqlens(seqlens),
+                state_in=st, ring_in=rg, **a)
+
+
+def make_decode(B: int, H: int, io: str, steps: int, seed: int, device="cpu",
+                d: int = HEAD_DIM) -> dict:
+    """A decode problem: params, per-step activations [steps, B, ...], state, ring."""
+    g = gen(seed, device)
+    p = layer_params(H, g, device, d)
+    a = activations(B, H, io, g, device, d, lead=(steps,))
+    st = initial_state(B, H, g, device, d)
+    rg = initial_ring(B, H, g, device, d)
+    return dict(layer=p, io=io, batch=B, steps=steps, state=st, ring=rg, **a)
+
+
+def make_workload(name: str, device="cpu") -> dict:
+    w = WORKLOADS[name]
+    if w.kind == "decode":
+        return make_decode(w.batch, w.heads, w.io, w.steps, w.seed, device)
+    return make_prefill(w.seqlens, w.heads, w.io, w.seed, device, w.init_state, w.init_ring)
