@@ -1,0 +1,178 @@
+// C ABI of libkda.so: argument validation, then one launch per call on the caller's
+// stream.  Nothing here allocates device memory or synchronises.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status fail(kda_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+kda_status ok() {
+  g_last_error.clear();
+  return KDA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kda_status check_layer(const kda_layer* L, bool chunked) {
+  if (!L) return fail(KDA_ERR_INVALID_ARG, "layer is NULL");
+  if (L->num_heads <= 0) return fail(KDA_ERR_INVALID_ARG, "num_heads must be positive");
+  if (L->head_dim != kda::kHeadDimHost)
+    return fail(KDA_ERR_UNSUPPORTED, "head_dim %d is not supported (only 128)", L->head_dim);
+  if (L->conv_kernel != 4)
+    return fail(KDA_ERR_UNSUPPORTED, "conv_kernel %d is not supported (only 4)", L->conv_kernel);
+  if (!L->conv_w || !L->dt_bias || !L->A_log || !L->norm_w)
+    return fail(KDA_ERR_INVALID_ARG, "a layer parameter pointer is NULL");
+  if (!(L->l2_eps >= 0.f) || !(L->rms_eps >= 0.f) || !std::isfinite(L->l2_eps) ||
+      !std::isfinite(L->rms_eps))
+    return fail(KDA_ERR_INVALID_ARG, "epsilons must be finite and non-negative");
+  if (!std::isfinite(L->lower_bound) || L->lower_bound > 0.f)
+    return fail(KDA_ERR_INVALID_ARG, "lower_bound must be finite and <= 0");
+  // The chunked kernel forms exp(+-Gcum) over 16-token tiles from a mid-tile reference:
+  // with g >= -5 every factor stays within e^(+-40), far inside fp32 and bf16 range.
+  if (chunked && L->lower_bound < -5.f)
+    return fail(KDA_ERR_UNSUPPORTED, "prefill needs lower_bound >= -5 (16-token tile bound)");
+  return KDA_OK;
+}
+
+kda::LayerParams layer_params(const kda_layer* L) {
+  kda::LayerParams p;
+  p.H = L->num_heads;
+  p.lower_bound = L->lower_bound;
+  p.l2_eps = L->l2_eps;
+  p.rms_eps = L->rms_eps;
+  p.conv_w = L->conv_w;
+  p.dt_bias = L->dt_bias;
+  p.A_log = L->A_log;
+  p.norm_w = L->norm_w;
+  return p;
+}
+
+bool io_ok(kda_dtype io) { return io == KDA_F32 || io == KDA_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+kda_status kda_decode_step(const kda_layer* layer, kda_dtype io, int32_t batch, const void* q,
+                           const void* k, const void* v, const void* z, const void* beta,
+                           const void* gate, float* state, float* ring, void* out,
+                           hipStream_t stream) {
+  kda_status st = check_layer(layer, false);
+  if (st != KDA_OK) return st;
+  if (!io_ok(io)) return fail(KDA_ERR_INVALID_ARG, "unknown io dtype %d", static_cast<int>(io));
+  if (batch < 0) return fail(KDA_ERR_INVALID_ARG, "batch must be >= 0");
+  if (batch == 0) return ok();
+  if (!q || !k || !v || !z || !beta || !gate || !state || !ring || !out)
+    return fail(KDA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned16(state)) return fail(KDA_ERR_INVALID_ARG, "state must be 16-byte aligned");
+  if (static_cast<int64_t>(batch) * layer->num_heads > 0x7fffffffLL)
+    return fail(KDA_ERR_INVALID_ARG, "batch * num_heads exceeds the grid limit");
+  kda::DecodeArgs a;
+  a.L = layer_params(layer);
+  a.batch = batch;
+  a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.gate = gate;
+  a.state = state;
+  a.ring = ring;
+  a.out = out;
+  hipError_t e = kda::launch_decode(a, io, stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t kda_prefill_workspace_bytes(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
+                                   const int32_t* cu_seqlens_host, int64_t total_tokens) {
+  (void)layer; (void)io; (void)num_seqs; (void)cu_seqlens_host; (void)total_tokens;
+  return 0;
+}
+
+kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
+                       const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                       int64_t total_tokens, const void* q, const void* k, const void* v,
+                       const void* z, const void* beta, const void* gate, const float* state_in,
+                       const float* ring_in, void* out, float* state_out, float* ring_out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  kda_status st = check_layer(layer, true);
+  if (st != KDA_OK) return st;
+  if (!io_ok(io)) return fail(KDA_ERR_INVALID_ARG, "unknown io dtype %d", static_cast<int>(io));
+  if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (num_seqs == 0) {
+    if (total_tokens != 0) return fail(KDA_ERR_INVALID_ARG, "no sequences but total_tokens != 0");
+    return ok();
+  }
+  if (!cu_seqlens_dev || !cu_seqlens_host)
+    return fail(KDA_ERR_INVALID_ARG, "cu_seqlens (device and host copies) are required");
+  if (cu_seqlens_host[0] != 0) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
+  for (int32_t n = 0; n < num_seqs; ++n)
+    if (cu_seqlens_host[n + 1] < cu_seqlens_host[n])
+      return fail(KDA_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing (at %d)", n);
+  if (static_cast<int64_t>(cu_seqlens_host[num_seqs]) != total_tokens)
+    return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[num_seqs] = %d != total_tokens = %lld",
+                cu_seqlens_host[num_seqs], static_cast<long long>(total_tokens));
+  if (total_tokens > 0 && (!q || !k || !v || !z || !beta || !gate || !out))
+    return fail(KDA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out)))
+    return fail(KDA_ERR_INVALID_ARG, "state buffers must be 16-byte aligned");
+  const size_t need = kda_prefill_workspace_bytes(layer, io, num_seqs, cu_seqlens_host, total_tokens);
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                workspace_bytes, need);
+  if (static_cast<int64_t>(num_seqs) * layer->num_heads > 0x7fffffffLL)
+    return fail(KDA_ERR_INVALID_ARG, "num_seqs * num_heads exceeds the grid limit");
+
+  // Longest sequences first, so the long serial chains start early.
+  std::vector<int32_t> order(num_seqs);
+  std::iota(order.begin(), order.end(), 0);
+  if (num_seqs <= kda::kMaxOrdered)
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+      return cu_seqlens_host[x + 1] - cu_seqlens_host[x] > cu_seqlens_host[y + 1] - cu_seqlens_host[y];
+    });
+
+  kda::PrefillArgs a;
+  a.L = layer_params(layer);
+  a.num_seqs = num_seqs;
+  a.cu_seqlens = cu_seqlens_dev;
+  a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.gate = gate;
+  a.state_in = state_in;
+  a.ring_in = ring_in;
+  a.out = out;
+  a.state_out = state_out;
+  a.ring_out = ring_out;
+  hipError_t e = kda::launch_prefill(a, io, order.data(), stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,179 @@
+// Recurrent decode step of the KDA core: one token per sequence, fp32 state streamed
+// through HBM once.
+//
+// Math ("Kimi Delta Attention (KDA) -- analysis & C kernel plan", section "Recurrence",
+// and its "C kernel plan / Decode" outline): S' = Diag(exp(g)) S; u = S'^T k;
+// delta = beta (v - u); S = S' + k delta^T; o = S^T q.  The readout is taken from the
+// same pass: o = S'^T q + delta (k . q), so S is read once and written once.
+//
+// One workgroup of 256 threads per (sequence, head).  Thread t owns value columns
+// 4*(t%32) .. +3 and key rows (t/32) + 8m, m = 0..15: 64 fp32 of state in registers,
+// loaded and stored as float4 so each wave moves two whole 512-byte rows per access.
+// The prologue (conv + ring roll, L2 norms, gate, beta) runs while those loads are in
+// flight; the epilogue is the sigmoid-gated RMSNorm over the head's 128 outputs.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <typename IO>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+  const int H = a.L.H;
+  const int unit = blockIdx.x;  // (b, h), h fastest
+  const int b = unit / H;
+  const int h = unit - b * H;
+  const int t = threadIdx.x;
+  const int wave = t >> 6;
+  const int cg = t & 31;
+  const int rg = t >> 5;
+  const int64_t Hd = static_cast<int64_t>(H) * kHeadDim;
+
+  __shared__ float a_q[kHeadDim], a_k[kHeadDim], a_v[kHeadDim], eg[kHeadDim], sg[kHeadDim];
+  __shared__ float dlt[kHeadDim];
+  __shared__ float part[2][3];
+  __shared__ float red[4][2][kHeadDim];
+  __shared__ float part2[2];
+
+  // 1. state loads first, so their latency overlaps the prologue
+  float4* Sg = reinterpret_cast<float4*>(a.state + static_cast<int64_t>(unit) * kHeadDim * kHeadDim);
+  float4 s[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) s[m] = Sg[(rg + 8 * m) * (kHeadDim / 4) + cg];
+
+  // 2. prologue: conv + SiLU with the ring as history, ring roll, gate, beta
+  const IO* x_q = static_cast<const IO*>(a.q);
+  const IO* x_k = static_cast<const IO*>(a.k);
+  const IO* x_v = static_cast<const IO*>(a.v);
+  const IO* x_z = static_cast<const IO*>(a.z);
+  const IO* x_g = static_cast<const IO*>(a.gate);
+  const IO* x_b = static_cast<const IO*>(a.beta);
+  const int i = t & (kHeadDim - 1);
+  const int64_t c = static_cast<int64_t>(h) * kHeadDim + i;
+  const int64_t xrow = static_cast<int64_t>(b) * Hd;
+  float* ring = a.ring + static_cast<int64_t>(b) * 3 * Hd * kRingTaps;
+  const float beta = sigmoidf_(load_io(x_b, static_cast<int64_t>(b) * H + h));
+
+  if (t < kHeadDim) {
+    float sums[3];
+    float act[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {  // planes q, k
+      const float x = load_io(p == 0 ? x_q : x_k, xrow + c);
+      const float* w = a.L.conv_w + (p * Hd + c) * kConvTaps;
+      float* r = ring + (p * Hd + c) * kRingTaps;
+      const float h0 = r[0], h1 = r[1], h2 = r[2];
+      const float y = w[3] * x + w[0] * h0 + w[1] * h1 + w[2] * h2;
+      r[0] = h1;
+      r[1] = h2;
+      r[2] = x;
+      act[p] = siluf_(y);
+    }
+    a_q[i] = act[0];
+    a_k[i] = act[1];
+    sums[0] = wave_sum(act[0] * act[0]);
+    sums[1] = wave_sum(act[1] * act[1]);
+    sums[2] = wave_sum(act[0] * act[1]);
+    if ((t & 63) == 0) {
+      part[wave][0] = sums[0];
+      part[wave][1] = sums[1];
+      part[wave][2] = sums[2];
+    }
+  } else {
+    const float x = load_io(x_v, xrow + c);
+    const float* w = a.L.conv_w + (2 * Hd + c) * kConvTaps;
+    float* r = ring + (2 * Hd + c) * kRingTaps;
+    const float h0 = r[0], h1 = r[1], h2 = r[2];
+    const float y = w[3] * x + w[0] * h0 + w[1] * h1 + w[2] * h2;
+    r[0] = h1;
+    r[1] = h2;
+    r[2] = x;
+    a_v[i] = siluf_(y);
+    const float g = kda_gate(load_io(x_z, xrow + c), a.L.dt_bias[c], expf(a.L.A_log[h]),
+                             a.L.lower_bound);
+    eg[i] = expf(g);
+    sg[i] = sigmoidf_(load_io(x_g, xrow + c));
+  }
+  __syncthreads();
+
+  // 3. decay the state and form both GEMVs, u = S'^T k-hat and w = S'^T q-hat
+  const float rq = 1.0f / sqrtf(part[0][0] + part[1][0] + a.L.l2_eps) * 0.08838834764831845f;
+  const float rk = 1.0f / sqrtf(part[0][1] + part[1][1] + a.L.l2_eps);
+  const float qk = (part[0][2] + part[1][2]) * rq * rk;  // k-hat . q-hat
+  float kh[16];
+  float u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f, w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int r = rg + 8 * m;
+    kh[m] = a_k[r] * rk;
+    const float qh = a_q[r] * rq;
+    const float e = eg[r];
+    s[m].x *= e;
+    s[m].y *= e;
+    s[m].z *= e;
+    s[m].w *= e;
+    u0 += s[m].x * kh[m];
+    u1 += s[m].y * kh[m];
+    u2 += s[m].z * kh[m];
+    u3 += s[m].w * kh[m];
+    w0 += s[m].x * qh;
+    w1 += s[m].y * qh;
+    w2 += s[m].z * qh;
+    w3 += s[m].w * qh;
+  }
+  u0 += __shfl_xor(u0, 32, 64);
+  u1 += __shfl_xor(u1, 32, 64);
+  u2 += __shfl_xor(u2, 32, 64);
+  u3 += __shfl_xor(u3, 32, 64);
+  w0 += __shfl_xor(w0, 32, 64);
+  w1 += __shfl_xor(w1, 32, 64);
+  w2 += __shfl_xor(w2, 32, 64);
+  w3 += __shfl_xor(w3, 32, 64);
+  if ((t & 32) == 0) {
+    *reinterpret_cast<float4*>(&red[wave][0][cg * 4]) = make_float4(u0, u1, u2, u3);
+    *reinterpret_cast<float4*>(&red[wave][1][cg * 4]) = make_float4(w0, w1, w2, w3);
+  }
+  __syncthreads();
+
+  // 4. delta and the readout for column j = t
+  float o = 0.f;
+  if (t < kHeadDim) {
+    const int j = t;
+    const float uj = red[0][0][j] + red[1][0][j] + red[2][0][j] + red[3][0][j];
+    const float wj = red[0][1][j] + red[1][1][j] + red[2][1][j] + red[3][1][j];
+    const float d = beta * (a_v[j] - uj);
+    dlt[j] = d;
+    o = wj + qk * d;
+    const float so = wave_sum(o * o);
+    if ((t & 63) == 0) part2[wave] = so;
+  }
+  __syncthreads();
+
+  // 5. rank-1 update and the single state write; gated RMSNorm on the output
+  const float4 d4 = *reinterpret_cast<const float4*>(&dlt[cg * 4]);
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    s[m].x += kh[m] * d4.x;
+    s[m].y += kh[m] * d4.y;
+    s[m].z += kh[m] * d4.z;
+    s[m].w += kh[m] * d4.w;
+    Sg[(rg + 8 * m) * (kHeadDim / 4) + cg] = s[m];
+  }
+  if (t < kHeadDim) {
+    const int j = t;
+    const float r = 1.0f / sqrtf((part2[0] + part2[1]) * (1.0f / kHeadDim) + a.L.rms_eps);
+    store_io(static_cast<IO*>(a.out), xrow + static_cast<int64_t>(h) * kHeadDim + j,
+             a.L.norm_w[j] * o * r * sg[j]);
+  }
+}
+
+hipError_t launch_decode(const DecodeArgs& a, kda_dtype io, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(a.batch) * static_cast<unsigned>(a.L.H));
+  const dim3 block(256);
+  if (io == KDA_F32)
+    hipLaunchKernelGGL(decode_kernel<float>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_kernel<bf16_t>, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace kda

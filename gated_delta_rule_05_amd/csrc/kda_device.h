@@ -1,0 +1,75 @@
+// Device-side helpers shared by the KDA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kHeadDim = 128;
+constexpr int kConvTaps = 4;
+constexpr int kRingTaps = kConvTaps - 1;
+
+// bf16 travels as its 16-bit pattern: the top half of an IEEE binary32.
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename IO>
+__device__ __forceinline__ float load_io(const IO* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_io<float>(const float* p, int64_t i) {
+  return p[i];
+}
+template <>
+__device__ __forceinline__ float load_io<bf16_t>(const bf16_t* p, int64_t i) {
+  return bf16_to_f32(p[i].bits);
+}
+
+template <typename IO>
+__device__ __forceinline__ void store_io(IO* p, int64_t i, float x);
+template <>
+__device__ __forceinline__ void store_io<float>(float* p, int64_t i, float x) {
+  p[i] = x;
+}
+template <>
+__device__ __forceinline__ void store_io<bf16_t>(bf16_t* p, int64_t i, float x) {
+  p[i].bits = f32_to_bf16(x);
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ __forceinline__ float siluf_(float x) { return x / (1.0f + expf(-x)); }
+
+// Lower-bounded per-channel log decay: lb * sigmoid(exp(A_log) * (z + dt_bias)).
+__device__ __forceinline__ float kda_gate(float z, float dt_bias, float a_scale, float lb) {
+  return lb * sigmoidf_(a_scale * (z + dt_bias));
+}
+
+// Sum over the 64 lanes of a wave; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// Sum over aligned groups of `W` consecutive lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int m = W / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+}  // namespace kda

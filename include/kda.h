@@ -1,0 +1,144 @@
+/*
+ * kda.h -- C ABI of libkda.so, the MI355X (gfx950) Kimi Delta Attention (KDA) mixer core.
+ *
+ * The library takes one layer's already-projected activations and runs, per (sequence,
+ * head): the short causal depthwise conv (kernel 4, no bias) with SiLU on q, k and v;
+ * L2 normalisation of q and k (eps l2_eps) and the head_dim^-1/2 scale on q; the
+ * lower-bounded per-channel log decay g = lower_bound * sigmoid(exp(A_log) * (z + dt_bias));
+ * beta = sigmoid(raw beta); the gated delta-rule recurrence; and the sigmoid-gated RMSNorm
+ * on the output.  Sources, by page and section:
+ *   - docs.rs "ferrox_models::kda" module page: conv (depthwise causal Conv1d, padding
+ *     kernel_size-1, no bias), q/k L2 norm with eps 1e-6 then q * head_dim^-1/2, the
+ *     per-channel gate and the sigmoid output gate;
+ *   - "Kimi Delta Attention (KDA) -- analysis & C kernel plan", sections "The KDA layer,
+ *     precisely" and "Recurrence": S' = Diag(exp(g_t)) S_{t-1};
+ *     S_t = S' + beta_t k_t (v_t - S'^T k_t)^T; o_t = S_t^T q_t;
+ *   - OpenModelAtlas "Kimi K3 - Retention gate": formula and gate.py excerpt for g;
+ *     "Why": lower bound -5 keeps a 16-token tile's rescale below e^80;
+ *   - docs.rs "memra_engine::kda": fused conv weights and ring (plane offset
+ *     plane * H * d), token-major channel c = h * d + i, head_dim 128 only, stateless /
+ *     stateful prefill and the T = 1 decode step.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is device memory owned by the caller, unless named *_host.
+ *     The library allocates nothing, keeps no pointer after returning, and never
+ *     synchronises: work is enqueued on `stream` and completes asynchronously.
+ *   - Errors are reported by status code only, and arguments are checked before any
+ *     work is enqueued: on a non-OK return nothing has been written.  Faults inside a
+ *     kernel surface at the caller's next synchronisation.  kda_last_error() returns a
+ *     thread-local description of the last failure.
+ *   - Activations are token-major: q, k, v, z (decay pre-activation) and gate (output
+ *     gate pre-activation) are [T][H * d] with channel c = h * d + i; raw beta is [T][H].
+ *     They are all of the io dtype; out has the io dtype and the [T][H * d] layout.
+ *   - The recurrent state is fp32 [N][H][d_k = d][d_v = d], row-major with the key index
+ *     (the decayed axis) first.
+ *   - The conv ring is fp32 [N][3 * H * d][kernel - 1]: planes q, k, v (plane offset
+ *     plane * H * d), then channel, then taps oldest first; it holds the most recent
+ *     kernel - 1 raw (pre-conv) inputs of each channel.
+ *   - conv_w is fp32 [3 * H * d][kernel], same plane order; tap kernel - 1 multiplies the
+ *     current token, tap 0 the oldest.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = 1, /* null or misaligned pointer, bad size, inconsistent cu_seqlens */
+  KDA_ERR_UNSUPPORTED = 2, /* head_dim != 128, conv kernel != 4, lower bound outside [-5, 0] */
+  KDA_ERR_WORKSPACE = 3,   /* workspace smaller than kda_prefill_workspace_bytes() */
+  KDA_ERR_HIP = 4          /* the HIP runtime refused a launch */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/*
+ * One layer's shape and parameters (device pointers, fp32):
+ *   conv_w  [3 * H * d][conv_kernel]   fused short-conv weights, planes q, k, v
+ *   dt_bias [H * d]                    added to z before the gate
+ *   A_log   [H]                        per-head log scale of the gate
+ *   norm_w  [d]                        gated-RMSNorm weight, shared by all heads
+ * lower_bound is the gate's lower bound (-5 in the pages' models); l2_eps the q/k L2
+ * epsilon (1e-6); rms_eps the output RMSNorm epsilon.
+ */
+typedef struct kda_layer {
+  int32_t num_heads;
+  int32_t head_dim;    /* must be 128 */
+  int32_t conv_kernel; /* must be 4 */
+  float lower_bound;
+  float l2_eps;
+  float rms_eps;
+  const float* conv_w;
+  const float* dt_bias;
+  const float* A_log;
+  const float* norm_w;
+} kda_layer;
+
+/*
+ * Bytes of device workspace kda_prefill() needs for this problem (may be 0).  The
+ * workspace holds per-chunk partial results when a head's value columns are split across
+ * several workgroups.  Returns 0 also for invalid arguments (kda_prefill reports those).
+ */
+size_t kda_prefill_workspace_bytes(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
+                                   const int32_t* cu_seqlens_host, int64_t total_tokens);
+
+/*
+ * Chunked prefill over num_seqs packed sequences (stateless when state_in / ring_in are
+ * NULL, stateful otherwise; memra_engine::kda kda_attn / kda_attn_prime).
+ *   cu_seqlens_dev / cu_seqlens_host  int32 [num_seqs + 1], the same offsets in device and
+ *       host memory, non-decreasing, starting at 0 and ending at total_tokens.  Empty
+ *       sequences are allowed (their state and ring pass through unchanged).
+ *   q, k, v, z, gate  [total_tokens][H * d] io;  beta [total_tokens][H] io (raw, pre-sigmoid)
+ *   state_in  fp32 [num_seqs][H][d][d] or NULL (zero initial state)
+ *   ring_in   fp32 [num_seqs][3 * H * d][kernel - 1] or NULL (zero history)
+ *   out       [total_tokens][H * d] io
+ *   state_out fp32 [num_seqs][H][d][d] or NULL (not written); may equal state_in
+ *   ring_out  fp32 [num_seqs][3 * H * d][kernel - 1] or NULL; may equal ring_in
+ *   workspace device buffer of at least kda_prefill_workspace_bytes() bytes (may be NULL
+ *             when that is 0).
+ * Partial overlap between inputs and outputs is invalid.  State pointers must be 16-byte
+ * aligned.
+ */
+kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
+                       const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                       int64_t total_tokens, const void* q, const void* k, const void* v,
+                       const void* z, const void* beta, const void* gate, const float* state_in,
+                       const float* ring_in, void* out, float* state_out, float* ring_out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One decode token for each of `batch` sequences (memra_engine::kda kda_attn_decode: the
+ * same math as a one-token prime).  q, k, v, z, gate [batch][H * d] io; beta [batch][H] io.
+ * state fp32 [batch][H][d][d] and ring fp32 [batch][3 * H * d][kernel - 1] are read and
+ * updated in place (the ring shifts by one token).  out [batch][H * d] io.  batch = 0 is a
+ * no-op.  state must be 16-byte aligned.
+ */
+kda_status kda_decode_step(const kda_layer* layer, kda_dtype io, int32_t batch, const void* q,
+                           const void* k, const void* v, const void* z, const void* beta,
+                           const void* gate, float* state, float* ring, void* out,
+                           hipStream_t stream);
+
+/* Short name of a status code. */
+const char* kda_status_string(kda_status status);
+
+/* Thread-local description of the calling thread's last non-OK status ("" if none). */
+const char* kda_last_error(void);
+
+/* KDA_ABI_VERSION of the loaded library. */
+int32_t kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

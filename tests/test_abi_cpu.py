@@ -1,0 +1,99 @@
+"""The C ABI on the CPU: libkda.so loads, exports every function include/kda.h declares,
+and rejects bad arguments before touching the GPU (no compute is launched here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def _lib():
+    import gated_delta_rule_05_amd as kda
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built (run __graft_entry__.build())")
+    return kda, kda.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert names == sorted(["kda_prefill_workspace_bytes", "kda_prefill", "kda_decode_step",
+                            "kda_status_string", "kda_last_error", "kda_abi_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    kda, lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(kda.EXPORTED) == set(declared_functions())
+    assert lib.kda_abi_version() == kda.ABI_VERSION
+
+
+def test_status_strings():
+    _, lib = _lib()
+    for code, name in enumerate(["KDA_OK", "KDA_ERR_INVALID_ARG", "KDA_ERR_UNSUPPORTED",
+                                 "KDA_ERR_WORKSPACE", "KDA_ERR_HIP"]):
+        assert lib.kda_status_string(code).decode() == name
+
+
+FAKE = 0x10000  # a non-null device address that validation never dereferences
+
+
+def _layer(kda, H=2, head_dim=128, conv_kernel=4, lb=-5.0, null_param=False):
+    p = 0 if null_param else FAKE
+    return kda._binding.KdaLayerC(H, head_dim, conv_kernel, lb, 1e-6, 1e-5, p, FAKE, FAKE, FAKE)
+
+
+def _decode(lib, layer, batch=1, state=FAKE, q=FAKE):
+    return lib.kda_decode_step(ctypes.byref(layer), 1, batch, q, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               state, FAKE, FAKE, None)
+
+
+def test_decode_validation():
+    kda, lib = _lib()
+    assert _decode(lib, _layer(kda, head_dim=64)) == 2
+    assert b"head_dim" in lib.kda_last_error()
+    assert _decode(lib, _layer(kda, conv_kernel=3)) == 2
+    assert _decode(lib, _layer(kda, H=0)) == 1
+    assert _decode(lib, _layer(kda, null_param=True)) == 1
+    assert _decode(lib, _layer(kda), q=0) == 1
+    assert _decode(lib, _layer(kda), state=FAKE + 4) == 1  # misaligned state
+    assert _decode(lib, _layer(kda), batch=-1) == 1
+    assert _decode(lib, _layer(kda), batch=0) == 0  # no-op, nothing launched
+    assert lib.kda_last_error() == b""
+    assert lib.kda_decode_step(ctypes.byref(_layer(kda)), 7, 1, *([FAKE] * 9), None) == 1
+
+
+def _prefill(lib, layer, cu, total, ws_bytes=0, lb_ok=True):
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    return lib.kda_prefill(ctypes.byref(layer), 1, len(cu) - 1, FAKE, cu.ctypes.data, total,
+                           *([FAKE] * 6), None, None, FAKE, None, None, None, ws_bytes, None)
+
+
+def test_prefill_validation():
+    kda, lib = _lib()
+    L = _layer(kda)
+    assert _prefill(lib, L, [0, 5, 3], 3) == 1          # decreasing
+    assert _prefill(lib, L, [1, 5], 5) == 1             # does not start at 0
+    assert _prefill(lib, L, [0, 5, 9], 8) == 1          # total mismatch
+    assert _prefill(lib, _layer(kda, lb=-6.0), [0, 4], 4) == 2  # beyond the tile bound
+    assert _prefill(lib, _layer(kda, lb=1.0), [0, 4], 4) == 1
+    assert _prefill(lib, _layer(kda, head_dim=256), [0, 4], 4) == 2
+    # zero sequences is a no-op
+    assert lib.kda_prefill(ctypes.byref(L), 1, 0, None, None, 0, *([None] * 11), None, 0, None) == 0
+
+
+def test_workspace_query_is_host_only():
+    kda, lib = _lib()
+    cu = np.array([0, 100, 300], dtype=np.int32)
+    n = lib.kda_prefill_workspace_bytes(ctypes.byref(_layer(kda)), 1, 2, cu.ctypes.data, 300)
+    assert n >= 0
