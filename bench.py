@@ -1,0 +1,346 @@
+"""Benchmark of the KDA mixer core on one MI355X.
+
+Default workload: the batched decode step, 256 sequences x 32 heads x head_dim 128, bf16
+activations, fp32 state and conv rings, fresh activations for each of 128 consecutive
+steps (all resident in HBM before timing).  One benchmark step = one kda_decode_step
+launch over the whole batch.  Printed as one JSON line with:
+
+* value      -- decode tokens/s per layer (256 x steps / time);
+* roofline   -- the decode kernel against HBM: algorithmic bytes per launch / average
+                launch duration (HIP events on the launch stream) vs 8 TB/s; `traffic` is
+                the HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE +
+                WRITE_SIZE, scaled by a copy-kernel calibration) when the stored
+                measurement matches the current kernel source, else null;
+* cpu_baseline -- the fp64 oracle timed on the host cores on a bounded sample of the
+                same workload;
+* prefill    -- the chunked prefill on the 1 x 4096 x 32-head and 2 x 8192 x 96-head
+                workloads: tokens/s, fraction of HBM and of dense bf16 MFMA peak.
+
+`--summarize-pmc DIR` turns rocprofv3 counter output into profiles/ summaries.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+D = 128
+
+# Algorithmic HBM bytes per (token, head) of the decode step, bf16 io: fp32 state read and
+# written once (2 x 128 x 128 x 4), fp32 ring of 3 planes x 128 channels x 3 taps read and
+# written (2 x 4608), q/k/v/z/gate in (5 x 256), raw beta in (2), out (256).
+DECODE_BYTES_PER_TOKEN_HEAD = 2 * D * D * 4 + 2 * 3 * D * 3 * 4 + 5 * D * 2 + 2 + D * 2
+# Prefill, bf16 io: q/k/v/z/gate in, beta in, out; state/ring in and out are added per sequence.
+PREFILL_BYTES_PER_TOKEN_HEAD = 5 * D * 2 + 2 + D * 2
+# Algorithmic prefill flops per (token, head) at chunk 64, the same count for every
+# prefill workload whatever chunk the kernel uses: 6 d^2 + 5 C d + C^2 / 3.
+PREFILL_FLOPS_PER_TOKEN_HEAD = 6 * D * D + 5 * 64 * D + 64 * 64 // 3
+METRIC = "KDA tokens/s per layer (chunked prefill, decode); % of MFMA / HBM roofline"
+DECODE_KERNEL = "decode_kernel"
+PREFILL_KERNEL = "prefill_kernel"
+
+
+def kernel_source_hash(name: str) -> str:
+    """Hash of the sources a kernel is built from, to tell whether stored counters are stale."""
+    files = {"decode": ["kda_decode.hip", "kda_device.h", "kda_internal.h"],
+             "prefill": ["kda_prefill.hip", "kda_device.h", "kda_internal.h"]}[name]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "gated_delta_rule_05_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_cores() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+# --------------------------------------------------------------------------- decode
+
+def bench_decode(steps: int, warmup: int, calibrate_copy: bool):
+    import torch
+
+    import gated_delta_rule_05_amd as kda
+    import synthetic
+
+    w = synthetic.WORKLOADS["decode_b256_h32"]
+    dev = "cuda:0"
+    dec = synthetic.make_workload(w.name, device=dev)
+    layer = kda.Layer(**dec["layer"])
+    B, H = w.batch, w.heads
+    state, ring = dec["state"], dec["ring"]
+    out = torch.empty((B, H * D), dtype=torch.bfloat16, device=dev)
+    acts = [(dec["q"][s], dec["k"][s], dec["v"][s], dec["z"][s], dec["beta"][s], dec["gate"][s])
+            for s in range(w.steps)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        q, k, v, z, b, g = acts[i % w.steps]
+        kda.decode_step(layer, q, k, v, z, b, g, state, ring, out=out, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    if calibrate_copy:
+        copy_calibration()
+    res = dict(B=B, H=H, ms_total=ms, ms_per_step=ms / steps,
+               finite=bool(torch.isfinite(out.float()).all()))
+    return res, dec
+
+
+def copy_calibration(nbytes: int = 1 << 30):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def decode_traffic(steps_hash: str):
+    """Measured HBM bytes per decode launch from the stored counter summary, or None."""
+    p = os.path.join(ROOT, "profiles", "decode_b256_h32_pmc.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        doc = json.load(f)
+    if doc.get("source_hash") != steps_hash:
+        return None
+    return doc.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------------------- prefill
+
+def bench_prefill(name: str, reps: int):
+    import torch
+
+    import gated_delta_rule_05_amd as kda
+    import synthetic
+
+    w = synthetic.WORKLOADS[name]
+    dev = "cuda:0"
+    prob = synthetic.make_workload(name, device=dev)
+    layer = kda.Layer(**prob["layer"])
+    cu_dev = prob["cu_seqlens"].to(dev)
+    T = sum(w.seqlens)
+    N = len(w.seqlens)
+    out = torch.empty((T, w.heads * D), dtype=torch.bfloat16, device=dev)
+    st = torch.empty((N, w.heads, D, D), dtype=torch.float32, device=dev)
+    rg = torch.empty((N, 3 * w.heads * D, 3), dtype=torch.float32, device=dev)
+    flush = torch.empty(768 << 20, dtype=torch.uint8, device=dev)  # larger than the 256 MB MALL
+    stream = torch.cuda.current_stream()
+
+    def run():
+        kda.prefill(layer, prob["q"], prob["k"], prob["v"], prob["z"], prob["beta"], prob["gate"],
+                    cu_dev, prob["cu_seqlens"], state_in=prob["state_in"], ring_in=prob["ring_in"],
+                    out=out, state_out=st, ring_out=rg, stream=stream)
+
+    run()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        flush.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    ms = times[len(times) // 2]
+    H = w.heads
+    nbytes = (PREFILL_BYTES_PER_TOKEN_HEAD * T * H + N * H * D * D * 4 * (2 if w.init_state else 1)
+              + N * 3 * H * D * 3 * 4 * (2 if w.init_ring else 1))
+    flops = PREFILL_FLOPS_PER_TOKEN_HEAD * T * H
+    s = ms / 1e3
+    return dict(workload=name, tokens=T, heads=H, ms=ms, tokens_per_s=T / s,
+                hbm_gbs=nbytes / s / 1e9, hbm_frac=nbytes / s / 1e9 / HBM_PEAK_GBS,
+                mfma_tflops=flops / s / 1e12, mfma_frac=flops / s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                algorithmic_bytes=nbytes, algorithmic_flops=flops,
+                finite=bool(torch.isfinite(out.float()).all()))
+
+
+# --------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(dec, target_s: float = 10.0):
+    """The fp64 oracle on a bounded sample of the decode workload: all heads of the first
+    u sequences over all 128 steps (each sequence's 128 steps as one oracle sequence, the
+    same math as 128 decode steps), threaded over (sequence, head) units; u grows until
+    the sample takes about target_s seconds or covers the whole batch."""
+    import numpy as np
+
+    import oracle
+
+    H = dec["layer"]["num_heads"]
+    Hd = H * D
+    steps = dec["q"].shape[0]
+    B = dec["q"].shape[1]
+    p = dec["layer"]
+    lay = oracle.Layer(H, D, p["conv_w"].cpu().numpy(), p["dt_bias"].cpu().numpy(),
+                       p["A_log"].cpu().numpy(), p["norm_w"].cpu().numpy(),
+                       lower_bound=p["lower_bound"], l2_eps=p["l2_eps"], rms_eps=p["rms_eps"])
+    cores = cpu_cores()
+
+    def sample(u):
+        acts = {n: dec[n][:, :u].transpose(0, 1).reshape(u * steps, -1).cpu()
+                for n in ("q", "k", "v", "z", "gate", "beta")}
+        st = dec["state"][:u].double().cpu().numpy()
+        rg = dec["ring"][:u].cpu().numpy()
+        cu = np.arange(u + 1, dtype=np.int64) * steps
+        t = time.perf_counter()
+        oracle.prefill_units(lay, oracle.BF16, cu, acts["q"], acts["k"], acts["v"], acts["z"],
+                             acts["beta"], acts["gate"], st, rg, nthreads=cores)
+        return time.perf_counter() - t
+
+    u = 2
+    el = sample(u)
+    u2 = int(min(B, max(u, u * target_s / max(el, 1e-3))))
+    if u2 > u:
+        u, el = u2, sample(u2)
+    token_heads = u * steps * H
+    return {"value": u * steps / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{u} sequences x {H} heads x {steps} decode steps ({token_heads} "
+                      f"token-heads) in {el:.1f} s"}
+
+
+# --------------------------------------------------------------------------- PMC summaries
+
+def summarize_pmc(fetch_dir: str, write_dir: str, out_name: str = "decode_b256_h32_pmc"):
+    """Reads two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) of
+    `bench.py --calibrate-copy`, scales each by the same counter's reading on the 1 GiB
+    copy kernel, and writes profiles/<out_name>.{md,json}."""
+    import csv
+
+    def read(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r.get("Counter_Name") == counter:
+                        rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        return rows
+
+    fetch = read(fetch_dir, "FETCH_SIZE")
+    write = read(write_dir, "WRITE_SIZE")
+
+    def mean_for(rows, pat):
+        v = [x for k, x in rows if pat in k]
+        return (sum(v) / len(v), len(v)) if v else (None, 0)
+
+    copy_bytes = float(1 << 30)
+    f_dec, nf = mean_for(fetch, DECODE_KERNEL)
+    w_dec, nw = mean_for(write, DECODE_KERNEL)
+    # the 1 GiB device copy: the largest copy dispatch in each run
+    f_copy = max((x for k, x in fetch if "copyBuffer" in k), default=None)
+    w_copy = max((x for k, x in write if "copyBuffer" in k), default=None)
+    f_scale = copy_bytes / (f_copy * 1024) if f_copy else None
+    w_scale = copy_bytes / (w_copy * 1024) if w_copy else None
+    fetched = f_dec * 1024 * f_scale if (f_dec and f_scale) else None
+    written = w_dec * 1024 * w_scale if (w_dec and w_scale) else None
+    alg = DECODE_BYTES_PER_TOKEN_HEAD * 256 * 32
+    total = (fetched + written) if (fetched and written) else None
+    doc = dict(kernel=DECODE_KERNEL, source_hash=kernel_source_hash("decode"),
+               fetch_kib_per_dispatch=f_dec, write_kib_per_dispatch=w_dec, dispatches=[nf, nw],
+               copy_fetch_kib=f_copy, copy_write_kib=w_copy, fetch_scale=f_scale,
+               write_scale=w_scale, fetched_bytes=fetched, written_bytes=written,
+               bytes_per_launch=total, algorithmic_bytes_per_launch=alg,
+               traffic_over_algorithmic=(total / alg) if total else None)
+    with open(os.path.join(ROOT, "profiles", out_name + ".json"), "w") as fh:
+        json.dump(doc, fh, indent=1)
+    print(json.dumps(doc, indent=1))
+
+
+# --------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-reps", type=int, default=10)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the KDA core shards by head or sequence with no exchange; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import gated_delta_rule_05_amd as kda
+    kda.load()  # fails loudly without the HIP library
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+
+    dres, dec = bench_decode(args.steps, args.warmup, args.calibrate_copy)
+    B, H = dres["B"], dres["H"]
+    ms_step = dres["ms_per_step"]
+    bytes_launch = DECODE_BYTES_PER_TOKEN_HEAD * B * H
+    achieved = bytes_launch / (ms_step / 1e3) / 1e9
+    traffic = decode_traffic(kernel_source_hash("decode"))
+    line = {
+        "metric": METRIC,
+        "value": B * args.steps / (dres["ms_total"] / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode_b256_h32", "batch": B, "heads": H, "head_dim": D,
+                   "io": "bf16", "state": "f32", "activation_sets": 128},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": DECODE_KERNEL, "algorithmic_bytes_per_launch": bytes_launch},
+    }
+    if not args.no_prefill:
+        pf = []
+        for name in ("prefill_t4096_h32", "prefill_2x8192_h96"):
+            pf.append(bench_prefill(name, args.prefill_reps))
+            torch.cuda.empty_cache()
+        line["prefill"] = pf
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(dec)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
