@@ -49,6 +49,14 @@ __device__ __forceinline__ void store_io<bf16_t>(bf16_t* p, int64_t i, float x) 
   p[i].bits = f32_to_bf16(x);
 }
 
+// Streaming store of 16 bytes: marked non-temporal so that a buffer written once per
+// launch (the decode state) does not displace reusable lines from the caches.
+__device__ __forceinline__ void store_streaming(float4* p, const float4& v) {
+  typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+  const f32x4_nt x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4_nt*>(p));
+}
+
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 __device__ __forceinline__ float siluf_(float x) { return x / (1.0f + expf(-x)); }
 

@@ -6,26 +6,31 @@
 // Gcum_r = g_1 + ... + g_r per key channel,
 //   A[r][j] = beta_r sum_i k_ri k_ji exp(Gcum_ri - Gcum_ji)      (j < r)
 //   P[r][j] =        sum_i q_ri k_ji exp(Gcum_ri - Gcum_ji)      (j <= r)
-//   (I + A) [W | U~] = Diag(beta) [Ka | V],   Ka_r = k_r exp(Gcum_r)
-//   U = U~ - W S;   O = Qa S + P U,           Qa_r = q_r exp(Gcum_r)
-//   S <- Diag(exp(Gcum_C)) S + Kl^T U,        Kl_r = k_r exp(Gcum_C - Gcum_r)
-// C = 16 here, the tile length of OpenModelAtlas "Kimi K3 - Retention gate" ("Why"):
-// with g >= -5, exp(Gcum_r - Gcum_j) inside the Gram matrices is formed from a reference
-// at the chunk midpoint, so each factor stays within e^(+-40); Ka, Qa and Kl only carry
-// factors <= 1.
+//   T = (I + A)^-1 Diag(beta);  W = T Ka,  U~ = T V,          Ka_r = k_r exp(Gcum_r)
+//   U = U~ - W S;   O = Qa S + P U,                              Qa_r = q_r exp(Gcum_r)
+//   S <- Diag(exp(Gcum_C)) S + Kl^T U,                           Kl_r = k_r exp(Gcum_C - Gcum_r)
+// C = 16, the tile length of OpenModelAtlas "Kimi K3 - Retention gate" ("Why"): with
+// g >= -5, exp(Gcum_r - Gcum_j) inside the Gram tiles is formed from a reference at the
+// chunk midpoint, so each factor stays within e^(+-40); Ka, Qa and Kl carry factors <= 1.
 //
-// Mapping: one workgroup (8 waves) per (sequence, head).  Each wave owns 16 value columns
-// of the fp32 128x128 state, held across the whole sequence in MFMA accumulator tiles
-// (8 key tiles of 16x16).  Those tiles double as the B operand of W.S and
-// Qa.S (the contraction order inside an MFMA is free, so the A operand is read from LDS
-// in the matching key order) and as the accumulator of Kl^T.U.  The bf16 instantiation
-// uses v_mfma_f32_16x16x32_bf16 / 16x16x16_bf16 with fp32 accumulation; the fp32
-// instantiation (fp32 io) the same data flow on v_mfma_f32_16x16x4_f32.
+// Mapping: one workgroup of 8 waves per (sequence, head).  Wave w owns value columns
+// 16w .. 16w+15 of the fp32 128x128 state for the whole sequence, as 8 MFMA accumulator
+// tiles (key rows 16 it + 4 (lane/16) + s, value column 16 w + lane%16).  Those tiles are
+// also the B operand of W.S and Qa.S (the contraction order inside an MFMA is free, so the
+// A operand is supplied in the matching key order) and the accumulator of Kl^T.U.
 //
-// Per chunk: (1) raw q/k/v/z/gate rows -> conv + SiLU with the conv history in registers,
-// gate, Gcum, exp(+-Gcum); (2) q/k row norms; (3) scaled operands; (4) Gram tiles A, P;
-// (5) forward substitution for W and U~ (fp32, one column per thread); (6) the state pass;
-// (7) gated RMSNorm and the output store.
+// Per chunk, with the raw rows of the next chunk already loading:
+//   (1) q/k/v conv + SiLU (history in registers), gate, Gcum, sigmoid(gate), beta
+//   (2) q/k row norms
+//   (3) scaled operands, stored once in MFMA-ready form (bf16 hi/lo pairs)
+//   (4) Gram tiles A and P (waves 0 and 1)
+//   (5) every wave: T by elimination across lanes (DPP broadcasts); W^T = Ka^T T^T lands directly in the
+//       A-operand layout of W.S; U~ = T V for its own value tile; the state pass
+//   (6) sigmoid-gated RMSNorm of each output row and the store
+// Precision (bf16 io): bf16 MFMA, fp32 accumulation; the operands of the Gram tiles,
+// U~ = T V, Qa.S, P.U and Kl^T.U are split into bf16 hi + lo (three MFMAs, about 16
+// significant bits); W and W.S use one bf16 rounding.  fp32 io runs the same data flow on
+// v_mfma_f32_16x16x4_f32.
 #include <type_traits>
 
 #include "kda_device.h"
@@ -35,11 +40,11 @@ namespace kda {
 
 namespace {
 
-constexpr int C = 16;          // chunk = exponent tile
-constexpr int LDP = 132;       // padded row stride of [16][128] LDS arrays
-constexpr int KLP = 20;        // padded row stride of the transposed Kl array
-constexpr int NWAVES = 8;      // one 16-column value tile of the state per wave
+constexpr int C = 16;        // chunk = exponent tile
+constexpr int NWAVES = 8;    // one 16-column value tile of the state per wave
 constexpr int NTHREADS = 64 * NWAVES;
+constexpr int LDP = 132;     // row stride (floats) of fp32 [16][128] arrays
+constexpr int AP = 20;       // row stride (floats) of the A tile
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -49,63 +54,64 @@ struct SeqOrder {
   int32_t idx[kMaxOrdered];
 };
 
-struct Smem {
-  float qa[C][LDP];   // silu(conv q) -> Qp = q-hat exp(Gcum - Gref)
-  float ka[C][LDP];   // silu(conv k) -> Kp = k-hat exp(Gcum - Gref)
-  float kx[C][LDP];   // Ka = k-hat exp(Gcum) -> W
-  float va[C][LDP];   // silu(conv v) -> U~
-  float ep[C][LDP];   // exp(+Gcum)
-  float em[C][LDP];   // exp(-Gcum) -> Km = k-hat exp(Gref - Gcum)
-  float sg[C][LDP];   // sigmoid(gate)
-  float klt[kHeadDim][KLP];  // Kl^T: k-hat exp(Gcum_C - Gcum), [key][token]
-  float A[C][C + 1];
-  float P[C][C + 1];
-  float erefp[kHeadDim], erefm[kHeadDim], eglast[kHeadDim];
-  float rn[2 * C];    // 1/|q| * d^-1/2 for rows 0..15, 1/|k| for rows 16..31
+// Operand storage: bf16 hi/lo planes, or one fp32 plane for fp32 io.
+template <bool F32>
+struct alignas(16) Ops {
+  using E = typename std::conditional<F32, float, __bf16>::type;
+  static constexpr int NP = F32 ? 1 : 2;
+  static constexpr int OPP = F32 ? 132 : 136;  // row stride of [16][128] operands
+  static constexpr int KTP = F32 ? 20 : 24;    // row stride of [128][16] operands
+  static constexpr int PPP = 20;               // row stride of the P tile
+  E qp[NP][C][OPP];    // Qp = q-hat exp(Gcum - Gref), natural key order
+  E qa[NP][C][OPP];    // Qa = q-hat exp(Gcum), key order of the .S products
+  E kp[NP][C][OPP];    // Kp = k-hat exp(Gcum - Gref)
+  E km[NP][C][OPP];    // Km = k-hat exp(Gref - Gcum)
+  E kat[kHeadDim][KTP];      // Ka^T, hi only
+  E klt[NP][kHeadDim][KTP];  // Kl^T
+  E p[NP][C][PPP];     // P tile (lower incl.)
+};
+
+template <bool F32>
+struct alignas(16) Smem {
+  float aq[C][LDP];    // silu(conv q)
+  float ak[C][LDP];    // silu(conv k)
+  float va[C][LDP];    // silu(conv v) = V
+  float gam[C][LDP];   // Gcum
+  float sg[2][C][LDP];  // sigmoid(gate), double-buffered across chunks
+  Ops<F32> op;
+  float A[C][AP];      // A tile times beta (strict lower), fp32
+  float g7[kHeadDim];  // Gcum at the chunk midpoint (Gram reference)
+  float g15[kHeadDim];  // Gcum at the chunk end
+  float eg15[kHeadDim];  // exp(Gcum at the chunk end)
+  float rn[2 * C];     // 1/|q| * d^-1/2 for rows 0..15, 1/|k| for rows 16..31
   float beta[C];
-  float ss[NWAVES][C];
+  float ss[2][NWAVES][C];
 };
 
-// ---- MFMA operand helpers -------------------------------------------------------------
-// bf16 operands are either rounded once ("hi") or split as x = hi + lo with both parts in
-// bf16; a split product takes three MFMAs (hi.hi + hi.lo + lo.hi), which keeps about 16
-// significant bits.  The split is used where a single rounding would show in the output
-// (Gram tiles, Qa.S, P.U and the state update).
+// exp(x) through the hardware base-2 exponential; relative error ~1e-6 over the ranges
+// used here (|x| <= 80).
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fsigmoid(float x) { return frcp(1.0f + fexp(-x)); }
 
-template <int N>
-struct SplitBf16;
-template <>
-struct SplitBf16<8> {
-  bf16x8_t hi, lo;
-};
-template <>
-struct SplitBf16<4> {
-  bf16x4_t hi, lo;
-};
-
-template <int N>
-__device__ __forceinline__ void split_bf16(const float* x, SplitBf16<N>& r) {
-#pragma unroll
-  for (int s = 0; s < N; ++s) {
-    const __bf16 hi = static_cast<__bf16>(x[s]);
-    r.hi[s] = hi;
-    r.lo[s] = static_cast<__bf16>(x[s] - static_cast<float>(hi));
-  }
+// Cross-lane moves inside a row of 16 lanes (DPP): row_newbcast:n hands every lane of the
+// row the value of its lane n; row_ror:k rotates the row by k lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
 }
-
-__device__ __forceinline__ f32x4_t mma32(const SplitBf16<8>& a, const SplitBf16<8>& b, f32x4_t acc,
-                                         bool split) {
-  if (split) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
-  }
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return dpp<0x150 + N>(x);
 }
-
-__device__ __forceinline__ f32x4_t mma16(const SplitBf16<4>& a, const SplitBf16<4>& b, f32x4_t acc) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, acc, 0, 0, 0);
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, acc, 0, 0, 0);
+// Sum over the 16 lanes of a row, delivered to every lane of the row.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<0x128>(x);
+  x += dpp<0x124>(x);
+  x += dpp<0x122>(x);
+  x += dpp<0x121>(x);
+  return x;
 }
 
 // Hides a value from the optimiser so that address arithmetic is recomputed where it is
@@ -115,77 +121,95 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-__device__ __forceinline__ f32x4_t mma_f32(float a, float b, f32x4_t acc) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+__device__ __forceinline__ void split_store(__bf16* hi, __bf16* lo, float x) {
+  const __bf16 h = static_cast<__bf16>(x);
+  *hi = h;
+  *lo = static_cast<__bf16>(x - static_cast<float>(h));
 }
 
-// acc += X[m][.] . S[.][n] over all 128 keys: X row-major in LDS, times an optional
-// per-key scale; S is the wave's value tile (S[it][s] = key 16 it + 4 (l/16) + s).
-// bf16: the key order inside each 32-key MFMA block is (l/16, s) -> 4 (l/16) + s for
-// s < 4 and 16 + 4 (l/16) + s - 4 otherwise, which matches two consecutive S tiles.
-template <bool F32OPS>
-__device__ __forceinline__ f32x4_t x_times_s(const float (*X)[LDP], const float* scale,
-                                             const f32x4_t* S, const SplitBf16<8>* Sb, bool split,
-                                             int lane, f32x4_t acc) {
-  const int m = lane & 15;
-  const int q = lane >> 4;
-  if constexpr (F32OPS) {
+template <int N, typename V>
+__device__ __forceinline__ void split_vec(const float* x, V& hi, V& lo) {
 #pragma unroll
-    for (int it = 0; it < 8; ++it)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int i = 16 * it + 4 * q + s;
-        float a = X[m][i];
-        if (scale) a *= scale[i];
-        acc = mma_f32(a, S[it][s], acc);
-      }
-  } else {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      float a8[8];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int i0 = 32 * kb + 4 * q + s;
-        a8[s] = X[m][i0];
-        a8[4 + s] = X[m][i0 + 16];
-        if (scale) {
-          a8[s] *= scale[i0];
-          a8[4 + s] *= scale[i0 + 16];
-        }
-      }
-      SplitBf16<8> A;
-      split_bf16<8>(a8, A);
-      acc = mma32(A, Sb[kb], acc, split);
-    }
+  for (int s = 0; s < N; ++s) {
+    const __bf16 h = static_cast<__bf16>(x[s]);
+    hi[s] = h;
+    lo[s] = static_cast<__bf16>(x[s] - static_cast<float>(h));
   }
-  return acc;
 }
 
-// acc += M[m][r] . U[r][n] over the chunk's 16 tokens; M row-major in LDS (row stride
-// ld), U in accumulator layout (token 4 (l/16) + s), always split in bf16.
-template <bool F32OPS>
-__device__ __forceinline__ f32x4_t m_times_u(const float* M, int ld, const f32x4_t& U,
-                                             const SplitBf16<4>& Ub, int lane, f32x4_t acc) {
-  const int m = lane & 15;
-  const int q = lane >> 4;
-  if constexpr (F32OPS) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mma_f32(M[m * ld + 4 * q + s], U[s], acc);
+__device__ __forceinline__ f32x4_t mma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma16(bf16x4_t a, bf16x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma4(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// split products: (ah + al)(bh + bl) ~ ah bh + ah bl + al bh
+__device__ __forceinline__ f32x4_t mma32s(bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl,
+                                          f32x4_t c) {
+  c = mma32(al, bh, c);
+  c = mma32(ah, bl, c);
+  return mma32(ah, bh, c);
+}
+__device__ __forceinline__ f32x4_t mma16s(bf16x4_t ah, bf16x4_t al, bf16x4_t bh, bf16x4_t bl,
+                                          f32x4_t c) {
+  c = mma16(al, bh, c);
+  c = mma16(ah, bl, c);
+  return mma16(ah, bh, c);
+}
+
+template <typename V, typename E>
+__device__ __forceinline__ V ld(const E* p) {
+  return *reinterpret_cast<const V*>(p);
+}
+
+// Stores 8 consecutive operand values at [row][col0..col0+7] of a (hi, lo) plane pair
+// (bf16) or of the single fp32 plane, as 16-byte writes.
+template <bool F32, typename Arr>
+__device__ __forceinline__ void store8(Arr& planes, int row, int col0, const float* x) {
+  if constexpr (F32) {
+    *reinterpret_cast<float4*>(&planes[0][row][col0]) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(&planes[0][row][col0 + 4]) = make_float4(x[4], x[5], x[6], x[7]);
   } else {
-    float a4[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) a4[s] = M[m * ld + 4 * q + s];
-    SplitBf16<4> A;
-    split_bf16<4>(a4, A);
-    acc = mma16(A, Ub, acc);
+    bf16x8_t hi, lo;
+    split_vec<8>(x, hi, lo);
+    *reinterpret_cast<bf16x8_t*>(&planes[0][row][col0]) = hi;
+    *reinterpret_cast<bf16x8_t*>(&planes[1][row][col0]) = lo;
   }
-  return acc;
+}
+
+// Same for a single plane rounded once (no lo part).
+template <bool F32, typename E>
+__device__ __forceinline__ void store8_hi(E* dst, const float* x) {
+  if constexpr (F32) {
+    *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  } else {
+    bf16x8_t hi;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) hi[v] = static_cast<__bf16>(x[v]);
+    *reinterpret_cast<bf16x8_t*>(dst) = hi;
+  }
+}
+
+// One elimination step per row j of the 16x16 unit-lower system: every lane of a 16-lane
+// row takes row j's values from lane j of its own row (DPP broadcast).
+template <int J>
+__device__ __forceinline__ void eliminate(float* tt, const float* arow) {
+  if constexpr (J < C - 1) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) tt[s] -= arow[J] * row_bcast<J>(tt[s]);
+    eliminate<J + 1>(tt, arow);
+  }
 }
 
 template <typename IO>
 __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrder order) {
-  constexpr bool F32OPS = std::is_same<IO, float>::value;
-  __shared__ Smem sm;
+  constexpr bool F32 = std::is_same<IO, float>::value;
+  using OP = Ops<F32>;
+  __shared__ Smem<F32> sm;
 
   const int H = a.L.H;
   const int rank = blockIdx.x / H;
@@ -200,16 +224,14 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
   const int lane = t & 63;
   const int lm = lane & 15;
   const int lq = lane >> 4;
-  // elementwise roles: 0 = q, 1 = k, 2 = v, 3 = z and gate, each over 128 channels
-  const int role = t >> 7;
+  const int role = t >> 7;  // elementwise roles: 0 = q, 1 = k, 2 = v, 3 = z and gate
   const int ch = t & (kHeadDim - 1);
   const int64_t c = static_cast<int64_t>(h) * kHeadDim + ch;
-  const int col = 16 * wave + lm;  // the value column this lane holds in the state pass
+  const int col = 16 * wave + lm;  // value column this lane holds in the state pass
 
   const IO* x_b = static_cast<const IO*>(a.beta);
-  const IO* x_z = static_cast<const IO*>(a.z);
+  const IO* x_p = static_cast<const IO*>(role == 0 ? a.q : role == 1 ? a.k : role == 2 ? a.v : a.z);
   const IO* x_g = static_cast<const IO*>(a.gate);
-  const IO* x_p = static_cast<const IO*>(role == 0 ? a.q : role == 1 ? a.k : a.v);
 
   // conv weights and history of the owned channel (roles 0-2: plane = role)
   float w[4] = {0.f, 0.f, 0.f, 0.f}, hist[3] = {0.f, 0.f, 0.f};
@@ -225,7 +247,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
   const float ascale = expf(a.L.A_log[h]);
   const float lb = a.L.lower_bound;
 
-  // the wave's state tile: S[it] covers keys 16 it + 4 lq + s, value column `col`
+  // the wave's state tile
   f32x4_t S[8];
   const int64_t sbase = (static_cast<int64_t>(n) * H + h) * kHeadDim * kHeadDim;
   if (a.state_in) {
@@ -240,60 +262,72 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
   }
   const float nw = a.L.norm_w[col];
 
-  for (int c0 = 0; c0 < T; c0 += C) {
+  // raw rows of the upcoming chunk, loaded one chunk ahead while the current chunk is
+  // processed; rows past the end of the sequence re-read its last row (always in bounds)
+  // and are masked when used
+  float xa[C], xb[C];
+  float braw = 0.f;
+  auto prefetch = [&](int c0n) {
+    const int Ln = min(C, T - c0n);
+    const IO* p = x_p + (t0 + c0n) * Hd + c;
+#pragma unroll
+    for (int r = 0; r < C; ++r) xa[r] = load_io(p, static_cast<int64_t>(min(r, Ln - 1)) * Hd);
+    if (role == 3) {
+      const IO* pg = x_g + (t0 + c0n) * Hd + c;
+#pragma unroll
+      for (int r = 0; r < C; ++r) xb[r] = load_io(pg, static_cast<int64_t>(min(r, Ln - 1)) * Hd);
+    }
+    if (t < C) braw = load_io(x_b, (t0 + c0n + min(t, Ln - 1)) * H + h);
+  };
+  if (T > 0) prefetch(0);
+
+  const int last_c0 = T > 0 ? ((T - 1) / C) * C : 0;
+  int buf = 0;
+  for (int c0 = 0; c0 < T; c0 += C, buf ^= 1) {
     const int L = min(C, T - c0);
     const int64_t row0 = t0 + c0;
-    __syncthreads();  // the previous chunk is done with every LDS array
+    const float* cur = xa;
+    const float* cur2 = xb;
+    const float bcur = braw;
 
-    // (1) elementwise prologue: conv + SiLU per plane, gate and Gcum, sigmoid(gate), beta.
-    // Rows are walked with pointer increments so that no per-row 64-bit offsets stay live.
+    // (1) elementwise prologue
     if (role < 3) {
-      float(*dst)[LDP] = role == 0 ? sm.qa : role == 1 ? sm.ka : sm.va;
-      const IO* px = x_p + row0 * Hd + c;
+      float(*dst)[LDP] = role == 0 ? sm.aq : role == 1 ? sm.ak : sm.va;
 #pragma unroll
       for (int r = 0; r < C; ++r) {
-        float act = 0.f;
-        if (r < L) {
-          const float x = load_io(px, 0);
-          const float y = w[3] * x + w[0] * hist[0] + w[1] * hist[1] + w[2] * hist[2];
+        const float x = cur[r];
+        const float y = w[3] * x + w[0] * hist[0] + w[1] * hist[1] + w[2] * hist[2];
+        const bool live = r < L;
+        if (live) {
           hist[0] = hist[1];
           hist[1] = hist[2];
           hist[2] = x;
-          act = siluf_(y);
         }
-        px += Hd;
-        dst[r][ch] = act;
+        dst[r][ch] = live ? y * fsigmoid(y) : 0.f;
       }
-      if (role == 0 && t < C) sm.beta[t] = (t < L) ? sigmoidf_(load_io(x_b, (row0 + t) * H + h)) : 0.f;
     } else {
       float G = 0.f;
-      const IO* pz = x_z + row0 * Hd + c;
-      const IO* pg = x_g + row0 * Hd + c;
 #pragma unroll
       for (int r = 0; r < C; ++r) {
-        float sgv = 0.f;
-        if (r < L) {
-          G += kda_gate(load_io(pz, 0), dtb, ascale, lb);
-          sgv = sigmoidf_(load_io(pg, 0));
-        }
-        pz += Hd;
-        pg += Hd;
-        sm.sg[r][ch] = sgv;
-        sm.ep[r][ch] = expf(G);
-        sm.em[r][ch] = expf(-G);
-        if (r == C / 2 - 1) {
-          sm.erefp[ch] = expf(G);
-          sm.erefm[ch] = expf(-G);
-        }
+        const bool live = r < L;
+        G += live ? lb * fsigmoid(ascale * (cur[r] + dtb)) : 0.f;
+        sm.gam[r][ch] = G;
+        sm.sg[buf][r][ch] = live ? fsigmoid(cur2[r]) : 0.f;
+        if (r == C / 2 - 1) sm.g7[ch] = G;
       }
-      sm.eglast[ch] = expf(G);
+      sm.g15[ch] = G;
+      sm.eg15[ch] = fexp(G);
     }
+    if (t < C) sm.beta[t] = (t < L) ? fsigmoid(bcur) : 0.f;
+    // next chunk's raw rows: issued unconditionally (the last chunk re-reads itself) so
+    // that their wait lands at the next iteration's first use
+    prefetch(min(c0 + C, last_c0));
     __syncthreads();
 
     // (2) row norms: 16 threads per (plane, row)
     {
       const int task = t >> 4, part = t & 15;
-      const float(*X)[LDP] = task < C ? sm.qa : sm.ka;
+      const float(*X)[LDP] = task < C ? sm.aq : sm.ak;
       const int r = task & (C - 1);
       float ss = 0.f;
 #pragma unroll
@@ -301,126 +335,261 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
         const float x = X[r][part + 16 * m];
         ss += x * x;
       }
-      ss = group_sum<16>(ss);
+      ss = row_sum16(ss);
       if (part == 0)
         sm.rn[task] = (1.0f / sqrtf(ss + a.L.l2_eps)) * (task < C ? 0.08838834764831845f : 1.0f);
     }
     __syncthreads();
 
-    // (3) scaled operands.  q owners: Qp over qa.  k owners: Kp over ka, Km over em, Kl^T
-    // and Ka = k-hat exp(Gcum) for the forward substitution.
-    if (role == 0) {
-      const float erm = sm.erefm[ch];
+    // (3) scaled operands, written once in MFMA-ready form, by 8-channel work items:
+    // threads 0..255 take (row, 8 channels) of Qp, Kp, Km; threads 256..511 take
+    // (row, one lane group) of Qa in the key order of the .S products, and
+    // (channel, 8 rows) of Ka^T and Kl^T
+    {
+      if (t < 256) {
+        const int r = t >> 4, c8 = 8 * (t & 15);
+        float q8[8], k8[8], d8[8];
 #pragma unroll
-      for (int r = 0; r < C; ++r) sm.qa[r][ch] = sm.qa[r][ch] * sm.rn[r] * (sm.ep[r][ch] * erm);
-    } else if (role == 1) {
-      const float erp = sm.erefp[ch], erm = sm.erefm[ch], egl = sm.eglast[ch];
+        for (int v = 0; v < 8; v += 4) {
+          const float4 qv = *reinterpret_cast<const float4*>(&sm.aq[r][c8 + v]);
+          const float4 kv = *reinterpret_cast<const float4*>(&sm.ak[r][c8 + v]);
+          const float4 gv = *reinterpret_cast<const float4*>(&sm.gam[r][c8 + v]);
+          const float4 g7 = *reinterpret_cast<const float4*>(&sm.g7[c8 + v]);
+          q8[v] = qv.x; q8[v + 1] = qv.y; q8[v + 2] = qv.z; q8[v + 3] = qv.w;
+          k8[v] = kv.x; k8[v + 1] = kv.y; k8[v + 2] = kv.z; k8[v + 3] = kv.w;
+          d8[v] = gv.x - g7.x; d8[v + 1] = gv.y - g7.y; d8[v + 2] = gv.z - g7.z; d8[v + 3] = gv.w - g7.w;
+        }
+        const float rq = sm.rn[r], rk = sm.rn[C + r];
+        float qp[8], kp[8], km[8];
 #pragma unroll
-      for (int r = 0; r < C; ++r) {
-        const float kh = sm.ka[r][ch] * sm.rn[C + r];
-        const float ep = sm.ep[r][ch], em = sm.em[r][ch];
-        sm.kx[r][ch] = kh * ep;
-        sm.ka[r][ch] = kh * (ep * erm);
-        sm.em[r][ch] = kh * (em * erp);
-        sm.klt[ch][r] = kh * (em * egl);
+        for (int v = 0; v < 8; ++v) {
+          const float el = fexp(d8[v]), er = fexp(-d8[v]);
+          qp[v] = q8[v] * rq * el;
+          kp[v] = k8[v] * rk * el;
+          km[v] = k8[v] * rk * er;
+        }
+        store8<F32>(sm.op.qp, r, c8, qp);
+        store8<F32>(sm.op.kp, r, c8, kp);
+        store8<F32>(sm.op.km, r, c8, km);
+      } else {
+        const int u = t - 256;
+        {
+          // Qa: row r, lane group (kb, g): keys 32kb + 4g + 0..3 and 32kb + 16 + 4g + 0..3
+          const int r = u >> 4, kb = (u >> 2) & 3, g = u & 3;
+          const int k0 = 32 * kb + 4 * g;
+          const float rq = sm.rn[r];
+          float qa[8];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const float4 qv = *reinterpret_cast<const float4*>(&sm.aq[r][k0 + 16 * half]);
+            const float4 gv = *reinterpret_cast<const float4*>(&sm.gam[r][k0 + 16 * half]);
+            qa[4 * half + 0] = qv.x * rq * fexp(gv.x);
+            qa[4 * half + 1] = qv.y * rq * fexp(gv.y);
+            qa[4 * half + 2] = qv.z * rq * fexp(gv.z);
+            qa[4 * half + 3] = qv.w * rq * fexp(gv.w);
+          }
+          if constexpr (F32) {
+            // fp32 operands keep the natural key order
+            *reinterpret_cast<float4*>(&sm.op.qa[0][r][k0]) = make_float4(qa[0], qa[1], qa[2], qa[3]);
+            *reinterpret_cast<float4*>(&sm.op.qa[0][r][k0 + 16]) = make_float4(qa[4], qa[5], qa[6], qa[7]);
+          } else {
+            store8<F32>(sm.op.qa, r, 32 * kb + 8 * g, qa);
+          }
+        }
+        {
+          // Ka^T and Kl^T: channel cc, rows 8 hf .. 8 hf + 7
+          const int cc = u >> 1, hf = u & 1;
+          const float gend = sm.g15[cc];
+          float ka[8], kl[8];
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            const int r = 8 * hf + v;
+            const float kh = sm.ak[r][cc] * sm.rn[C + r];
+            const float G = sm.gam[r][cc];
+            ka[v] = kh * fexp(G);
+            kl[v] = kh * fexp(gend - G);
+          }
+          store8_hi<F32>(&sm.op.kat[cc][8 * hf], ka);
+          store8<F32>(sm.op.klt, cc, 8 * hf, kl);
+        }
       }
     }
     __syncthreads();
 
     // (4) Gram tiles: wave 0 -> A = Kp Km^T (strict lower, times beta_r); wave 1 -> P = Qp Km^T
     if (wave < 2) {
-      const float(*X)[LDP] = wave == 0 ? sm.ka : sm.qa;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (F32OPS) {
+      if constexpr (F32) {
+        const float(*X)[OP::OPP] = wave == 0 ? sm.op.kp[0] : sm.op.qp[0];
 #pragma unroll 8
         for (int kk = 0; kk < kHeadDim / 4; ++kk)
-          acc = mma_f32(X[lm][4 * kk + lq], sm.em[lm][4 * kk + lq], acc);
+          acc = mma4(X[lm][4 * kk + lq], sm.op.km[0][lm][4 * kk + lq], acc);
       } else {
+        const __bf16(*Xh)[OP::OPP] = wave == 0 ? sm.op.kp[0] : sm.op.qp[0];
+        const __bf16(*Xl)[OP::OPP] = wave == 0 ? sm.op.kp[1] : sm.op.qp[1];
 #pragma unroll
         for (int kb = 0; kb < kHeadDim / 32; ++kb) {
-          float a8[8], b8[8];
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            a8[s] = X[lm][32 * kb + 8 * lq + s];
-            b8[s] = sm.em[lm][32 * kb + 8 * lq + s];
-          }
-          SplitBf16<8> Af, Bf;
-          split_bf16<8>(a8, Af);
-          split_bf16<8>(b8, Bf);
-          acc = mma32(Af, Bf, acc, true);
+          const int o = 32 * kb + 8 * lq;
+          acc = mma32s(ld<bf16x8_t>(&Xh[lm][o]), ld<bf16x8_t>(&Xl[lm][o]),
+                       ld<bf16x8_t>(&sm.op.km[0][lm][o]), ld<bf16x8_t>(&sm.op.km[1][lm][o]), acc);
         }
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int r = 4 * lq + s, j = lm;
-        if (wave == 0)
+        if (wave == 0) {
           sm.A[r][j] = (j < r) ? sm.beta[r] * acc[s] : 0.f;
-        else
-          sm.P[r][j] = (j <= r) ? acc[s] : 0.f;
-      }
-    }
-    __syncthreads();
-
-    // (5) forward substitution (I + A) X = Diag(beta) [Ka | V], one column per thread and in
-    // place in LDS: k owners turn Ka into W, v owners turn V into U~
-    if (role == 1 || role == 2) {
-      float(*X)[LDP] = role == 1 ? sm.kx : sm.va;
-      for (int r = 0; r < C; ++r) {
-        float v = sm.beta[r] * X[r][ch];
-        for (int j = 0; j < r; ++j) v -= sm.A[r][j] * X[j][ch];
-        X[r][ch] = v;
-      }
-    }
-    __syncthreads();
-
-    // (6) state pass on the wave's value tile
-    f32x4_t O;
-    {
-      SplitBf16<8> Sb[4];
-      if constexpr (!F32OPS) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          float b8[8];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            b8[s] = S[2 * kb][s];
-            b8[4 + s] = S[2 * kb + 1][s];
+        } else {
+          const float pv = (j <= r) ? acc[s] : 0.f;
+          if constexpr (F32) {
+            sm.op.p[0][r][j] = pv;
+          } else {
+            split_store(&sm.op.p[0][r][j], &sm.op.p[1][r][j], pv);
           }
-          split_bf16<8>(b8, Sb[kb]);
         }
       }
-      // U = U~ - W S
-      f32x4_t ws = {0.f, 0.f, 0.f, 0.f};
-      ws = x_times_s<F32OPS>(sm.kx, nullptr, S, Sb, false, lane, ws);
-      f32x4_t U;
+    }
+    __syncthreads();
+
+    // (5a) T = (I + A)^-1 Diag(beta), row-elimination with rows spread over lanes: lane
+    // (lm, lq) ends up holding T[lm][4 lq + s].  A[r][j] = 0 for j >= r, so the update
+    // is unconditional.
+    float tt[4];
+    {
+      float arow[C];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) U[s] = sm.va[4 * lq + s][col] - ws[s];
-      SplitBf16<4> Ub;
-      if constexpr (!F32OPS) {
-        float u4[4] = {U[0], U[1], U[2], U[3]};
-        split_bf16<4>(u4, Ub);
+      for (int j = 0; j < C; j += 4) {
+        const float4 v4 = *reinterpret_cast<const float4*>(&sm.A[lm][j]);
+        arow[j] = v4.x;
+        arow[j + 1] = v4.y;
+        arow[j + 2] = v4.z;
+        arow[j + 3] = v4.w;
       }
-      // O = Qa S + P U, with Qa = Qp exp(Gref)
-      O = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      O = x_times_s<F32OPS>(sm.qa, sm.erefp, S, Sb, true, lane, O);
-      O = m_times_u<F32OPS>(&sm.P[0][0], C + 1, U, Ub, lane, O);
-      // S = Diag(exp(Gcum_C)) S + Kl^T U
+      const float bl = sm.beta[lm];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) tt[s] = (4 * lq + s == lm) ? bl : 0.f;
+      eliminate<0>(tt, arow);
+    }
+
+    // (5b) U~ = T V for the wave's value tile (accumulator layout: row 4 lq + s, column col)
+    f32x4_t Ut = {0.f, 0.f, 0.f, 0.f};
+    {
+      float v4[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) v4[s] = sm.va[4 * lq + s][col];
+      if constexpr (F32) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) Ut = mma4(tt[s], v4[s], Ut);
+      } else {
+        bf16x4_t th, tl, vh, vl;
+        split_vec<4>(tt, th, tl);
+        split_vec<4>(v4, vh, vl);
+        Ut = mma16s(th, tl, vh, vl, Ut);
+      }
+    }
+
+    // (5c) W^T = Ka^T T^T, tile nt holding W[lm][16 nt + 4 lq + s]: exactly the A operand
+    // of W.S in the key order of the state tiles
+    f32x4_t Wt[8];
+    {
+      bf16x4_t tb;
+      if constexpr (!F32) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) tb[s] = static_cast<__bf16>(tt[s]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        Wt[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (F32) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) Wt[nt] = mma4(sm.op.kat[16 * nt + lm][4 * lq + s], tt[s], Wt[nt]);
+        } else {
+          Wt[nt] = mma16(ld<bf16x4_t>(&sm.op.kat[16 * nt + lm][4 * lq]), tb, Wt[nt]);
+        }
+      }
+    }
+
+    // (5d) the state pass on the wave's value tile
+    f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (F32) {
+      f32x4_t ws = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int it = 0; it < 8; ++it)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          ws = mma4(Wt[it][s], S[it][s], ws);
+          O = mma4(sm.op.qa[0][lm][16 * it + 4 * lq + s], S[it][s], O);
+        }
+      f32x4_t U = Ut - ws;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) O = mma4(sm.op.p[0][lm][4 * lq + s], U[s], O);
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) S[it][s] *= sm.eglast[16 * it + 4 * lq + s];
-        S[it] = m_times_u<F32OPS>(&sm.klt[16 * it][0], KLP, U, Ub, lane, S[it]);
+        for (int s = 0; s < 4; ++s) S[it][s] *= sm.eg15[16 * it + 4 * lq + s];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) S[it] = mma4(sm.op.klt[0][16 * it + lm][4 * lq + s], U[s], S[it]);
+      }
+    } else {
+      bf16x8_t sh[4], sl[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        float b8[8];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          b8[s] = S[2 * kb][s];
+          b8[4 + s] = S[2 * kb + 1][s];
+        }
+        split_vec<8>(b8, sh[kb], sl[kb]);
+      }
+      // U = U~ - W S
+      f32x4_t ws = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        bf16x8_t wb;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          wb[s] = static_cast<__bf16>(Wt[2 * kb][s]);
+          wb[4 + s] = static_cast<__bf16>(Wt[2 * kb + 1][s]);
+        }
+        ws = mma32(wb, sh[kb], ws);
+      }
+      const f32x4_t U = Ut - ws;
+      bf16x4_t uh, ul;
+      {
+        float u4[4] = {U[0], U[1], U[2], U[3]};
+        split_vec<4>(u4, uh, ul);
+      }
+      // O = Qa S + P U
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int o = 32 * kb + 8 * lq;
+        O = mma32s(ld<bf16x8_t>(&sm.op.qa[0][lm][o]), ld<bf16x8_t>(&sm.op.qa[1][lm][o]), sh[kb],
+                   sl[kb], O);
+      }
+      O = mma16s(ld<bf16x4_t>(&sm.op.p[0][lm][4 * lq]), ld<bf16x4_t>(&sm.op.p[1][lm][4 * lq]), uh,
+                 ul, O);
+      // S = Diag(exp(Gcum_C)) S + Kl^T U
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const float4 e4 = *reinterpret_cast<const float4*>(&sm.eg15[16 * it + 4 * lq]);
+        S[it][0] *= e4.x;
+        S[it][1] *= e4.y;
+        S[it][2] *= e4.z;
+        S[it][3] *= e4.w;
+        S[it] = mma16s(ld<bf16x4_t>(&sm.op.klt[0][16 * it + lm][4 * lq]),
+                       ld<bf16x4_t>(&sm.op.klt[1][16 * it + lm][4 * lq]), uh, ul, S[it]);
       }
     }
 
-    // (7) gated RMSNorm over each output row and the store
+    // (6) gated RMSNorm over each output row and the store
     {
       float ss[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) ss[s] = group_sum<16>(O[s] * O[s]);
+      for (int s = 0; s < 4; ++s) ss[s] = row_sum16(O[s] * O[s]);
       if (lm == 0)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) sm.ss[wave][4 * lq + s] = ss[s];
+        for (int s = 0; s < 4; ++s) sm.ss[buf][wave][4 * lq + s] = ss[s];
     }
     __syncthreads();
     {
@@ -431,9 +600,9 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
         if (r < L) {
           float tot = 0.f;
 #pragma unroll
-          for (int wv = 0; wv < NWAVES; ++wv) tot += sm.ss[wv][r];
+          for (int wv = 0; wv < NWAVES; ++wv) tot += sm.ss[buf][wv][r];
           const float rr = 1.0f / sqrtf(tot * (1.0f / kHeadDim) + a.L.rms_eps);
-          store_io(po, 0, nw * O[s] * rr * sm.sg[r][col]);
+          store_io(po, 0, nw * O[s] * rr * sm.sg[buf][r][col]);
         }
         po += Hd;
       }
