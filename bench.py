@@ -52,7 +52,8 @@ PREFILL_KERNEL = "prefill_kernel"
 def kernel_source_hash(name: str) -> str:
     """Hash of the sources a kernel is built from, to tell whether stored counters are stale."""
     files = {"decode": ["kda_decode.hip", "kda_device.h", "kda_internal.h"],
-             "prefill": ["kda_prefill.hip", "kda_device.h", "kda_internal.h"]}[name]
+             "prefill": ["kda_prefill.hip", "kda_prefill_pc.hip", "kda_mfma.h", "kda_device.h",
+                         "kda_internal.h"]}[name]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "gated_delta_rule_05_amd", "csrc", f), "rb") as fh:

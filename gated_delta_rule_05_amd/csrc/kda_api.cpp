@@ -145,6 +145,9 @@ kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
     return fail(KDA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out)))
     return fail(KDA_ERR_INVALID_ARG, "state buffers must be 16-byte aligned");
+  if (total_tokens > 0 &&
+      (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(gate)))
+    return fail(KDA_ERR_INVALID_ARG, "q, k, v, z and gate must be 16-byte aligned");
   const size_t need = kda_prefill_workspace_bytes(layer, io, num_seqs, cu_seqlens_host, total_tokens);
   if (workspace_bytes < need || (need > 0 && !workspace))
     return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",

@@ -46,5 +46,7 @@ struct PrefillArgs {
 hipError_t launch_decode(const DecodeArgs& a, kda_dtype io, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, kda_dtype io, const int32_t* order_host,
                           hipStream_t stream);
+// bf16 io: the producer/consumer kernel of kda_prefill_pc.hip
+hipError_t launch_prefill_bf16(const PrefillArgs& a, const int32_t* order_host, hipStream_t stream);
 
 }  // namespace kda

@@ -1,0 +1,150 @@
+// MFMA, DPP and LDS helpers shared by the prefill kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "kda_device.h"
+
+namespace kda {
+namespace mf {
+
+constexpr int C = 16;  // chunk = exponent tile
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// exp(x) through the hardware base-2 exponential; relative error ~1e-6 over the ranges
+// used here (|x| <= 80).
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fsigmoid(float x) { return frcp(1.0f + fexp(-x)); }
+
+// Cross-lane moves inside a row of 16 lanes (DPP): row_newbcast:n hands every lane of the
+// row the value of its lane n; row_ror:k rotates the row by k lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return dpp<0x150 + N>(x);
+}
+// Sum over the 16 lanes of a row, delivered to every lane of the row.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<0x128>(x);
+  x += dpp<0x124>(x);
+  x += dpp<0x122>(x);
+  x += dpp<0x121>(x);
+  return x;
+}
+
+__device__ __forceinline__ float raw_to_f32(float x) { return x; }
+__device__ __forceinline__ float raw_to_f32(uint16_t b) { return bf16_to_f32(b); }
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() is also a fence on global
+// memory and waits for every outstanding global load, which would drain the next
+// chunk's prefetched rows at each barrier; nothing global is exchanged between the
+// threads of a workgroup here, so waiting for LDS operations is enough.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Hides a value from the optimiser so that address arithmetic is recomputed where it is
+// used instead of being kept live (in 64-bit registers) across the whole kernel.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ void split_store(__bf16* hi, __bf16* lo, float x) {
+  const __bf16 h = static_cast<__bf16>(x);
+  *hi = h;
+  *lo = static_cast<__bf16>(x - static_cast<float>(h));
+}
+
+template <int N, typename V>
+__device__ __forceinline__ void split_vec(const float* x, V& hi, V& lo) {
+#pragma unroll
+  for (int s = 0; s < N; ++s) {
+    const __bf16 h = static_cast<__bf16>(x[s]);
+    hi[s] = h;
+    lo[s] = static_cast<__bf16>(x[s] - static_cast<float>(h));
+  }
+}
+
+__device__ __forceinline__ f32x4_t mma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma16(bf16x4_t a, bf16x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma4(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// split products: (ah + al)(bh + bl) ~ ah bh + ah bl + al bh
+__device__ __forceinline__ f32x4_t mma32s(bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl,
+                                          f32x4_t c) {
+  c = mma32(al, bh, c);
+  c = mma32(ah, bl, c);
+  return mma32(ah, bh, c);
+}
+__device__ __forceinline__ f32x4_t mma16s(bf16x4_t ah, bf16x4_t al, bf16x4_t bh, bf16x4_t bl,
+                                          f32x4_t c) {
+  c = mma16(al, bh, c);
+  c = mma16(ah, bl, c);
+  return mma16(ah, bh, c);
+}
+
+template <typename V, typename E>
+__device__ __forceinline__ V ld(const E* p) {
+  return *reinterpret_cast<const V*>(p);
+}
+
+// Stores 8 consecutive operand values at [row][col0..col0+7] of a (hi, lo) plane pair
+// (bf16) or of the single fp32 plane, as 16-byte writes.
+template <bool F32, typename Arr>
+__device__ __forceinline__ void store8(Arr& planes, int row, int col0, const float* x) {
+  if constexpr (F32) {
+    *reinterpret_cast<float4*>(&planes[0][row][col0]) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(&planes[0][row][col0 + 4]) = make_float4(x[4], x[5], x[6], x[7]);
+  } else {
+    bf16x8_t hi, lo;
+    split_vec<8>(x, hi, lo);
+    *reinterpret_cast<bf16x8_t*>(&planes[0][row][col0]) = hi;
+    *reinterpret_cast<bf16x8_t*>(&planes[1][row][col0]) = lo;
+  }
+}
+
+// Same for a single plane rounded once (no lo part).
+template <bool F32, typename E>
+__device__ __forceinline__ void store8_hi(E* dst, const float* x) {
+  if constexpr (F32) {
+    *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  } else {
+    bf16x8_t hi;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) hi[v] = static_cast<__bf16>(x[v]);
+    *reinterpret_cast<bf16x8_t*>(dst) = hi;
+  }
+}
+
+// One elimination step per row j of the 16x16 unit-lower system: every lane of a 16-lane
+// row takes row j's values from lane j of its own row (DPP broadcast).
+template <int J>
+__device__ __forceinline__ void eliminate(float* tt, const float* arow) {
+  if constexpr (J < C - 1) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) tt[s] -= arow[J] * row_bcast<J>(tt[s]);
+    eliminate<J + 1>(tt, arow);
+  }
+}
+
+
+}  // namespace mf
+}  // namespace kda

@@ -19,7 +19,8 @@
 // also the B operand of W.S and Qa.S (the contraction order inside an MFMA is free, so the
 // A operand is supplied in the matching key order) and the accumulator of Kl^T.U.
 //
-// Per chunk, with the raw rows of the next chunk already loading:
+// Per chunk, with the raw rows of the next chunk already loading (16-byte loads, parked
+// in LDS for the next iteration):
 //   (1) q/k/v conv + SiLU (history in registers), gate, Gcum, sigmoid(gate), beta
 //   (2) q/k row norms
 //   (3) scaled operands, stored once in MFMA-ready form (bf16 hi/lo pairs)
@@ -35,20 +36,17 @@
 
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_mfma.h"
 
 namespace kda {
 
 namespace {
 
-constexpr int C = 16;        // chunk = exponent tile
+using namespace mf;
 constexpr int NWAVES = 8;    // one 16-column value tile of the state per wave
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int LDP = 132;     // row stride (floats) of fp32 [16][128] arrays
 constexpr int AP = 20;       // row stride (floats) of the A tile
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct SeqOrder {
   int32_t idx[kMaxOrdered];
@@ -73,6 +71,10 @@ struct alignas(16) Ops {
 
 template <bool F32>
 struct alignas(16) Smem {
+  using RawE = typename std::conditional<F32, float, uint16_t>::type;
+  static constexpr int RAWP = kHeadDim + (F32 ? 4 : 8);
+  RawE raw[5][C][RAWP];  // raw rows of q, k, v, z, gate (io type bits)
+  RawE braw[C];          // raw beta
   float aq[C][LDP];    // silu(conv q)
   float ak[C][LDP];    // silu(conv k)
   float va[C][LDP];    // silu(conv v) = V
@@ -87,123 +89,6 @@ struct alignas(16) Smem {
   float beta[C];
   float ss[2][NWAVES][C];
 };
-
-// exp(x) through the hardware base-2 exponential; relative error ~1e-6 over the ranges
-// used here (|x| <= 80).
-__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
-__device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
-__device__ __forceinline__ float fsigmoid(float x) { return frcp(1.0f + fexp(-x)); }
-
-// Cross-lane moves inside a row of 16 lanes (DPP): row_newbcast:n hands every lane of the
-// row the value of its lane n; row_ror:k rotates the row by k lanes.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                               0xF, 0xF, false));
-}
-template <int N>
-__device__ __forceinline__ float row_bcast(float x) {
-  return dpp<0x150 + N>(x);
-}
-// Sum over the 16 lanes of a row, delivered to every lane of the row.
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dpp<0x128>(x);
-  x += dpp<0x124>(x);
-  x += dpp<0x122>(x);
-  x += dpp<0x121>(x);
-  return x;
-}
-
-// Hides a value from the optimiser so that address arithmetic is recomputed where it is
-// used instead of being kept live (in 64-bit registers) across the whole kernel.
-__device__ __forceinline__ int opaque(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
-__device__ __forceinline__ void split_store(__bf16* hi, __bf16* lo, float x) {
-  const __bf16 h = static_cast<__bf16>(x);
-  *hi = h;
-  *lo = static_cast<__bf16>(x - static_cast<float>(h));
-}
-
-template <int N, typename V>
-__device__ __forceinline__ void split_vec(const float* x, V& hi, V& lo) {
-#pragma unroll
-  for (int s = 0; s < N; ++s) {
-    const __bf16 h = static_cast<__bf16>(x[s]);
-    hi[s] = h;
-    lo[s] = static_cast<__bf16>(x[s] - static_cast<float>(h));
-  }
-}
-
-__device__ __forceinline__ f32x4_t mma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mma16(bf16x4_t a, bf16x4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mma4(float a, float b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-// split products: (ah + al)(bh + bl) ~ ah bh + ah bl + al bh
-__device__ __forceinline__ f32x4_t mma32s(bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl,
-                                          f32x4_t c) {
-  c = mma32(al, bh, c);
-  c = mma32(ah, bl, c);
-  return mma32(ah, bh, c);
-}
-__device__ __forceinline__ f32x4_t mma16s(bf16x4_t ah, bf16x4_t al, bf16x4_t bh, bf16x4_t bl,
-                                          f32x4_t c) {
-  c = mma16(al, bh, c);
-  c = mma16(ah, bl, c);
-  return mma16(ah, bh, c);
-}
-
-template <typename V, typename E>
-__device__ __forceinline__ V ld(const E* p) {
-  return *reinterpret_cast<const V*>(p);
-}
-
-// Stores 8 consecutive operand values at [row][col0..col0+7] of a (hi, lo) plane pair
-// (bf16) or of the single fp32 plane, as 16-byte writes.
-template <bool F32, typename Arr>
-__device__ __forceinline__ void store8(Arr& planes, int row, int col0, const float* x) {
-  if constexpr (F32) {
-    *reinterpret_cast<float4*>(&planes[0][row][col0]) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4*>(&planes[0][row][col0 + 4]) = make_float4(x[4], x[5], x[6], x[7]);
-  } else {
-    bf16x8_t hi, lo;
-    split_vec<8>(x, hi, lo);
-    *reinterpret_cast<bf16x8_t*>(&planes[0][row][col0]) = hi;
-    *reinterpret_cast<bf16x8_t*>(&planes[1][row][col0]) = lo;
-  }
-}
-
-// Same for a single plane rounded once (no lo part).
-template <bool F32, typename E>
-__device__ __forceinline__ void store8_hi(E* dst, const float* x) {
-  if constexpr (F32) {
-    *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4*>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
-  } else {
-    bf16x8_t hi;
-#pragma unroll
-    for (int v = 0; v < 8; ++v) hi[v] = static_cast<__bf16>(x[v]);
-    *reinterpret_cast<bf16x8_t*>(dst) = hi;
-  }
-}
-
-// One elimination step per row j of the 16x16 unit-lower system: every lane of a 16-lane
-// row takes row j's values from lane j of its own row (DPP broadcast).
-template <int J>
-__device__ __forceinline__ void eliminate(float* tt, const float* arow) {
-  if constexpr (J < C - 1) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) tt[s] -= arow[J] * row_bcast<J>(tt[s]);
-    eliminate<J + 1>(tt, arow);
-  }
-}
 
 template <typename IO>
 __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrder order) {
@@ -230,8 +115,6 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
   const int col = 16 * wave + lm;  // value column this lane holds in the state pass
 
   const IO* x_b = static_cast<const IO*>(a.beta);
-  const IO* x_p = static_cast<const IO*>(role == 0 ? a.q : role == 1 ? a.k : role == 2 ? a.v : a.z);
-  const IO* x_g = static_cast<const IO*>(a.gate);
 
   // conv weights and history of the owned channel (roles 0-2: plane = role)
   float w[4] = {0.f, 0.f, 0.f, 0.f}, hist[3] = {0.f, 0.f, 0.f};
@@ -262,40 +145,88 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
   }
   const float nw = a.L.norm_w[col];
 
-  // raw rows of the upcoming chunk, loaded one chunk ahead while the current chunk is
-  // processed; rows past the end of the sequence re-read its last row (always in bounds)
-  // and are masked when used
-  float xa[C], xb[C];
-  float braw = 0.f;
-  auto prefetch = [&](int c0n) {
+  // Raw rows of the next chunk (q, k, v, z, gate: 16 rows x 128 channels each) are
+  // fetched as 16-byte segments right after the current chunk's prologue, held in
+  // registers while the chunk is processed, and parked in LDS just before the chunk's last
+  // barrier.  Rows past the end of the sequence re-read its last row (always in bounds)
+  // and are masked when used.
+  constexpr int E = sizeof(IO);
+  constexpr int SPR = kHeadDim * E / 16;  // 16-byte segments per row
+  constexpr int NSEG = 5 * C * SPR;
+  constexpr int NRND = (NSEG + NTHREADS - 1) / NTHREADS;
+  using Raw = typename std::conditional<F32, float, uint16_t>::type;
+  uint4 seg0, seg1, seg2, seg3, seg4;
+  // plane base pointers (uniform per wave: a wave's segments all fall in one plane)
+  const char* const pq = static_cast<const char*>(a.q);
+  const char* const pk = static_cast<const char*>(a.k);
+  const char* const pv = static_cast<const char*>(a.v);
+  const char* const pz = static_cast<const char*>(a.z);
+  const char* const pgt = static_cast<const char*>(a.gate);
+#define KDA_SEG_SRC(k, c0n, Ln)                                                            \
+  ([&]() -> const uint4* {                                                                 \
+    const int sidx = t + (k) * NTHREADS;                                                   \
+    /* one plane per wave and round: make the plane index scalar */                        \
+    const int pl = __builtin_amdgcn_readfirstlane(sidx / (C * SPR));                       \
+    const int rem = sidx % (C * SPR);                                                      \
+    const int r = rem / SPR, part = rem % SPR;                                             \
+    const char* base = pl == 0 ? pq : pl == 1 ? pk : pl == 2 ? pv : pl == 3 ? pz : pgt;    \
+    return reinterpret_cast<const uint4*>(                                                 \
+        base + ((t0 + (c0n) + min(r, (Ln) - 1)) * Hd + static_cast<int64_t>(h) * kHeadDim) * E + \
+        16 * part);                                                                        \
+  }())
+#define KDA_SEG_DST(k)                                                                     \
+  ([&]() -> uint4* {                                                                       \
+    const int sidx = t + (k) * NTHREADS;                                                   \
+    const int pl = sidx / (C * SPR), rem = sidx % (C * SPR);                               \
+    const int r = rem / SPR, part = rem % SPR;                                             \
+    return reinterpret_cast<uint4*>(&sm.raw[pl][r][part * (16 / E)]);                      \
+  }())
+#define KDA_SEG_OK(k) (NSEG % NTHREADS == 0 || t + (k) * NTHREADS < NSEG)
+  Raw braw = 0;
+  auto prefetch = [&](int c0n) __attribute__((always_inline)) {
     const int Ln = min(C, T - c0n);
-    const IO* p = x_p + (t0 + c0n) * Hd + c;
-#pragma unroll
-    for (int r = 0; r < C; ++r) xa[r] = load_io(p, static_cast<int64_t>(min(r, Ln - 1)) * Hd);
-    if (role == 3) {
-      const IO* pg = x_g + (t0 + c0n) * Hd + c;
-#pragma unroll
-      for (int r = 0; r < C; ++r) xb[r] = load_io(pg, static_cast<int64_t>(min(r, Ln - 1)) * Hd);
+    if (KDA_SEG_OK(0)) seg0 = *KDA_SEG_SRC(0, c0n, Ln);
+    if (NRND > 1 && KDA_SEG_OK(1)) seg1 = *KDA_SEG_SRC(1, c0n, Ln);
+    if (NRND > 2 && KDA_SEG_OK(2)) seg2 = *KDA_SEG_SRC(2, c0n, Ln);
+    if (NRND > 3 && KDA_SEG_OK(3)) seg3 = *KDA_SEG_SRC(3, c0n, Ln);
+    if (NRND > 4 && KDA_SEG_OK(4)) seg4 = *KDA_SEG_SRC(4, c0n, Ln);
+    if (t < C) {
+      const IO* pb = x_b + (t0 + c0n + min(t, Ln - 1)) * H + h;
+      if constexpr (F32) {
+        braw = *pb;
+      } else {
+        braw = pb->bits;
+      }
     }
-    if (t < C) braw = load_io(x_b, (t0 + c0n + min(t, Ln - 1)) * H + h);
   };
-  if (T > 0) prefetch(0);
+  auto stage = [&]() __attribute__((always_inline)) {
+    if (KDA_SEG_OK(0)) *KDA_SEG_DST(0) = seg0;
+    if (NRND > 1 && KDA_SEG_OK(1)) *KDA_SEG_DST(1) = seg1;
+    if (NRND > 2 && KDA_SEG_OK(2)) *KDA_SEG_DST(2) = seg2;
+    if (NRND > 3 && KDA_SEG_OK(3)) *KDA_SEG_DST(3) = seg3;
+    if (NRND > 4 && KDA_SEG_OK(4)) *KDA_SEG_DST(4) = seg4;
+    if (t < C) sm.braw[t] = braw;
+  };
+  static_assert(NRND <= 5, "five prefetch registers");
+  static_assert((C * SPR) % 64 == 0, "a wave's segments must fall in one plane");
+  if (T > 0) {
+    prefetch(0);
+    stage();
+    lds_barrier();
+  }
 
   const int last_c0 = T > 0 ? ((T - 1) / C) * C : 0;
   int buf = 0;
   for (int c0 = 0; c0 < T; c0 += C, buf ^= 1) {
     const int L = min(C, T - c0);
     const int64_t row0 = t0 + c0;
-    const float* cur = xa;
-    const float* cur2 = xb;
-    const float bcur = braw;
 
     // (1) elementwise prologue
     if (role < 3) {
       float(*dst)[LDP] = role == 0 ? sm.aq : role == 1 ? sm.ak : sm.va;
 #pragma unroll
       for (int r = 0; r < C; ++r) {
-        const float x = cur[r];
+        const float x = raw_to_f32(sm.raw[role][r][ch]);
         const float y = w[3] * x + w[0] * hist[0] + w[1] * hist[1] + w[2] * hist[2];
         const bool live = r < L;
         if (live) {
@@ -310,19 +241,18 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
 #pragma unroll
       for (int r = 0; r < C; ++r) {
         const bool live = r < L;
-        G += live ? lb * fsigmoid(ascale * (cur[r] + dtb)) : 0.f;
+        G += live ? lb * fsigmoid(ascale * (raw_to_f32(sm.raw[3][r][ch]) + dtb)) : 0.f;
         sm.gam[r][ch] = G;
-        sm.sg[buf][r][ch] = live ? fsigmoid(cur2[r]) : 0.f;
+        sm.sg[buf][r][ch] = live ? fsigmoid(raw_to_f32(sm.raw[4][r][ch])) : 0.f;
         if (r == C / 2 - 1) sm.g7[ch] = G;
       }
       sm.g15[ch] = G;
       sm.eg15[ch] = fexp(G);
     }
-    if (t < C) sm.beta[t] = (t < L) ? fsigmoid(bcur) : 0.f;
-    // next chunk's raw rows: issued unconditionally (the last chunk re-reads itself) so
-    // that their wait lands at the next iteration's first use
+    if (t < C) sm.beta[t] = (t < L) ? fsigmoid(raw_to_f32(sm.braw[t])) : 0.f;
+    // next chunk's raw rows (the last chunk re-reads itself)
     prefetch(min(c0 + C, last_c0));
-    __syncthreads();
+    lds_barrier();
 
     // (2) row norms: 16 threads per (plane, row)
     {
@@ -339,7 +269,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
       if (part == 0)
         sm.rn[task] = (1.0f / sqrtf(ss + a.L.l2_eps)) * (task < C ? 0.08838834764831845f : 1.0f);
     }
-    __syncthreads();
+    lds_barrier();
 
     // (3) scaled operands, written once in MFMA-ready form, by 8-channel work items:
     // threads 0..255 take (row, 8 channels) of Qp, Kp, Km; threads 256..511 take
@@ -414,7 +344,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // (4) Gram tiles: wave 0 -> A = Kp Km^T (strict lower, times beta_r); wave 1 -> P = Qp Km^T
     if (wave < 2) {
@@ -449,7 +379,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // (5a) T = (I + A)^-1 Diag(beta), row-elimination with rows spread over lanes: lane
     // (lm, lq) ends up holding T[lm][4 lq + s].  A[r][j] = 0 for j >= r, so the update
@@ -591,7 +521,8 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
 #pragma unroll
         for (int s = 0; s < 4; ++s) sm.ss[buf][wave][4 * lq + s] = ss[s];
     }
-    __syncthreads();
+    stage();  // the next chunk's raw rows, for the next iteration's prologue
+    lds_barrier();
     {
       IO* po = static_cast<IO*>(a.out) + (row0 + 4 * lq) * Hd + static_cast<int64_t>(h) * kHeadDim + col;
 #pragma unroll
@@ -624,19 +555,20 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
   }
 }
 
+#undef KDA_SEG_SRC
+#undef KDA_SEG_DST
+#undef KDA_SEG_OK
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, kda_dtype io, const int32_t* order_host,
                           hipStream_t stream) {
+  if (io == KDA_BF16) return launch_prefill_bf16(a, order_host, stream);
   SeqOrder ord;
   const int nord = a.num_seqs < kMaxOrdered ? a.num_seqs : kMaxOrdered;
   for (int i = 0; i < kMaxOrdered; ++i) ord.idx[i] = i < nord ? order_host[i] : 0;
   const dim3 grid(static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.L.H));
-  const dim3 block(NTHREADS);
-  if (io == KDA_F32)
-    hipLaunchKernelGGL(prefill_kernel<float>, grid, block, 0, stream, a, ord);
-  else
-    hipLaunchKernelGGL(prefill_kernel<bf16_t>, grid, block, 0, stream, a, ord);
+  hipLaunchKernelGGL(prefill_kernel<float>, grid, dim3(NTHREADS), 0, stream, a, ord);
   return hipGetLastError();
 }
 

@@ -1,0 +1,543 @@
+// Chunked prefill of the KDA core for bf16 io on gfx950: producer/consumer waves.
+//
+// Same algebra as the fp32 prefill kernel (kda_prefill.hip; docs.rs "memra_engine::kda"
+// header prose for the per-channel Gcum chunk form, "Kimi Delta Attention (KDA) --
+// analysis & C kernel plan" section "Recurrence", OpenModelAtlas "Kimi K3 - Retention
+// gate" "Why" for the 16-token tile bound), mapped so that the two kinds of work overlap:
+//
+//   * 8 producer waves build everything chunk c+1 needs from its raw rows alone: short
+//     conv + SiLU, gate and Gcum, q/k norms, MFMA-ready operands (bf16 hi/lo), and the
+//     next-but-one chunk's raw rows are fetched meanwhile (16-byte loads staged in LDS);
+//   * 8 consumer waves run chunk c's state pass, one 16-column value tile of the fp32
+//     128x128 state each, held in MFMA accumulators for the whole sequence: U~ = T V,
+//     W^T = Ka^T T^T (landing in the A-operand layout of W.S), U = U~ - W S,
+//     O = Qa S + P U, the gated RMSNorm epilogue, S <- Diag(e^Gcum_C) S + Kl^T U; and,
+//     once chunk c+1's operands are ready, its Gram tiles and T = (I + A)^-1 Diag(beta)
+//     (DPP elimination, once per chunk).
+//
+// Operands that cross from producers to consumers are double-buffered by chunk parity.
+// Four LDS barriers per chunk; each wave works in every interval it can.  With 16 waves
+// per workgroup each SIMD holds two producer and two consumer waves, so the VALU-heavy
+// and MFMA-heavy halves hide each other's latencies.
+#include "kda_device.h"
+#include "kda_internal.h"
+#include "kda_mfma.h"
+
+namespace kda {
+
+namespace {
+
+using namespace mf;
+
+constexpr int PW = 8;                  // producer waves
+constexpr int CWN = 8;                 // consumer waves
+constexpr int PT = 64 * PW;            // producer threads
+constexpr int NT = 64 * (PW + CWN);
+constexpr int LDP = 132;               // fp32 row stride of [16][128] arrays
+constexpr int OPP = 136;               // bf16 row stride of [16][128] operands
+constexpr int KTP = 24;                // bf16 row stride of [128][16] operands
+constexpr int RWP = 136;               // row stride of the raw staging rows (bf16 bits)
+
+struct PcOrder {
+  int32_t idx[kMaxOrdered];
+};
+
+// What consumers read for one chunk (double-buffered by chunk parity).
+struct alignas(16) KBuf {
+  __bf16 qa[2][C][OPP];         // Qa = q-hat exp(Gcum), hi/lo, key order of the .S products
+  __bf16 kat[kHeadDim][KTP];    // Ka^T, hi
+  __bf16 klt[2][kHeadDim][KTP]; // Kl^T, hi/lo
+  __bf16 p[2][C][20];           // P (lower incl.), hi/lo
+  __bf16 tm[2][C][20];          // T = (I + A)^-1 Diag(beta), hi/lo
+  float V[C][LDP];              // V = silu(conv v)
+  float eg15[kHeadDim];         // exp(Gcum at the chunk end)
+  float beta[C];
+  uint16_t graw[C][RWP];        // raw output-gate bits
+};
+
+struct alignas(16) PcSmem {
+  KBuf kb[2];
+  uint16_t raw[5][C][RWP];      // staged raw rows of q, k, v, z, gate
+  uint16_t braw[C];             // staged raw beta
+  float aq[C][LDP];             // silu(conv q)
+  float ak[C][LDP];             // silu(conv k)
+  float gam[C][LDP];            // Gcum
+  __bf16 qp[2][C][OPP];         // Qp = q-hat exp(Gcum - Gref), hi/lo
+  __bf16 kp[2][C][OPP];         // Kp = k-hat exp(Gcum - Gref), hi/lo
+  __bf16 km[2][C][OPP];         // Km = k-hat exp(Gref - Gcum), hi/lo
+  float g7[kHeadDim];           // Gcum at the chunk midpoint (Gram reference)
+  float g15[kHeadDim];          // Gcum at the chunk end
+  float rn[2 * C];              // 1/|q| * d^-1/2, then 1/|k|
+  float A[C][20];               // A times beta (strict lower), for the elimination
+  float ss[CWN][C];             // per consumer wave, per row: sum of O^2 over its columns
+};
+
+static_assert(sizeof(PcSmem) <= 160 * 1024, "LDS budget of one workgroup");
+
+__global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder order) {
+  __shared__ PcSmem sm;
+
+  const int H = a.L.H;
+  const int rank = blockIdx.x / H;
+  const int h = blockIdx.x - rank * H;
+  const int n = (a.num_seqs <= kMaxOrdered) ? order.idx[rank] : rank;
+  const int64_t t0 = a.cu_seqlens[n];
+  const int T = a.cu_seqlens[n + 1] - static_cast<int>(t0);
+  const int64_t Hd = static_cast<int64_t>(H) * kHeadDim;
+  const int nch = (T + C - 1) / C;
+
+  const int t = threadIdx.x;
+  const int wave = t >> 6;
+  const int lane = t & 63;
+  const int lm = lane & 15;
+  const int lq = lane >> 4;
+  const bool producer = wave < PW;
+  // producers: role 0 = q, 1 = k, 2 = v, 3 = z and gate, over 128 channels each
+  const int role = (t >> 7) & 3;
+  const int ch = t & (kHeadDim - 1);
+  const int64_t c = static_cast<int64_t>(h) * kHeadDim + ch;
+  // consumers: value tile cw, column col
+  const int cw = wave - PW;
+  const int col = 16 * (cw & (CWN - 1)) + lm;
+
+  if (producer) {
+    // ============================================================== producer waves
+    float w[4] = {0.f, 0.f, 0.f, 0.f}, hist[3] = {0.f, 0.f, 0.f};
+    if (role < 3) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = a.L.conv_w[(role * Hd + c) * kConvTaps + j];
+      if (a.ring_in) {
+        const float* rin = a.ring_in + static_cast<int64_t>(n) * 3 * Hd * kRingTaps;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) hist[j] = rin[(role * Hd + c) * kRingTaps + j];
+      }
+    }
+    const float dtb = a.L.dt_bias[c];
+    const float ascale = expf(a.L.A_log[h]);
+    const float lb = a.L.lower_bound;
+
+    // raw-row prefetch: 5 planes x 16 rows x 16 segments of 16 bytes over 512 threads
+    constexpr int SPR = kHeadDim * 2 / 16;
+    constexpr int NSEG = 5 * C * SPR;
+    static_assert((NSEG + PT - 1) / PT == 3, "three prefetch registers");
+    static_assert((C * SPR) % 64 == 0, "a wave's segments must fall in one plane");
+    uint4 seg0, seg1, seg2;
+    uint16_t braw = 0;
+    const char* const pq = static_cast<const char*>(a.q);
+    const char* const pk = static_cast<const char*>(a.k);
+    const char* const pv = static_cast<const char*>(a.v);
+    const char* const pz = static_cast<const char*>(a.z);
+    const char* const pgt = static_cast<const char*>(a.gate);
+    const bf16_t* const x_b = static_cast<const bf16_t*>(a.beta);
+#define KDA_PC_SRC(k, c0n, Ln)                                                              \
+  ([&]() -> const uint4* {                                                                  \
+    const int sidx = t + (k) * PT;                                                          \
+    const int pl = __builtin_amdgcn_readfirstlane(sidx / (C * SPR));                        \
+    const int rem = sidx % (C * SPR);                                                       \
+    const int r = rem / SPR, part = rem % SPR;                                              \
+    const char* base = pl == 0 ? pq : pl == 1 ? pk : pl == 2 ? pv : pl == 3 ? pz : pgt;     \
+    return reinterpret_cast<const uint4*>(                                                  \
+        base + ((t0 + (c0n) + min(r, (Ln) - 1)) * Hd + static_cast<int64_t>(h) * kHeadDim) * 2 + \
+        16 * part);                                                                         \
+  }())
+#define KDA_PC_DST(k)                                                                       \
+  ([&]() -> uint4* {                                                                        \
+    const int sidx = t + (k) * PT;                                                          \
+    const int pl = sidx / (C * SPR), rem = sidx % (C * SPR);                                \
+    const int r = rem / SPR, part = rem % SPR;                                              \
+    return reinterpret_cast<uint4*>(&sm.raw[pl][r][part * 8]);                              \
+  }())
+#define KDA_PC_OK(k) (t + (k) * PT < NSEG)
+    auto prefetch = [&](int c0n) __attribute__((always_inline)) {
+      const int Ln = min(C, T - c0n);
+      if (KDA_PC_OK(0)) seg0 = *KDA_PC_SRC(0, c0n, Ln);
+      if (KDA_PC_OK(1)) seg1 = *KDA_PC_SRC(1, c0n, Ln);
+      if (KDA_PC_OK(2)) seg2 = *KDA_PC_SRC(2, c0n, Ln);
+      if (t < C) braw = x_b[(t0 + c0n + min(t, Ln - 1)) * H + h].bits;
+    };
+    auto stage = [&]() __attribute__((always_inline)) {
+      if (KDA_PC_OK(0)) *KDA_PC_DST(0) = seg0;
+      if (KDA_PC_OK(1)) *KDA_PC_DST(1) = seg1;
+      if (KDA_PC_OK(2)) *KDA_PC_DST(2) = seg2;
+      if (t < C) sm.braw[t] = braw;
+    };
+
+    if (T > 0) {
+      prefetch(0);
+      stage();
+    }
+    lds_barrier();
+
+    // iteration i: producers build chunk i + 1
+    for (int i = -1; i < nch; ++i) {
+      const bool has_next = i + 1 < nch;
+      const int Ln = min(C, T - (i + 1) * C);
+      KBuf& KN = sm.kb[(i + 1) & 1];
+
+      // ---------------------------------------------------------- interval 1
+      if (has_next) {
+        // conv + SiLU with the history in registers; gate and Gcum; raw gate; beta
+        // all raw values first: the reads are independent of the stores below, and
+        // issuing them together keeps one LDS round trip per chunk instead of per row
+        uint16_t xr[C], xg[C];
+#pragma unroll
+        for (int r = 0; r < C; ++r) xr[r] = sm.raw[role][r][ch];
+        if (role == 3) {
+#pragma unroll
+          for (int r = 0; r < C; ++r) xg[r] = sm.raw[4][r][ch];
+        }
+        if (role < 3) {
+#pragma unroll
+          for (int r = 0; r < C; ++r) {
+            const float x = bf16_to_f32(xr[r]);
+            const float y = w[3] * x + w[0] * hist[0] + w[1] * hist[1] + w[2] * hist[2];
+            const bool live = r < Ln;
+            if (live) {
+              hist[0] = hist[1];
+              hist[1] = hist[2];
+              hist[2] = x;
+            }
+            const float act = live ? y * fsigmoid(y) : 0.f;
+            if (role == 0)
+              sm.aq[r][ch] = act;
+            else if (role == 1)
+              sm.ak[r][ch] = act;
+            else
+              KN.V[r][ch] = act;
+          }
+        } else {
+          float G = 0.f;
+#pragma unroll
+          for (int r = 0; r < C; ++r) {
+            const bool live = r < Ln;
+            G += live ? lb * fsigmoid(ascale * (bf16_to_f32(xr[r]) + dtb)) : 0.f;
+            sm.gam[r][ch] = G;
+            KN.graw[r][ch] = live ? xg[r] : static_cast<uint16_t>(0);
+            if (r == C / 2 - 1) sm.g7[ch] = G;
+          }
+          sm.g15[ch] = G;
+          KN.eg15[ch] = fexp(G);
+        }
+        if (t < C) KN.beta[t] = (t < Ln) ? fsigmoid(bf16_to_f32(sm.braw[t])) : 0.f;
+        // raw rows of chunk i + 2 (the last chunk re-reads itself)
+        prefetch(min(i + 2, nch - 1) * C);
+      }
+      lds_barrier();
+
+      // ---------------------------------------------------------- interval 2
+      if (has_next) {
+        // q/k row norms: 16 threads per (plane, row)
+        const int task = t >> 4, part = t & 15;
+        const float(*X)[LDP] = task < C ? sm.aq : sm.ak;
+        const int r = task & (C - 1);
+        float ss = 0.f;
+#pragma unroll
+        for (int m = 0; m < kHeadDim / 16; ++m) {
+          const float x = X[r][part + 16 * m];
+          ss += x * x;
+        }
+        ss = row_sum16(ss);
+        if (part == 0)
+          sm.rn[task] = (1.0f / sqrtf(ss + a.L.l2_eps)) * (task < C ? 0.08838834764831845f : 1.0f);
+      }
+      lds_barrier();
+
+      // ---------------------------------------------------------- interval 3
+      if (has_next) {
+        // scaled operands of chunk i + 1, written once in MFMA-ready form
+        if (t < 256) {
+          const int r = t >> 4, c8 = 8 * (t & 15);
+          float q8[8], k8[8], d8[8];
+#pragma unroll
+          for (int v = 0; v < 8; v += 4) {
+            const float4 qv = *reinterpret_cast<const float4*>(&sm.aq[r][c8 + v]);
+            const float4 kv = *reinterpret_cast<const float4*>(&sm.ak[r][c8 + v]);
+            const float4 gv = *reinterpret_cast<const float4*>(&sm.gam[r][c8 + v]);
+            const float4 g7 = *reinterpret_cast<const float4*>(&sm.g7[c8 + v]);
+            q8[v] = qv.x; q8[v + 1] = qv.y; q8[v + 2] = qv.z; q8[v + 3] = qv.w;
+            k8[v] = kv.x; k8[v + 1] = kv.y; k8[v + 2] = kv.z; k8[v + 3] = kv.w;
+            d8[v] = gv.x - g7.x; d8[v + 1] = gv.y - g7.y; d8[v + 2] = gv.z - g7.z; d8[v + 3] = gv.w - g7.w;
+          }
+          const float rq = sm.rn[r], rk = sm.rn[C + r];
+          float qp[8], kp[8], km[8];
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            const float el = fexp(d8[v]), er = fexp(-d8[v]);
+            qp[v] = q8[v] * rq * el;
+            kp[v] = k8[v] * rk * el;
+            km[v] = k8[v] * rk * er;
+          }
+          store8<false>(sm.qp, r, c8, qp);
+          store8<false>(sm.kp, r, c8, kp);
+          store8<false>(sm.km, r, c8, km);
+        } else {
+          const int u = t - 256;
+          {
+            // Qa: row r, lane group (kb, g): keys 32kb + 4g + 0..3 and 32kb + 16 + 4g + 0..3
+            const int r = u >> 4, kb = (u >> 2) & 3, g = u & 3;
+            const int k0 = 32 * kb + 4 * g;
+            const float rq = sm.rn[r];
+            float qa[8];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const float4 qv = *reinterpret_cast<const float4*>(&sm.aq[r][k0 + 16 * half]);
+              const float4 gv = *reinterpret_cast<const float4*>(&sm.gam[r][k0 + 16 * half]);
+              qa[4 * half + 0] = qv.x * rq * fexp(gv.x);
+              qa[4 * half + 1] = qv.y * rq * fexp(gv.y);
+              qa[4 * half + 2] = qv.z * rq * fexp(gv.z);
+              qa[4 * half + 3] = qv.w * rq * fexp(gv.w);
+            }
+            store8<false>(KN.qa, r, 32 * kb + 8 * g, qa);
+          }
+          {
+            // Ka^T and Kl^T: channel cc, rows 8 hf .. 8 hf + 7
+            const int cc = u >> 1, hf = u & 1;
+            const float gend = sm.g15[cc];
+            float ka[8], kl[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+              const int r = 8 * hf + v;
+              const float kh = sm.ak[r][cc] * sm.rn[C + r];
+              const float G = sm.gam[r][cc];
+              ka[v] = kh * fexp(G);
+              kl[v] = kh * fexp(gend - G);
+            }
+            store8_hi<false>(&KN.kat[cc][8 * hf], ka);
+            store8<false>(KN.klt, cc, 8 * hf, kl);
+          }
+        }
+      }
+      lds_barrier();
+
+      // ---------------------------------------------------------- interval 4
+      if (has_next) stage();  // raw rows of chunk i + 2
+      lds_barrier();
+    }
+
+    // conv history of q, k, v -> ring
+    if (a.ring_out && role < 3) {
+      float* rout = a.ring_out + static_cast<int64_t>(n) * 3 * Hd * kRingTaps;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) rout[(role * Hd + c) * kRingTaps + j] = hist[j];
+    }
+  } else {
+    // ============================================================== consumer waves
+    // The consumers carry the serial chain through the state; the SIMD arbiter favours
+    // older waves (the producers), so raise the consumers' issue priority.
+    __builtin_amdgcn_s_setprio(2);
+    f32x4_t S[8];
+    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * kHeadDim * kHeadDim;
+    if (a.state_in) {
+      const float* sp = a.state_in + sbase + opaque(4 * lq * kHeadDim + col);
+#pragma unroll
+      for (int it = 0; it < 8; ++it)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) S[it][s] = sp[(16 * it + s) * kHeadDim];
+    } else {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) S[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const float nw = a.L.norm_w[col];
+    lds_barrier();
+
+    // iteration i: consumers run chunk i, then the Gram tiles of chunk i + 1
+    for (int i = -1; i < nch; ++i) {
+      const bool has_next = i + 1 < nch;
+      KBuf& K = sm.kb[i & 1];
+      KBuf& KN = sm.kb[(i + 1) & 1];
+      f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+      bf16x4_t uh = {}, ul = {};
+
+      // ---------------------------------------------------------- interval 1
+      if (i >= 0) {
+        // T, split into bf16 hi/lo by the wave that formed it: lane (lm, lq) holds
+        // T[lm][4 lq + s]
+        const bf16x4_t th = ld<bf16x4_t>(&K.tm[0][lm][4 * lq]);
+        const bf16x4_t tl = ld<bf16x4_t>(&K.tm[1][lm][4 * lq]);
+        // U~ = T V for this wave's value tile
+        f32x4_t Ut = {0.f, 0.f, 0.f, 0.f};
+        {
+          float v4[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) v4[s] = K.V[4 * lq + s][col];
+          bf16x4_t vh, vl;
+          split_vec<4>(v4, vh, vl);
+          Ut = mma16s(th, tl, vh, vl, Ut);
+        }
+        // S as bf16 hi/lo B operands (per 32 keys: 4 lq + s, then 16 + 4 lq + s)
+        bf16x8_t sh[4], sl[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          float b8[8];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            b8[s] = S[2 * kb][s];
+            b8[4 + s] = S[2 * kb + 1][s];
+          }
+          split_vec<8>(b8, sh[kb], sl[kb]);
+        }
+        // W S, with W^T = Ka^T T^T computed two 16-key tiles at a time
+        f32x4_t ws = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const f32x4_t w0 = mma16(ld<bf16x4_t>(&K.kat[32 * kb + lm][4 * lq]), th,
+                                   f32x4_t{0.f, 0.f, 0.f, 0.f});
+          const f32x4_t w1 = mma16(ld<bf16x4_t>(&K.kat[32 * kb + 16 + lm][4 * lq]), th,
+                                   f32x4_t{0.f, 0.f, 0.f, 0.f});
+          bf16x8_t wb;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            wb[s] = static_cast<__bf16>(w0[s]);
+            wb[4 + s] = static_cast<__bf16>(w1[s]);
+          }
+          ws = mma32(wb, sh[kb], ws);
+        }
+        const f32x4_t U = Ut - ws;
+        {
+          float u4[4] = {U[0], U[1], U[2], U[3]};
+          split_vec<4>(u4, uh, ul);
+        }
+        // O = Qa S + P U
+        f32x4_t o1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int o = 32 * kb + 8 * lq;
+          const bf16x8_t qh = ld<bf16x8_t>(&K.qa[0][lm][o]);
+          const bf16x8_t ql = ld<bf16x8_t>(&K.qa[1][lm][o]);
+          O = mma32(qh, sh[kb], O);
+          o1 = mma32(qh, sl[kb], o1);
+          o1 = mma32(ql, sh[kb], o1);
+        }
+        O = mma16s(ld<bf16x4_t>(&K.p[0][lm][4 * lq]), ld<bf16x4_t>(&K.p[1][lm][4 * lq]), uh, ul, O);
+        O += o1;
+        float ss[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) ss[s] = row_sum16(O[s] * O[s]);
+        if (lm == 0)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) sm.ss[cw][4 * lq + s] = ss[s];
+      }
+      lds_barrier();
+
+      // ---------------------------------------------------------- interval 2
+      if (i >= 0) {
+        // gated RMSNorm of the chunk's output rows and the store
+        const int L = min(C, T - i * C);
+        float tot[4] = {0.f, 0.f, 0.f, 0.f};
+        uint16_t gr[4];
+#pragma unroll
+        for (int wv = 0; wv < CWN; ++wv) {
+          const float4 s4 = *reinterpret_cast<const float4*>(&sm.ss[wv][4 * lq]);
+          tot[0] += s4.x;
+          tot[1] += s4.y;
+          tot[2] += s4.z;
+          tot[3] += s4.w;
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) gr[s] = K.graw[4 * lq + s][col];
+        bf16_t* po = static_cast<bf16_t*>(a.out) + (t0 + i * C + 4 * lq) * Hd +
+                     static_cast<int64_t>(h) * kHeadDim + col;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if (4 * lq + s < L) {
+            const float rr = 1.0f / sqrtf(tot[s] * (1.0f / kHeadDim) + a.L.rms_eps);
+            const float g = fsigmoid(bf16_to_f32(gr[s]));
+            po->bits = f32_to_bf16(nw * O[s] * rr * g);
+          }
+          po += Hd;
+        }
+        // S = Diag(exp(Gcum_C)) S + Kl^T U
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const float4 e4 = *reinterpret_cast<const float4*>(&K.eg15[16 * it + 4 * lq]);
+          S[it][0] *= e4.x;
+          S[it][1] *= e4.y;
+          S[it][2] *= e4.z;
+          S[it][3] *= e4.w;
+          S[it] = mma16s(ld<bf16x4_t>(&K.klt[0][16 * it + lm][4 * lq]),
+                         ld<bf16x4_t>(&K.klt[1][16 * it + lm][4 * lq]), uh, ul, S[it]);
+        }
+      }
+      lds_barrier();
+
+      // ---------------------------------------------------------- interval 3 (producers only)
+      lds_barrier();
+
+      // ---------------------------------------------------------- interval 4
+      if (has_next && cw < 2) {
+        // Gram tiles of chunk i + 1: consumer wave 0 -> A = Kp Km^T (strict lower, times
+        // beta_r); consumer wave 1 -> P = Qp Km^T (lower incl.)
+        const __bf16(*Xh)[OPP] = cw == 0 ? sm.kp[0] : sm.qp[0];
+        const __bf16(*Xl)[OPP] = cw == 0 ? sm.kp[1] : sm.qp[1];
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < kHeadDim / 32; ++kb) {
+          const int o = 32 * kb + 8 * lq;
+          const bf16x8_t xh = ld<bf16x8_t>(&Xh[lm][o]), xl = ld<bf16x8_t>(&Xl[lm][o]);
+          const bf16x8_t mh = ld<bf16x8_t>(&sm.km[0][lm][o]), ml = ld<bf16x8_t>(&sm.km[1][lm][o]);
+          acc = mma32(xh, mh, acc);
+          a1 = mma32(xh, ml, a1);
+          a1 = mma32(xl, mh, a1);
+        }
+        acc += a1;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int r = 4 * lq + s, j = lm;
+          if (cw == 0) {
+            sm.A[r][j] = (j < r) ? KN.beta[r] * acc[s] : 0.f;
+          } else {
+            split_store(&KN.p[0][r][j], &KN.p[1][r][j], (j <= r) ? acc[s] : 0.f);
+          }
+        }
+        if (cw == 0) {
+          // T = (I + A)^-1 Diag(beta) by elimination with rows spread over lanes (DPP
+          // broadcasts inside each 16-lane row); A[r][j] = 0 for j >= r, so the update
+          // is unconditional.  The wave reads back only what it wrote itself.
+          float arow[C], tt[4];
+#pragma unroll
+          for (int j = 0; j < C; j += 4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(&sm.A[lm][j]);
+            arow[j] = v4.x;
+            arow[j + 1] = v4.y;
+            arow[j + 2] = v4.z;
+            arow[j + 3] = v4.w;
+          }
+          const float bl = KN.beta[lm];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) tt[s] = (4 * lq + s == lm) ? bl : 0.f;
+          eliminate<0>(tt, arow);
+          bf16x4_t th, tl;
+          split_vec<4>(tt, th, tl);
+          *reinterpret_cast<bf16x4_t*>(&KN.tm[0][lm][4 * lq]) = th;
+          *reinterpret_cast<bf16x4_t*>(&KN.tm[1][lm][4 * lq]) = tl;
+        }
+      }
+      lds_barrier();
+    }
+
+    if (a.state_out) {
+      float* sp = a.state_out + sbase + opaque(4 * lq * kHeadDim + col);
+#pragma unroll
+      for (int it = 0; it < 8; ++it)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sp[(16 * it + s) * kHeadDim] = S[it][s];
+    }
+  }
+}
+
+#undef KDA_PC_SRC
+#undef KDA_PC_DST
+#undef KDA_PC_OK
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, const int32_t* order_host, hipStream_t stream) {
+  PcOrder ord;
+  const int nord = a.num_seqs < kMaxOrdered ? a.num_seqs : kMaxOrdered;
+  for (int i = 0; i < kMaxOrdered; ++i) ord.idx[i] = i < nord ? order_host[i] : 0;
+  const dim3 grid(static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.L.H));
+  hipLaunchKernelGGL(prefill_pc_kernel, grid, dim3(NT), 0, stream, a, ord);
+  return hipGetLastError();
+}
+
+}  // namespace kda

@@ -106,8 +106,8 @@ size_t kda_prefill_workspace_bytes(const kda_layer* layer, kda_dtype io, int32_t
  *   ring_out  fp32 [num_seqs][3 * H * d][kernel - 1] or NULL; may equal ring_in
  *   workspace device buffer of at least kda_prefill_workspace_bytes() bytes (may be NULL
  *             when that is 0).
- * Partial overlap between inputs and outputs is invalid.  State pointers must be 16-byte
- * aligned.
+ * Partial overlap between inputs and outputs is invalid.  State pointers and q, k, v, z,
+ * gate must be 16-byte aligned (the kernel reads activation rows in 16-byte pieces).
  */
 kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
                        const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
