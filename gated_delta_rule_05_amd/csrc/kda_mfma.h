@@ -54,6 +54,16 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane
+// l's bytes land at lds_wave_base + 16 l, so one wave fills 1 KiB.  lds_wave_base must be
+// wave-uniform (it goes to M0).  Completion is counted by vmcnt, not lgkmcnt: the issuing
+// wave waits with wait_vm() before the barrier that publishes the data.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                   16, 0, 0);
+}
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Hides a value from the optimiser so that address arithmetic is recomputed where it is
 // used instead of being kept live (in 64-bit registers) across the whole kernel.
 __device__ __forceinline__ int opaque(int x) {

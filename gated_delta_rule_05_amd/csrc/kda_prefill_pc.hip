@@ -6,8 +6,8 @@
 // gate" "Why" for the 16-token tile bound), mapped so that the two kinds of work overlap:
 //
 //   * 8 producer waves build everything chunk c+1 needs from its raw rows alone: short
-//     conv + SiLU, gate and Gcum, q/k norms, MFMA-ready operands (bf16 hi/lo), and the
-//     next-but-one chunk's raw rows are fetched meanwhile (16-byte loads staged in LDS);
+//     conv + SiLU, gate and Gcum, q/k norms, MFMA-ready operands (bf16 hi/lo), while the
+//     next-but-one chunk's raw rows stream from HBM straight into LDS;
 //   * 8 consumer waves run chunk c's state pass, one 16-column value tile of the fp32
 //     128x128 state each, held in MFMA accumulators for the whole sequence: U~ = T V,
 //     W^T = Ka^T T^T (landing in the A-operand layout of W.S), U = U~ - W S,
@@ -36,7 +36,6 @@ constexpr int NT = 64 * (PW + CWN);
 constexpr int LDP = 132;               // fp32 row stride of [16][128] arrays
 constexpr int OPP = 136;               // bf16 row stride of [16][128] operands
 constexpr int KTP = 24;                // bf16 row stride of [128][16] operands
-constexpr int RWP = 136;               // row stride of the raw staging rows (bf16 bits)
 
 struct PcOrder {
   int32_t idx[kMaxOrdered];
@@ -52,12 +51,12 @@ struct alignas(16) KBuf {
   float V[C][LDP];              // V = silu(conv v)
   float eg15[kHeadDim];         // exp(Gcum at the chunk end)
   float beta[C];
-  uint16_t graw[C][RWP];        // raw output-gate bits
+  uint16_t graw[C][OPP];        // raw output-gate bits
 };
 
 struct alignas(16) PcSmem {
+  uint16_t raw[5][C][kHeadDim]; // raw rows of q, k, v, z, gate, unpadded: loaded by LDS DMA
   KBuf kb[2];
-  uint16_t raw[5][C][RWP];      // staged raw rows of q, k, v, z, gate
   uint16_t braw[C];             // staged raw beta
   float aq[C][LDP];             // silu(conv q)
   float ak[C][LDP];             // silu(conv k)
@@ -92,7 +91,8 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
   const int lm = lane & 15;
   const int lq = lane >> 4;
   const bool producer = wave < PW;
-  // producers: role 0 = q, 1 = k, 2 = v, 3 = z and gate, over 128 channels each
+  // producers: role 0 = q, 1 = k, 2 = v, 3 = z and gate, over 128 channels each (two
+  // waves per role, so the role is wave-uniform)
   const int role = (t >> 7) & 3;
   const int ch = t & (kHeadDim - 1);
   const int64_t c = static_cast<int64_t>(h) * kHeadDim + ch;
@@ -102,8 +102,9 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 
   if (producer) {
     // ============================================================== producer waves
+    const int urole = __builtin_amdgcn_readfirstlane(role);
     float w[4] = {0.f, 0.f, 0.f, 0.f}, hist[3] = {0.f, 0.f, 0.f};
-    if (role < 3) {
+    if (urole < 3) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) w[j] = a.L.conv_w[(role * Hd + c) * kConvTaps + j];
       if (a.ring_in) {
@@ -116,12 +117,13 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     const float ascale = expf(a.L.A_log[h]);
     const float lb = a.L.lower_bound;
 
-    // raw-row prefetch: 5 planes x 16 rows x 16 segments of 16 bytes over 512 threads
+    // Raw rows of a chunk, straight into LDS: 5 planes x 16 rows x 16 pieces of 16 bytes.
+    // Piece s (plane s / 256, row (s / 16) % 16, bytes 16 (s % 16) of the row) lands at
+    // byte 16 s of sm.raw, so the 64 pieces of one wave instruction are 1 KiB contiguous,
+    // as the instruction writes them.  Rows past the end of a sequence re-read its last row.
     constexpr int SPR = kHeadDim * 2 / 16;
     constexpr int NSEG = 5 * C * SPR;
-    static_assert((NSEG + PT - 1) / PT == 3, "three prefetch registers");
-    static_assert((C * SPR) % 64 == 0, "a wave's segments must fall in one plane");
-    uint4 seg0, seg1, seg2;
+    static_assert(NSEG % 64 == 0 && (C * SPR) % 64 == 0, "a wave's pieces fall in one plane");
     uint16_t braw = 0;
     const char* const pq = static_cast<const char*>(a.q);
     const char* const pk = static_cast<const char*>(a.k);
@@ -129,42 +131,28 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     const char* const pz = static_cast<const char*>(a.z);
     const char* const pgt = static_cast<const char*>(a.gate);
     const bf16_t* const x_b = static_cast<const bf16_t*>(a.beta);
-#define KDA_PC_SRC(k, c0n, Ln)                                                              \
-  ([&]() -> const uint4* {                                                                  \
-    const int sidx = t + (k) * PT;                                                          \
-    const int pl = __builtin_amdgcn_readfirstlane(sidx / (C * SPR));                        \
-    const int rem = sidx % (C * SPR);                                                       \
-    const int r = rem / SPR, part = rem % SPR;                                              \
-    const char* base = pl == 0 ? pq : pl == 1 ? pk : pl == 2 ? pv : pl == 3 ? pz : pgt;     \
-    return reinterpret_cast<const uint4*>(                                                  \
-        base + ((t0 + (c0n) + min(r, (Ln) - 1)) * Hd + static_cast<int64_t>(h) * kHeadDim) * 2 + \
-        16 * part);                                                                         \
-  }())
-#define KDA_PC_DST(k)                                                                       \
-  ([&]() -> uint4* {                                                                        \
-    const int sidx = t + (k) * PT;                                                          \
-    const int pl = sidx / (C * SPR), rem = sidx % (C * SPR);                                \
-    const int r = rem / SPR, part = rem % SPR;                                              \
-    return reinterpret_cast<uint4*>(&sm.raw[pl][r][part * 8]);                              \
-  }())
-#define KDA_PC_OK(k) (t + (k) * PT < NSEG)
+    const int row_bytes = static_cast<int>(Hd) * 2;
     auto prefetch = [&](int c0n) __attribute__((always_inline)) {
       const int Ln = min(C, T - c0n);
-      if (KDA_PC_OK(0)) seg0 = *KDA_PC_SRC(0, c0n, Ln);
-      if (KDA_PC_OK(1)) seg1 = *KDA_PC_SRC(1, c0n, Ln);
-      if (KDA_PC_OK(2)) seg2 = *KDA_PC_SRC(2, c0n, Ln);
+#pragma unroll
+      for (int k = 0; k < (NSEG + PT - 1) / PT; ++k) {
+        const int s0 = __builtin_amdgcn_readfirstlane(64 * wave + k * PT);
+        if (s0 < NSEG) {
+          const int pl = s0 / (C * SPR);
+          const int rem = s0 + lane - pl * (C * SPR);
+          const char* base = pl == 0 ? pq : pl == 1 ? pk : pl == 2 ? pv : pl == 3 ? pz : pgt;
+          base += ((t0 + c0n) * Hd + static_cast<int64_t>(h) * kHeadDim) * 2;
+          const int off = min(rem / SPR, Ln - 1) * row_bytes + 16 * (rem % SPR);
+          lds_dma16(base + off, &sm.raw[0][0][0] + 8 * s0);
+        }
+      }
       if (t < C) braw = x_b[(t0 + c0n + min(t, Ln - 1)) * H + h].bits;
-    };
-    auto stage = [&]() __attribute__((always_inline)) {
-      if (KDA_PC_OK(0)) *KDA_PC_DST(0) = seg0;
-      if (KDA_PC_OK(1)) *KDA_PC_DST(1) = seg1;
-      if (KDA_PC_OK(2)) *KDA_PC_DST(2) = seg2;
-      if (t < C) sm.braw[t] = braw;
     };
 
     if (T > 0) {
       prefetch(0);
-      stage();
+      wait_vm();
+      if (t < C) sm.braw[t] = braw;
     }
     lds_barrier();
 
@@ -176,55 +164,74 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 
       // ---------------------------------------------------------- interval 1
       if (has_next) {
-        // conv + SiLU with the history in registers; gate and Gcum; raw gate; beta
-        // all raw values first: the reads are independent of the stores below, and
-        // issuing them together keeps one LDS round trip per chunk instead of per row
+        // conv + SiLU with the history in registers; gate and Gcum; raw gate; beta.
+        // All raw values are read first (one LDS round trip per chunk).  Every chunk but
+        // a sequence's last is full, and takes a path without per-row liveness tests so
+        // that the rows' exp/rcp chains interleave.
         uint16_t xr[C], xg[C];
 #pragma unroll
-        for (int r = 0; r < C; ++r) xr[r] = sm.raw[role][r][ch];
-        if (role == 3) {
+        for (int r = 0; r < C; ++r) xr[r] = sm.raw[urole][r][ch];
+        if (urole == 3) {
 #pragma unroll
           for (int r = 0; r < C; ++r) xg[r] = sm.raw[4][r][ch];
         }
-        if (role < 3) {
+        const bool full = Ln == C;
+        if (urole < 3) {
+          float(*dst)[LDP] = urole == 0 ? sm.aq : urole == 1 ? sm.ak : KN.V;
+          if (full) {
 #pragma unroll
-          for (int r = 0; r < C; ++r) {
-            const float x = bf16_to_f32(xr[r]);
-            const float y = w[3] * x + w[0] * hist[0] + w[1] * hist[1] + w[2] * hist[2];
-            const bool live = r < Ln;
-            if (live) {
+            for (int r = 0; r < C; ++r) {
+              const float x = bf16_to_f32(xr[r]);
+              const float y = w[3] * x + w[0] * hist[0] + w[1] * hist[1] + w[2] * hist[2];
               hist[0] = hist[1];
               hist[1] = hist[2];
               hist[2] = x;
+              dst[r][ch] = y * fsigmoid(y);
             }
-            const float act = live ? y * fsigmoid(y) : 0.f;
-            if (role == 0)
-              sm.aq[r][ch] = act;
-            else if (role == 1)
-              sm.ak[r][ch] = act;
-            else
-              KN.V[r][ch] = act;
+          } else {
+#pragma unroll
+            for (int r = 0; r < C; ++r) {
+              const float x = bf16_to_f32(xr[r]);
+              const float y = w[3] * x + w[0] * hist[0] + w[1] * hist[1] + w[2] * hist[2];
+              const bool live = r < Ln;
+              if (live) {
+                hist[0] = hist[1];
+                hist[1] = hist[2];
+                hist[2] = x;
+              }
+              dst[r][ch] = live ? y * fsigmoid(y) : 0.f;
+            }
           }
         } else {
           float G = 0.f;
+          if (full) {
 #pragma unroll
-          for (int r = 0; r < C; ++r) {
-            const bool live = r < Ln;
-            G += live ? lb * fsigmoid(ascale * (bf16_to_f32(xr[r]) + dtb)) : 0.f;
-            sm.gam[r][ch] = G;
-            KN.graw[r][ch] = live ? xg[r] : static_cast<uint16_t>(0);
-            if (r == C / 2 - 1) sm.g7[ch] = G;
+            for (int r = 0; r < C; ++r) {
+              G += lb * fsigmoid(ascale * (bf16_to_f32(xr[r]) + dtb));
+              sm.gam[r][ch] = G;
+              KN.graw[r][ch] = xg[r];
+              if (r == C / 2 - 1) sm.g7[ch] = G;
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < C; ++r) {
+              const bool live = r < Ln;
+              G += live ? lb * fsigmoid(ascale * (bf16_to_f32(xr[r]) + dtb)) : 0.f;
+              sm.gam[r][ch] = G;
+              KN.graw[r][ch] = live ? xg[r] : static_cast<uint16_t>(0);
+              if (r == C / 2 - 1) sm.g7[ch] = G;
+            }
           }
           sm.g15[ch] = G;
           KN.eg15[ch] = fexp(G);
         }
         if (t < C) KN.beta[t] = (t < Ln) ? fsigmoid(bf16_to_f32(sm.braw[t])) : 0.f;
-        // raw rows of chunk i + 2 (the last chunk re-reads itself)
-        prefetch(min(i + 2, nch - 1) * C);
       }
       lds_barrier();
 
       // ---------------------------------------------------------- interval 2
+      // raw rows of chunk i + 2 (chunk i + 1's were consumed in interval 1)
+      if (i + 2 < nch) prefetch((i + 2) * C);
       if (has_next) {
         // q/k row norms: 16 threads per (plane, row)
         const int task = t >> 4, part = t & 15;
@@ -310,12 +317,15 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       lds_barrier();
 
       // ---------------------------------------------------------- interval 4
-      if (has_next) stage();  // raw rows of chunk i + 2
+      if (i + 2 < nch) {
+        wait_vm();  // this wave's pieces of chunk i + 2 are in LDS
+        if (t < C) sm.braw[t] = braw;
+      }
       lds_barrier();
     }
 
     // conv history of q, k, v -> ring
-    if (a.ring_out && role < 3) {
+    if (a.ring_out && urole < 3) {
       float* rout = a.ring_out + static_cast<int64_t>(n) * 3 * Hd * kRingTaps;
 #pragma unroll
       for (int j = 0; j < 3; ++j) rout[(role * Hd + c) * kRingTaps + j] = hist[j];
@@ -524,10 +534,6 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     }
   }
 }
-
-#undef KDA_PC_SRC
-#undef KDA_PC_DST
-#undef KDA_PC_OK
 
 }  // namespace
 
