@@ -9,11 +9,12 @@
 //     conv + SiLU, gate and Gcum, q/k norms, MFMA-ready operands (bf16 hi/lo), while the
 //     next-but-one chunk's raw rows stream from HBM straight into LDS;
 //   * 8 consumer waves run chunk c's state pass, one 16-column value tile of the fp32
-//     128x128 state each, held in MFMA accumulators for the whole sequence: U~ = T V,
-//     W^T = Ka^T T^T (landing in the A-operand layout of W.S), U = U~ - W S,
-//     O = Qa S + P U, the gated RMSNorm epilogue, S <- Diag(e^Gcum_C) S + Kl^T U; and,
-//     once chunk c+1's operands are ready, its Gram tiles and T = (I + A)^-1 Diag(beta)
-//     (DPP elimination, once per chunk).
+//     128x128 state each, held in MFMA accumulators for the whole sequence:
+//     T = (I + A)^-1 Diag(beta) (DPP elimination, one wave, once per chunk) beside O = Qa S;
+//     then U~ = T V, W^T = Ka^T T^T (landing in the A-operand layout of W.S),
+//     U = U~ - W S, O += P U; then the gated RMSNorm epilogue and
+//     S <- Diag(e^Gcum_C) S + Kl^T U; and, once chunk c+1's operands are ready, its Gram
+//     tiles.
 //
 // Operands that cross from producers to consumers are double-buffered by chunk parity.
 // Four LDS barriers per chunk; each wave works in every interval it can.  With 16 waves
@@ -51,11 +52,11 @@ struct alignas(16) KBuf {
   float V[C][LDP];              // V = silu(conv v)
   float eg15[kHeadDim];         // exp(Gcum at the chunk end)
   float beta[C];
-  uint16_t graw[C][OPP];        // raw output-gate bits
+  uint16_t graw[C][kHeadDim];   // raw output-gate bits, unpadded: loaded by LDS DMA
 };
 
 struct alignas(16) PcSmem {
-  uint16_t raw[5][C][kHeadDim]; // raw rows of q, k, v, z, gate, unpadded: loaded by LDS DMA
+  uint16_t raw[4][C][kHeadDim]; // raw rows of q, k, v, z, unpadded: loaded by LDS DMA
   KBuf kb[2];
   uint16_t braw[C];             // staged raw beta
   float aq[C][LDP];             // silu(conv q)
@@ -72,6 +73,16 @@ struct alignas(16) PcSmem {
 };
 
 static_assert(sizeof(PcSmem) <= 160 * 1024, "LDS budget of one workgroup");
+// 16-byte LDS accesses (DMA targets, float4 and bf16x8 reads)
+static_assert(offsetof(PcSmem, raw) % 16 == 0 && offsetof(PcSmem, kb) % 16 == 0 &&
+                  sizeof(KBuf) % 16 == 0 && offsetof(KBuf, graw) % 16 == 0 &&
+                  offsetof(KBuf, qa) % 16 == 0 && offsetof(KBuf, eg15) % 16 == 0 &&
+                  offsetof(KBuf, V) % 16 == 0 && offsetof(PcSmem, ss) % 16 == 0 &&
+                  offsetof(PcSmem, A) % 16 == 0 && offsetof(PcSmem, aq) % 16 == 0 &&
+                  offsetof(PcSmem, ak) % 16 == 0 && offsetof(PcSmem, gam) % 16 == 0 &&
+                  offsetof(PcSmem, g7) % 16 == 0 && offsetof(PcSmem, qp) % 16 == 0 &&
+                  offsetof(PcSmem, kp) % 16 == 0 && offsetof(PcSmem, km) % 16 == 0,
+              "16-byte aligned LDS members");
 
 __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder order) {
   __shared__ PcSmem sm;
@@ -117,13 +128,16 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     const float ascale = expf(a.L.A_log[h]);
     const float lb = a.L.lower_bound;
 
-    // Raw rows of a chunk, straight into LDS: 5 planes x 16 rows x 16 pieces of 16 bytes.
-    // Piece s (plane s / 256, row (s / 16) % 16, bytes 16 (s % 16) of the row) lands at
-    // byte 16 s of sm.raw, so the 64 pieces of one wave instruction are 1 KiB contiguous,
-    // as the instruction writes them.  Rows past the end of a sequence re-read its last row.
+    // Raw rows of a chunk, straight into LDS, as 16 pieces of 16 bytes per row.  Planes q,
+    // k, v, z go to sm.raw: piece s (plane s / 256, row (s / 16) % 16, bytes 16 (s % 16) of
+    // the row) lands at byte 16 s, so the 64 pieces of one wave instruction are 1 KiB
+    // contiguous, as the instruction writes them.  The output-gate plane goes to the
+    // consumers' double-buffered copy in the same way.  Rows past the end of a sequence
+    // re-read its last row.
     constexpr int SPR = kHeadDim * 2 / 16;
-    constexpr int NSEG = 5 * C * SPR;
-    static_assert(NSEG % 64 == 0 && (C * SPR) % 64 == 0, "a wave's pieces fall in one plane");
+    constexpr int NSEG = 4 * C * SPR;
+    static_assert(NSEG == 2 * PT && (C * SPR) % 64 == 0, "two pieces per producer thread");
+    static_assert(C * SPR == 4 * 64, "the gate plane is four waves' pieces");
     uint16_t braw = 0;
     const char* const pq = static_cast<const char*>(a.q);
     const char* const pk = static_cast<const char*>(a.k);
@@ -132,25 +146,35 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     const char* const pgt = static_cast<const char*>(a.gate);
     const bf16_t* const x_b = static_cast<const bf16_t*>(a.beta);
     const int row_bytes = static_cast<int>(Hd) * 2;
+    const int64_t head_bytes = static_cast<int64_t>(h) * kHeadDim * 2;
     auto prefetch = [&](int c0n) __attribute__((always_inline)) {
       const int Ln = min(C, T - c0n);
 #pragma unroll
-      for (int k = 0; k < (NSEG + PT - 1) / PT; ++k) {
+      for (int k = 0; k < 2; ++k) {
         const int s0 = __builtin_amdgcn_readfirstlane(64 * wave + k * PT);
-        if (s0 < NSEG) {
-          const int pl = s0 / (C * SPR);
-          const int rem = s0 + lane - pl * (C * SPR);
-          const char* base = pl == 0 ? pq : pl == 1 ? pk : pl == 2 ? pv : pl == 3 ? pz : pgt;
-          base += ((t0 + c0n) * Hd + static_cast<int64_t>(h) * kHeadDim) * 2;
-          const int off = min(rem / SPR, Ln - 1) * row_bytes + 16 * (rem % SPR);
-          lds_dma16(base + off, &sm.raw[0][0][0] + 8 * s0);
-        }
+        const int pl = s0 / (C * SPR);
+        const int rem = s0 + lane - pl * (C * SPR);
+        const char* base = pl == 0 ? pq : pl == 1 ? pk : pl == 2 ? pv : pz;
+        base += (t0 + c0n) * Hd * 2 + head_bytes;
+        const int off = min(rem / SPR, Ln - 1) * row_bytes + 16 * (rem % SPR);
+        lds_dma16(base + off, &sm.raw[0][0][0] + 8 * s0);
       }
       if (t < C) braw = x_b[(t0 + c0n + min(t, Ln - 1)) * H + h].bits;
+    };
+    auto prefetch_gate = [&](int c0n, KBuf& dst) __attribute__((always_inline)) {
+      if (__builtin_amdgcn_readfirstlane(wave) < 4) {
+        const int Ln = min(C, T - c0n);
+        const int s0 = __builtin_amdgcn_readfirstlane(64 * wave);
+        const int rem = s0 + lane;
+        const char* base = pgt + (t0 + c0n) * Hd * 2 + head_bytes;
+        const int off = min(rem / SPR, Ln - 1) * row_bytes + 16 * (rem % SPR);
+        lds_dma16(base + off, &dst.graw[0][0] + 8 * s0);
+      }
     };
 
     if (T > 0) {
       prefetch(0);
+      prefetch_gate(0, sm.kb[0]);
       wait_vm();
       if (t < C) sm.braw[t] = braw;
     }
@@ -164,17 +188,13 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 
       // ---------------------------------------------------------- interval 1
       if (has_next) {
-        // conv + SiLU with the history in registers; gate and Gcum; raw gate; beta.
+        // conv + SiLU with the history in registers; gate and Gcum; beta.
         // All raw values are read first (one LDS round trip per chunk).  Every chunk but
         // a sequence's last is full, and takes a path without per-row liveness tests so
         // that the rows' exp/rcp chains interleave.
-        uint16_t xr[C], xg[C];
+        uint16_t xr[C];
 #pragma unroll
         for (int r = 0; r < C; ++r) xr[r] = sm.raw[urole][r][ch];
-        if (urole == 3) {
-#pragma unroll
-          for (int r = 0; r < C; ++r) xg[r] = sm.raw[4][r][ch];
-        }
         const bool full = Ln == C;
         if (urole < 3) {
           float(*dst)[LDP] = urole == 0 ? sm.aq : urole == 1 ? sm.ak : KN.V;
@@ -209,7 +229,6 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
             for (int r = 0; r < C; ++r) {
               G += lb * fsigmoid(ascale * (bf16_to_f32(xr[r]) + dtb));
               sm.gam[r][ch] = G;
-              KN.graw[r][ch] = xg[r];
               if (r == C / 2 - 1) sm.g7[ch] = G;
             }
           } else {
@@ -218,7 +237,6 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
               const bool live = r < Ln;
               G += live ? lb * fsigmoid(ascale * (bf16_to_f32(xr[r]) + dtb)) : 0.f;
               sm.gam[r][ch] = G;
-              KN.graw[r][ch] = live ? xg[r] : static_cast<uint16_t>(0);
               if (r == C / 2 - 1) sm.g7[ch] = G;
             }
           }
@@ -320,6 +338,8 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       if (i + 2 < nch) {
         wait_vm();  // this wave's pieces of chunk i + 2 are in LDS
         if (t < C) sm.braw[t] = braw;
+        // chunk i's output gate has been read by now; its buffer takes chunk i + 2's
+        prefetch_gate((i + 2) * C, sm.kb[(i + 2) & 1]);
       }
       lds_barrier();
     }
@@ -356,12 +376,62 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       KBuf& K = sm.kb[i & 1];
       KBuf& KN = sm.kb[(i + 1) & 1];
       f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+      bf16x8_t sh[4], sl[4];
       bf16x4_t uh = {}, ul = {};
 
       // ---------------------------------------------------------- interval 1
       if (i >= 0) {
-        // T, split into bf16 hi/lo by the wave that formed it: lane (lm, lq) holds
-        // T[lm][4 lq + s]
+        if (cw == 0) {
+          // T = (I + A)^-1 Diag(beta) by elimination with rows spread over lanes (DPP
+          // broadcasts inside each 16-lane row); A[r][j] = 0 for j >= r, so the update
+          // is unconditional.  Lane (lm, lq) ends up with T[lm][4 lq + s].
+          float arow[C], tt[4];
+#pragma unroll
+          for (int j = 0; j < C; j += 4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(&sm.A[lm][j]);
+            arow[j] = v4.x;
+            arow[j + 1] = v4.y;
+            arow[j + 2] = v4.z;
+            arow[j + 3] = v4.w;
+          }
+          const float bl = K.beta[lm];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) tt[s] = (4 * lq + s == lm) ? bl : 0.f;
+          eliminate<0>(tt, arow);
+          bf16x4_t th, tl;
+          split_vec<4>(tt, th, tl);
+          *reinterpret_cast<bf16x4_t*>(&K.tm[0][lm][4 * lq]) = th;
+          *reinterpret_cast<bf16x4_t*>(&K.tm[1][lm][4 * lq]) = tl;
+        }
+        // S as bf16 hi/lo B operands (per 32 keys: 4 lq + s, then 16 + 4 lq + s)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          float b8[8];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            b8[s] = S[2 * kb][s];
+            b8[4 + s] = S[2 * kb + 1][s];
+          }
+          split_vec<8>(b8, sh[kb], sl[kb]);
+        }
+        // O = Qa S, both split
+        f32x4_t o1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int o = 32 * kb + 8 * lq;
+          const bf16x8_t qh = ld<bf16x8_t>(&K.qa[0][lm][o]);
+          const bf16x8_t ql = ld<bf16x8_t>(&K.qa[1][lm][o]);
+          O = mma32(qh, sh[kb], O);
+          o1 = mma32(qh, sl[kb], o1);
+          o1 = mma32(ql, sh[kb], o1);
+        }
+        O += o1;
+      }
+      lds_barrier();
+
+      // ---------------------------------------------------------- interval 2
+      if (i >= 0) {
+        // T, split into bf16 hi/lo: lane (lm, lq) holds T[lm][4 lq + s]
         const bf16x4_t th = ld<bf16x4_t>(&K.tm[0][lm][4 * lq]);
         const bf16x4_t tl = ld<bf16x4_t>(&K.tm[1][lm][4 * lq]);
         // U~ = T V for this wave's value tile
@@ -373,18 +443,6 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           bf16x4_t vh, vl;
           split_vec<4>(v4, vh, vl);
           Ut = mma16s(th, tl, vh, vl, Ut);
-        }
-        // S as bf16 hi/lo B operands (per 32 keys: 4 lq + s, then 16 + 4 lq + s)
-        bf16x8_t sh[4], sl[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          float b8[8];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            b8[s] = S[2 * kb][s];
-            b8[4 + s] = S[2 * kb + 1][s];
-          }
-          split_vec<8>(b8, sh[kb], sl[kb]);
         }
         // W S, with W^T = Ka^T T^T computed two 16-key tiles at a time
         f32x4_t ws = {0.f, 0.f, 0.f, 0.f};
@@ -407,29 +465,17 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           float u4[4] = {U[0], U[1], U[2], U[3]};
           split_vec<4>(u4, uh, ul);
         }
-        // O = Qa S + P U
-        f32x4_t o1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const int o = 32 * kb + 8 * lq;
-          const bf16x8_t qh = ld<bf16x8_t>(&K.qa[0][lm][o]);
-          const bf16x8_t ql = ld<bf16x8_t>(&K.qa[1][lm][o]);
-          O = mma32(qh, sh[kb], O);
-          o1 = mma32(qh, sl[kb], o1);
-          o1 = mma32(ql, sh[kb], o1);
-        }
+        // O += P U
         O = mma16s(ld<bf16x4_t>(&K.p[0][lm][4 * lq]), ld<bf16x4_t>(&K.p[1][lm][4 * lq]), uh, ul, O);
-        O += o1;
         float ss[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) ss[s] = row_sum16(O[s] * O[s]);
         if (lm == 0)
-#pragma unroll
-          for (int s = 0; s < 4; ++s) sm.ss[cw][4 * lq + s] = ss[s];
+          *reinterpret_cast<float4*>(&sm.ss[cw][4 * lq]) = make_float4(ss[0], ss[1], ss[2], ss[3]);
       }
       lds_barrier();
 
-      // ---------------------------------------------------------- interval 2
+      // ---------------------------------------------------------- interval 3
       if (i >= 0) {
         // gated RMSNorm of the chunk's output rows and the store
         const int L = min(C, T - i * C);
@@ -450,7 +496,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           if (4 * lq + s < L) {
-            const float rr = 1.0f / sqrtf(tot[s] * (1.0f / kHeadDim) + a.L.rms_eps);
+            const float rr = __builtin_amdgcn_rsqf(tot[s] * (1.0f / kHeadDim) + a.L.rms_eps);
             const float g = fsigmoid(bf16_to_f32(gr[s]));
             po->bits = f32_to_bf16(nw * O[s] * rr * g);
           }
@@ -470,13 +516,11 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       }
       lds_barrier();
 
-      // ---------------------------------------------------------- interval 3 (producers only)
-      lds_barrier();
-
       // ---------------------------------------------------------- interval 4
       if (has_next && cw < 2) {
         // Gram tiles of chunk i + 1: consumer wave 0 -> A = Kp Km^T (strict lower, times
-        // beta_r); consumer wave 1 -> P = Qp Km^T (lower incl.)
+        // beta_r), eliminated in the next interval 1; consumer wave 1 -> P = Qp Km^T
+        // (lower incl.)
         const __bf16(*Xh)[OPP] = cw == 0 ? sm.kp[0] : sm.qp[0];
         const __bf16(*Xl)[OPP] = cw == 0 ? sm.kp[1] : sm.qp[1];
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
@@ -498,28 +542,6 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           } else {
             split_store(&KN.p[0][r][j], &KN.p[1][r][j], (j <= r) ? acc[s] : 0.f);
           }
-        }
-        if (cw == 0) {
-          // T = (I + A)^-1 Diag(beta) by elimination with rows spread over lanes (DPP
-          // broadcasts inside each 16-lane row); A[r][j] = 0 for j >= r, so the update
-          // is unconditional.  The wave reads back only what it wrote itself.
-          float arow[C], tt[4];
-#pragma unroll
-          for (int j = 0; j < C; j += 4) {
-            const float4 v4 = *reinterpret_cast<const float4*>(&sm.A[lm][j]);
-            arow[j] = v4.x;
-            arow[j + 1] = v4.y;
-            arow[j + 2] = v4.z;
-            arow[j + 3] = v4.w;
-          }
-          const float bl = KN.beta[lm];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) tt[s] = (4 * lq + s == lm) ? bl : 0.f;
-          eliminate<0>(tt, arow);
-          bf16x4_t th, tl;
-          split_vec<4>(tt, th, tl);
-          *reinterpret_cast<bf16x4_t*>(&KN.tm[0][lm][4 * lq]) = th;
-          *reinterpret_cast<bf16x4_t*>(&KN.tm[1][lm][4 * lq]) = tl;
         }
       }
       lds_barrier();
