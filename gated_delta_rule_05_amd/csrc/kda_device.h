@@ -20,11 +20,9 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 }
 
 // Round to nearest, ties to even; NaN stays a quiet NaN.
+// fp32 -> bf16 bits, round to nearest even (the hardware conversion, v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 template <typename IO>

@@ -20,6 +20,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // exp(x) through the hardware base-2 exponential; relative error ~1e-6 over the ranges
 // used here (|x| <= 80).
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float fsigmoid(float x) { return frcp(1.0f + fexp(-x)); }
 
@@ -57,10 +59,19 @@ __device__ __forceinline__ void lds_barrier() {
 // 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane
 // l's bytes land at lds_wave_base + 16 l, so one wave fills 1 KiB.  lds_wave_base must be
 // wave-uniform (it goes to M0).  Completion is counted by vmcnt, not lgkmcnt: the issuing
-// wave waits with wait_vm() before the barrier that publishes the data.
+// wave waits with wait_vm() before the barrier that publishes the data.  The instruction
+// is issued from inline assembly so that the compiler does not track it: it would
+// otherwise wait for the transfer before LDS accesses it cannot prove disjoint from the
+// target, which stalls on HBM latency.  The vmcnt waits the compiler does compute for its
+// own loads stay correct (vector memory operations complete in issue order, so extra
+// ones in flight only make those waits longer).
 __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base,
-                                   16, 0, 0);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)lds_wave_base)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(lds)
+               : "memory", "m0");
 }
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -144,6 +155,20 @@ __device__ __forceinline__ void store8_hi(E* dst, const float* x) {
   }
 }
 
+// 4 consecutive values as (hi, lo) bf16 at hi[0..3], lo[0..3] (8-byte writes), or hi only.
+__device__ __forceinline__ void store4(__bf16* hi, __bf16* lo, const float* x) {
+  bf16x4_t h, l;
+  split_vec<4>(x, h, l);
+  *reinterpret_cast<bf16x4_t*>(hi) = h;
+  *reinterpret_cast<bf16x4_t*>(lo) = l;
+}
+__device__ __forceinline__ void store4_hi(__bf16* hi, const float* x) {
+  bf16x4_t h;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) h[v] = static_cast<__bf16>(x[v]);
+  *reinterpret_cast<bf16x4_t*>(hi) = h;
+}
+
 // One elimination step per row j of the 16x16 unit-lower system: every lane of a 16-lane
 // row takes row j's values from lane j of its own row (DPP broadcast).
 template <int J>
@@ -155,6 +180,17 @@ __device__ __forceinline__ void eliminate(float* tt, const float* arow) {
   }
 }
 
+// The same with lane (lm, lq) holding columns lq + 4 s (s = 0..3) of row lm.  Column c of
+// T is zero above row c, so step J can only change the values with lq + 4 s <= J: steps
+// 0..3 touch s = 0 only, 4..7 s <= 1, and so on (36 updates instead of 60).
+template <int J>
+__device__ __forceinline__ void eliminate_strided(float* tt, const float* arow) {
+  if constexpr (J < C - 1) {
+#pragma unroll
+    for (int s = 0; s <= J / 4; ++s) tt[s] -= arow[J] * row_bcast<J>(tt[s]);
+    eliminate_strided<J + 1>(tt, arow);
+  }
+}
 
 }  // namespace mf
 }  // namespace kda

@@ -6,20 +6,20 @@
 // gate" "Why" for the 16-token tile bound), mapped so that the two kinds of work overlap:
 //
 //   * 8 producer waves build everything chunk c+1 needs from its raw rows alone: short
-//     conv + SiLU, gate and Gcum, q/k norms, MFMA-ready operands (bf16 hi/lo), while the
-//     next-but-one chunk's raw rows stream from HBM straight into LDS;
+//     conv + SiLU, gate and Gcum, q/k norms, MFMA-ready operands (bf16 hi/lo) and the
+//     Gram tiles A and P, while the next-but-one chunk's raw rows stream from HBM straight
+//     into LDS; one of them also forms chunk c's T = (I + A)^-1 Diag(beta) (DPP
+//     elimination, once per chunk);
 //   * 8 consumer waves run chunk c's state pass, one 16-column value tile of the fp32
-//     128x128 state each, held in MFMA accumulators for the whole sequence:
-//     T = (I + A)^-1 Diag(beta) (DPP elimination, one wave, once per chunk) beside O = Qa S;
+//     128x128 state each, held in MFMA accumulators for the whole sequence: O = Qa S;
 //     then U~ = T V, W^T = Ka^T T^T (landing in the A-operand layout of W.S),
-//     U = U~ - W S, O += P U; then the gated RMSNorm epilogue and
-//     S <- Diag(e^Gcum_C) S + Kl^T U; and, once chunk c+1's operands are ready, its Gram
-//     tiles.
+//     U = U~ - W S, O += P U; then the gated RMSNorm epilogue; then
+//     S <- Diag(e^Gcum_C) S + Kl^T U.
 //
 // Operands that cross from producers to consumers are double-buffered by chunk parity.
-// Four LDS barriers per chunk; each wave works in every interval it can.  With 16 waves
-// per workgroup each SIMD holds two producer and two consumer waves, so the VALU-heavy
-// and MFMA-heavy halves hide each other's latencies.
+// Four LDS barriers per chunk.  With 16 waves per workgroup each SIMD holds two producer
+// and two consumer waves, so the VALU-heavy and MFMA-heavy halves hide each other's
+// latencies.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_mfma.h"
@@ -33,6 +33,13 @@ using namespace mf;
 constexpr int PW = 8;                  // producer waves
 constexpr int CWN = 8;                 // consumer waves
 constexpr int PT = 64 * PW;            // producer threads
+// Producer waves that also run the once-per-chunk jobs: the T elimination goes to a gate
+// wave (the lightest role of the conv interval, on SIMD 3), the two Gram tiles to the v
+// waves (SIMDs 0 and 1), which are otherwise idle in interval 4.  Wave w runs on SIMD
+// w % 4.
+constexpr int kElimWave = 7;
+constexpr int kGramAWave = 4;
+constexpr int kGramPWave = 5;
 constexpr int NT = 64 * (PW + CWN);
 constexpr int LDP = 132;               // fp32 row stride of [16][128] arrays
 constexpr int OPP = 136;               // bf16 row stride of [16][128] operands
@@ -52,30 +59,33 @@ struct alignas(16) KBuf {
   float V[C][LDP];              // V = silu(conv v)
   float eg15[kHeadDim];         // exp(Gcum at the chunk end)
   float beta[C];
-  uint16_t graw[C][kHeadDim];   // raw output-gate bits, unpadded: loaded by LDS DMA
 };
 
 struct alignas(16) PcSmem {
-  uint16_t raw[4][C][kHeadDim]; // raw rows of q, k, v, z, unpadded: loaded by LDS DMA
   KBuf kb[2];
   uint16_t braw[C];             // staged raw beta
   float aq[C][LDP];             // silu(conv q)
   float ak[C][LDP];             // silu(conv k)
-  float gam[C][LDP];            // Gcum
+  float gam[C][LDP];            // Gcum (log2 units)
   __bf16 qp[2][C][OPP];         // Qp = q-hat exp(Gcum - Gref), hi/lo
   __bf16 kp[2][C][OPP];         // Kp = k-hat exp(Gcum - Gref), hi/lo
   __bf16 km[2][C][OPP];         // Km = k-hat exp(Gref - Gcum), hi/lo
-  float g7[kHeadDim];           // Gcum at the chunk midpoint (Gram reference)
-  float g15[kHeadDim];          // Gcum at the chunk end
+  float g7[kHeadDim];           // Gcum at the chunk midpoint (Gram reference), log2 units
+  float g15[kHeadDim];          // Gcum at the chunk end, log2 units
+  float eg7[kHeadDim];          // exp(Gcum at the midpoint)
+  float e157[kHeadDim];         // exp(Gcum at the end - Gcum at the midpoint)
   float rn[2 * C];              // 1/|q| * d^-1/2, then 1/|k|
   float A[C][20];               // A times beta (strict lower), for the elimination
   float ss[CWN][C];             // per consumer wave, per row: sum of O^2 over its columns
 };
 
-static_assert(sizeof(PcSmem) <= 160 * 1024, "LDS budget of one workgroup");
+// The LDS DMA targets are variables of their own: the compiler then knows that the
+// loads in flight cannot alias the other LDS data, and does not wait for them before
+// every LDS read.
+constexpr int kDmaBytes = (4 + 2) * C * kHeadDim * 2;
+static_assert(sizeof(PcSmem) + kDmaBytes <= 160 * 1024, "LDS budget of one workgroup");
 // 16-byte LDS accesses (DMA targets, float4 and bf16x8 reads)
-static_assert(offsetof(PcSmem, raw) % 16 == 0 && offsetof(PcSmem, kb) % 16 == 0 &&
-                  sizeof(KBuf) % 16 == 0 && offsetof(KBuf, graw) % 16 == 0 &&
+static_assert(offsetof(PcSmem, kb) % 16 == 0 && sizeof(KBuf) % 16 == 0 &&
                   offsetof(KBuf, qa) % 16 == 0 && offsetof(KBuf, eg15) % 16 == 0 &&
                   offsetof(KBuf, V) % 16 == 0 && offsetof(PcSmem, ss) % 16 == 0 &&
                   offsetof(PcSmem, A) % 16 == 0 && offsetof(PcSmem, aq) % 16 == 0 &&
@@ -86,6 +96,10 @@ static_assert(offsetof(PcSmem, raw) % 16 == 0 && offsetof(PcSmem, kb) % 16 == 0 
 
 __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder order) {
   __shared__ PcSmem sm;
+  // raw rows of q, k, v, z of the next-but-one chunk, unpadded
+  __shared__ __attribute__((aligned(16))) uint16_t raw_lds[4][C][kHeadDim];
+  // raw output-gate rows, double-buffered by chunk parity (read by the epilogue)
+  __shared__ __attribute__((aligned(16))) uint16_t graw_lds[2][C][kHeadDim];
 
   const int H = a.L.H;
   const int rank = blockIdx.x / H;
@@ -114,6 +128,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
   if (producer) {
     // ============================================================== producer waves
     const int urole = __builtin_amdgcn_readfirstlane(role);
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
     float w[4] = {0.f, 0.f, 0.f, 0.f}, hist[3] = {0.f, 0.f, 0.f};
     if (urole < 3) {
 #pragma unroll
@@ -124,9 +139,11 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         for (int j = 0; j < 3; ++j) hist[j] = rin[(role * Hd + c) * kRingTaps + j];
       }
     }
-    const float dtb = a.L.dt_bias[c];
+    // gate: g = lb sigmoid(e^A_log (z + dt_bias)) = lb / (1 + 2^(z ga + gb)); Gcum is kept
+    // in log2 units (scaled by log2 e) so that every exponential below is one exp2
     const float ascale = expf(a.L.A_log[h]);
-    const float lb = a.L.lower_bound;
+    const float ga = -kLog2e * ascale, gb = -kLog2e * ascale * a.L.dt_bias[c];
+    const float lb2 = kLog2e * a.L.lower_bound;
 
     // Raw rows of a chunk, straight into LDS, as 16 pieces of 16 bytes per row.  Planes q,
     // k, v, z go to sm.raw: piece s (plane s / 256, row (s / 16) % 16, bytes 16 (s % 16) of
@@ -147,34 +164,42 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     const bf16_t* const x_b = static_cast<const bf16_t*>(a.beta);
     const int row_bytes = static_cast<int>(Hd) * 2;
     const int64_t head_bytes = static_cast<int64_t>(h) * kHeadDim * 2;
+    // byte offset of this lane's piece k inside a chunk (plane base and first row aside),
+    // for a full chunk and for a last chunk of Ln rows
+    auto piece_off = [&](int k, int Ln) __attribute__((always_inline)) {
+      const int s0 = 64 * wave + k * PT;
+      const int rem = (s0 + lane) % (C * SPR);
+      return min(rem / SPR, Ln - 1) * row_bytes + 16 * (rem % SPR);
+    };
+    const int off_full0 = piece_off(0, C), off_full1 = piece_off(1, C);
     auto prefetch = [&](int c0n) __attribute__((always_inline)) {
       const int Ln = min(C, T - c0n);
+      const bool full = Ln == C;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int s0 = __builtin_amdgcn_readfirstlane(64 * wave + k * PT);
         const int pl = s0 / (C * SPR);
-        const int rem = s0 + lane - pl * (C * SPR);
         const char* base = pl == 0 ? pq : pl == 1 ? pk : pl == 2 ? pv : pz;
         base += (t0 + c0n) * Hd * 2 + head_bytes;
-        const int off = min(rem / SPR, Ln - 1) * row_bytes + 16 * (rem % SPR);
-        lds_dma16(base + off, &sm.raw[0][0][0] + 8 * s0);
+        const int off = full ? (k == 0 ? off_full0 : off_full1) : piece_off(k, Ln);
+        lds_dma16(base + off, &raw_lds[0][0][0] + 8 * s0);
       }
       if (t < C) braw = x_b[(t0 + c0n + min(t, Ln - 1)) * H + h].bits;
     };
-    auto prefetch_gate = [&](int c0n, KBuf& dst) __attribute__((always_inline)) {
+    auto prefetch_gate = [&](int c0n, int buf) __attribute__((always_inline)) {
       if (__builtin_amdgcn_readfirstlane(wave) < 4) {
         const int Ln = min(C, T - c0n);
         const int s0 = __builtin_amdgcn_readfirstlane(64 * wave);
         const int rem = s0 + lane;
         const char* base = pgt + (t0 + c0n) * Hd * 2 + head_bytes;
-        const int off = min(rem / SPR, Ln - 1) * row_bytes + 16 * (rem % SPR);
-        lds_dma16(base + off, &dst.graw[0][0] + 8 * s0);
+        const int off = Ln == C ? off_full0 : min(rem / SPR, Ln - 1) * row_bytes + 16 * (rem % SPR);
+        lds_dma16(base + off, &graw_lds[buf][0][0] + 8 * s0);
       }
     };
 
     if (T > 0) {
       prefetch(0);
-      prefetch_gate(0, sm.kb[0]);
+      prefetch_gate(0, 0);
       wait_vm();
       if (t < C) sm.braw[t] = braw;
     }
@@ -194,7 +219,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         // that the rows' exp/rcp chains interleave.
         uint16_t xr[C];
 #pragma unroll
-        for (int r = 0; r < C; ++r) xr[r] = sm.raw[urole][r][ch];
+        for (int r = 0; r < C; ++r) xr[r] = raw_lds[urole][r][ch];
         const bool full = Ln == C;
         if (urole < 3) {
           float(*dst)[LDP] = urole == 0 ? sm.aq : urole == 1 ? sm.ak : KN.V;
@@ -223,27 +248,51 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
             }
           }
         } else {
-          float G = 0.f;
+          float G = 0.f, G7 = 0.f;
           if (full) {
 #pragma unroll
             for (int r = 0; r < C; ++r) {
-              G += lb * fsigmoid(ascale * (bf16_to_f32(xr[r]) + dtb));
+              G += lb2 * frcp(1.0f + fexp2(fmaf(bf16_to_f32(xr[r]), ga, gb)));
               sm.gam[r][ch] = G;
-              if (r == C / 2 - 1) sm.g7[ch] = G;
+              if (r == C / 2 - 1) G7 = G;
             }
           } else {
 #pragma unroll
             for (int r = 0; r < C; ++r) {
               const bool live = r < Ln;
-              G += live ? lb * fsigmoid(ascale * (bf16_to_f32(xr[r]) + dtb)) : 0.f;
+              G += live ? lb2 * frcp(1.0f + fexp2(fmaf(bf16_to_f32(xr[r]), ga, gb))) : 0.f;
               sm.gam[r][ch] = G;
-              if (r == C / 2 - 1) sm.g7[ch] = G;
+              if (r == C / 2 - 1) G7 = G;
             }
           }
+          sm.g7[ch] = G7;
           sm.g15[ch] = G;
-          KN.eg15[ch] = fexp(G);
+          KN.eg15[ch] = fexp2(G);
+          sm.eg7[ch] = fexp2(G7);
+          sm.e157[ch] = fexp2(G - G7);
         }
         if (t < C) KN.beta[t] = (t < Ln) ? fsigmoid(bf16_to_f32(sm.braw[t])) : 0.f;
+      }
+      if (i >= 0 && uwave == kElimWave) {
+        KBuf& K = sm.kb[i & 1];  // chunk i, whose state pass runs now
+        // T = (I + A)^-1 Diag(beta) by elimination with rows spread over lanes (DPP
+        // broadcasts inside each 16-lane row); A[r][j] = 0 for j >= r, so the update
+        // is unconditional.  Lane (lm, lq) ends up with T[lm][lq + 4 s].
+        float arow[C], tt[4];
+#pragma unroll
+        for (int j = 0; j < C; j += 4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(&sm.A[lm][j]);
+          arow[j] = v4.x;
+          arow[j + 1] = v4.y;
+          arow[j + 2] = v4.z;
+          arow[j + 3] = v4.w;
+        }
+        const float bl = K.beta[lm];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) tt[s] = (lq + 4 * s == lm) ? bl : 0.f;
+        eliminate_strided<0>(tt, arow);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) split_store(&K.tm[0][lm][lq + 4 * s], &K.tm[1][lm][lq + 4 * s], tt[s]);
       }
       lds_barrier();
 
@@ -269,77 +318,83 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 
       // ---------------------------------------------------------- interval 3
       if (has_next) {
-        // scaled operands of chunk i + 1, written once in MFMA-ready form
-        if (t < 256) {
-          const int r = t >> 4, c8 = 8 * (t & 15);
-          float q8[8], k8[8], d8[8];
+        // Every operand of chunk i + 1 for row r, channels c4 .. c4 + 3 (rows run fastest
+        // across lanes, so the transposed Ka / Kl writes are 32 contiguous bytes per
+        // channel).  With d = Gcum - Gcum_mid: Qp = q-hat e^d, Kp = k-hat e^d,
+        // Km = k-hat e^-d; Qa = Qp e^Gcum_mid, Ka = Kp e^Gcum_mid, Kl = Km e^(Gcum_end -
+        // Gcum_mid).
+        const int r = t & (C - 1), c4 = 4 * (t >> 4);
+        const float4 qv = ld<float4>(&sm.aq[r][c4]);
+        const float4 kv = ld<float4>(&sm.ak[r][c4]);
+        const float4 gv = ld<float4>(&sm.gam[r][c4]);
+        const float4 g7 = ld<float4>(&sm.g7[c4]);
+        const float4 e7 = ld<float4>(&sm.eg7[c4]);
+        const float4 e157 = ld<float4>(&sm.e157[c4]);
+        const float rq = sm.rn[r], rk = sm.rn[C + r];
+        const float q4[4] = {qv.x * rq, qv.y * rq, qv.z * rq, qv.w * rq};
+        const float k4[4] = {kv.x * rk, kv.y * rk, kv.z * rk, kv.w * rk};
+        const float d4[4] = {gv.x - g7.x, gv.y - g7.y, gv.z - g7.z, gv.w - g7.w};
+        const float m7[4] = {e7.x, e7.y, e7.z, e7.w};
+        const float m157[4] = {e157.x, e157.y, e157.z, e157.w};
+        float qp[4], kp[4], km[4], qa[4], ka[4], kl[4];
 #pragma unroll
-          for (int v = 0; v < 8; v += 4) {
-            const float4 qv = *reinterpret_cast<const float4*>(&sm.aq[r][c8 + v]);
-            const float4 kv = *reinterpret_cast<const float4*>(&sm.ak[r][c8 + v]);
-            const float4 gv = *reinterpret_cast<const float4*>(&sm.gam[r][c8 + v]);
-            const float4 g7 = *reinterpret_cast<const float4*>(&sm.g7[c8 + v]);
-            q8[v] = qv.x; q8[v + 1] = qv.y; q8[v + 2] = qv.z; q8[v + 3] = qv.w;
-            k8[v] = kv.x; k8[v + 1] = kv.y; k8[v + 2] = kv.z; k8[v + 3] = kv.w;
-            d8[v] = gv.x - g7.x; d8[v + 1] = gv.y - g7.y; d8[v + 2] = gv.z - g7.z; d8[v + 3] = gv.w - g7.w;
-          }
-          const float rq = sm.rn[r], rk = sm.rn[C + r];
-          float qp[8], kp[8], km[8];
+        for (int v = 0; v < 4; ++v) {
+          const float el = fexp2(d4[v]), er = fexp2(-d4[v]);
+          qp[v] = q4[v] * el;
+          kp[v] = k4[v] * el;
+          km[v] = k4[v] * er;
+          qa[v] = qp[v] * m7[v];
+          ka[v] = kp[v] * m7[v];
+          kl[v] = km[v] * m157[v];
+        }
+        store4(&sm.qp[0][r][c4], &sm.qp[1][r][c4], qp);
+        store4(&sm.kp[0][r][c4], &sm.kp[1][r][c4], kp);
+        store4(&sm.km[0][r][c4], &sm.km[1][r][c4], km);
+        // Qa in the key order of the .S products: channels 32 kb + 4 m .. + 3 sit at
+        // 32 kb + 8 (m % 4) + 4 (m / 4)
+        const int pa = 32 * (c4 >> 5) + 8 * ((c4 >> 2) & 3) + 4 * ((c4 >> 4) & 1);
+        store4(&KN.qa[0][r][pa], &KN.qa[1][r][pa], qa);
 #pragma unroll
-          for (int v = 0; v < 8; ++v) {
-            const float el = fexp(d8[v]), er = fexp(-d8[v]);
-            qp[v] = q8[v] * rq * el;
-            kp[v] = k8[v] * rk * el;
-            km[v] = k8[v] * rk * er;
-          }
-          store8<false>(sm.qp, r, c8, qp);
-          store8<false>(sm.kp, r, c8, kp);
-          store8<false>(sm.km, r, c8, km);
-        } else {
-          const int u = t - 256;
-          {
-            // Qa: row r, lane group (kb, g): keys 32kb + 4g + 0..3 and 32kb + 16 + 4g + 0..3
-            const int r = u >> 4, kb = (u >> 2) & 3, g = u & 3;
-            const int k0 = 32 * kb + 4 * g;
-            const float rq = sm.rn[r];
-            float qa[8];
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-              const float4 qv = *reinterpret_cast<const float4*>(&sm.aq[r][k0 + 16 * half]);
-              const float4 gv = *reinterpret_cast<const float4*>(&sm.gam[r][k0 + 16 * half]);
-              qa[4 * half + 0] = qv.x * rq * fexp(gv.x);
-              qa[4 * half + 1] = qv.y * rq * fexp(gv.y);
-              qa[4 * half + 2] = qv.z * rq * fexp(gv.z);
-              qa[4 * half + 3] = qv.w * rq * fexp(gv.w);
-            }
-            store8<false>(KN.qa, r, 32 * kb + 8 * g, qa);
-          }
-          {
-            // Ka^T and Kl^T: channel cc, rows 8 hf .. 8 hf + 7
-            const int cc = u >> 1, hf = u & 1;
-            const float gend = sm.g15[cc];
-            float ka[8], kl[8];
-#pragma unroll
-            for (int v = 0; v < 8; ++v) {
-              const int r = 8 * hf + v;
-              const float kh = sm.ak[r][cc] * sm.rn[C + r];
-              const float G = sm.gam[r][cc];
-              ka[v] = kh * fexp(G);
-              kl[v] = kh * fexp(gend - G);
-            }
-            store8_hi<false>(&KN.kat[cc][8 * hf], ka);
-            store8<false>(KN.klt, cc, 8 * hf, kl);
-          }
+        for (int v = 0; v < 4; ++v) {
+          KN.kat[c4 + v][r] = static_cast<__bf16>(ka[v]);
+          split_store(&KN.klt[0][c4 + v][r], &KN.klt[1][c4 + v][r], kl[v]);
         }
       }
       lds_barrier();
 
       // ---------------------------------------------------------- interval 4
+      if (has_next && (uwave == kGramAWave || uwave == kGramPWave)) {
+        const bool gram_a = uwave == kGramAWave;
+        // Gram tiles of chunk i + 1: A = Kp Km^T (strict lower, times beta_r), eliminated
+        // by wave kElimWave in the next interval 1; P = Qp Km^T (lower incl.)
+        const __bf16(*Xh)[OPP] = gram_a ? sm.kp[0] : sm.qp[0];
+        const __bf16(*Xl)[OPP] = gram_a ? sm.kp[1] : sm.qp[1];
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < kHeadDim / 32; ++kb) {
+          const int o = 32 * kb + 8 * lq;
+          const bf16x8_t xh = ld<bf16x8_t>(&Xh[lm][o]), xl = ld<bf16x8_t>(&Xl[lm][o]);
+          const bf16x8_t mh = ld<bf16x8_t>(&sm.km[0][lm][o]), ml = ld<bf16x8_t>(&sm.km[1][lm][o]);
+          acc = mma32(xh, mh, acc);
+          a1 = mma32(xh, ml, a1);
+          a1 = mma32(xl, mh, a1);
+        }
+        acc += a1;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int r = 4 * lq + s, j = lm;
+          if (gram_a) {
+            sm.A[r][j] = (j < r) ? KN.beta[r] * acc[s] : 0.f;
+          } else {
+            split_store(&KN.p[0][r][j], &KN.p[1][r][j], (j <= r) ? acc[s] : 0.f);
+          }
+        }
+      }
       if (i + 2 < nch) {
         wait_vm();  // this wave's pieces of chunk i + 2 are in LDS
         if (t < C) sm.braw[t] = braw;
         // chunk i's output gate has been read by now; its buffer takes chunk i + 2's
-        prefetch_gate((i + 2) * C, sm.kb[(i + 2) & 1]);
+        prefetch_gate((i + 2) * C, (i + 2) & 1);
       }
       lds_barrier();
     }
@@ -352,9 +407,6 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     }
   } else {
     // ============================================================== consumer waves
-    // The consumers carry the serial chain through the state; the SIMD arbiter favours
-    // older waves (the producers), so raise the consumers' issue priority.
-    __builtin_amdgcn_s_setprio(2);
     f32x4_t S[8];
     const int64_t sbase = (static_cast<int64_t>(n) * H + h) * kHeadDim * kHeadDim;
     if (a.state_in) {
@@ -370,39 +422,31 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     const float nw = a.L.norm_w[col];
     lds_barrier();
 
-    // iteration i: consumers run chunk i, then the Gram tiles of chunk i + 1
+    bf16x4_t uh = {}, ul = {};
+    // S = Diag(exp(Gcum_C)) S + Kl^T U, once chunk i's U is known
+    auto update_state = [&](const KBuf& K) __attribute__((always_inline)) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const float4 e4 = ld<float4>(&K.eg15[16 * it + 4 * lq]);
+        S[it][0] *= e4.x;
+        S[it][1] *= e4.y;
+        S[it][2] *= e4.z;
+        S[it][3] *= e4.w;
+        S[it] = mma16s(ld<bf16x4_t>(&K.klt[0][16 * it + lm][4 * lq]),
+                       ld<bf16x4_t>(&K.klt[1][16 * it + lm][4 * lq]), uh, ul, S[it]);
+      }
+    };
+
+    // iteration i: consumers run chunk i
     for (int i = -1; i < nch; ++i) {
       const bool has_next = i + 1 < nch;
       KBuf& K = sm.kb[i & 1];
       KBuf& KN = sm.kb[(i + 1) & 1];
       f32x4_t O = {0.f, 0.f, 0.f, 0.f};
       bf16x8_t sh[4], sl[4];
-      bf16x4_t uh = {}, ul = {};
 
       // ---------------------------------------------------------- interval 1
       if (i >= 0) {
-        if (cw == 0) {
-          // T = (I + A)^-1 Diag(beta) by elimination with rows spread over lanes (DPP
-          // broadcasts inside each 16-lane row); A[r][j] = 0 for j >= r, so the update
-          // is unconditional.  Lane (lm, lq) ends up with T[lm][4 lq + s].
-          float arow[C], tt[4];
-#pragma unroll
-          for (int j = 0; j < C; j += 4) {
-            const float4 v4 = *reinterpret_cast<const float4*>(&sm.A[lm][j]);
-            arow[j] = v4.x;
-            arow[j + 1] = v4.y;
-            arow[j + 2] = v4.z;
-            arow[j + 3] = v4.w;
-          }
-          const float bl = K.beta[lm];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) tt[s] = (4 * lq + s == lm) ? bl : 0.f;
-          eliminate<0>(tt, arow);
-          bf16x4_t th, tl;
-          split_vec<4>(tt, th, tl);
-          *reinterpret_cast<bf16x4_t*>(&K.tm[0][lm][4 * lq]) = th;
-          *reinterpret_cast<bf16x4_t*>(&K.tm[1][lm][4 * lq]) = tl;
-        }
         // S as bf16 hi/lo B operands (per 32 keys: 4 lq + s, then 16 + 4 lq + s)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -479,71 +523,44 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       if (i >= 0) {
         // gated RMSNorm of the chunk's output rows and the store
         const int L = min(C, T - i * C);
-        float tot[4] = {0.f, 0.f, 0.f, 0.f};
-        uint16_t gr[4];
+        float tot[4];
+        {
+          const float4 s4 = ld<float4>(&sm.ss[0][4 * lq]);
+          tot[0] = s4.x;
+          tot[1] = s4.y;
+          tot[2] = s4.z;
+          tot[3] = s4.w;
+        }
 #pragma unroll
-        for (int wv = 0; wv < CWN; ++wv) {
-          const float4 s4 = *reinterpret_cast<const float4*>(&sm.ss[wv][4 * lq]);
+        for (int wv = 1; wv < CWN; ++wv) {
+          const float4 s4 = ld<float4>(&sm.ss[wv][4 * lq]);
           tot[0] += s4.x;
           tot[1] += s4.y;
           tot[2] += s4.z;
           tot[3] += s4.w;
         }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) gr[s] = K.graw[4 * lq + s][col];
-        bf16_t* po = static_cast<bf16_t*>(a.out) + (t0 + i * C + 4 * lq) * Hd +
-                     static_cast<int64_t>(h) * kHeadDim + col;
+        float y[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          if (4 * lq + s < L) {
-            const float rr = __builtin_amdgcn_rsqf(tot[s] * (1.0f / kHeadDim) + a.L.rms_eps);
-            const float g = fsigmoid(bf16_to_f32(gr[s]));
-            po->bits = f32_to_bf16(nw * O[s] * rr * g);
-          }
-          po += Hd;
+          const float rr = __builtin_amdgcn_rsqf(tot[s] * (1.0f / kHeadDim) + a.L.rms_eps);
+          const float g = fsigmoid(bf16_to_f32(graw_lds[i & 1][4 * lq + s][col]));
+          y[s] = nw * O[s] * rr * g;
         }
-        // S = Diag(exp(Gcum_C)) S + Kl^T U
+        bf16_t* po = static_cast<bf16_t*>(a.out) + (t0 + i * C + 4 * lq) * Hd +
+                     static_cast<int64_t>(h) * kHeadDim + col;
+        if (L == C) {
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-          const float4 e4 = *reinterpret_cast<const float4*>(&K.eg15[16 * it + 4 * lq]);
-          S[it][0] *= e4.x;
-          S[it][1] *= e4.y;
-          S[it][2] *= e4.z;
-          S[it][3] *= e4.w;
-          S[it] = mma16s(ld<bf16x4_t>(&K.klt[0][16 * it + lm][4 * lq]),
-                         ld<bf16x4_t>(&K.klt[1][16 * it + lm][4 * lq]), uh, ul, S[it]);
+          for (int s = 0; s < 4; ++s) po[s * Hd].bits = f32_to_bf16(y[s]);
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            if (4 * lq + s < L) po[s * Hd].bits = f32_to_bf16(y[s]);
         }
       }
       lds_barrier();
 
       // ---------------------------------------------------------- interval 4
-      if (has_next && cw < 2) {
-        // Gram tiles of chunk i + 1: consumer wave 0 -> A = Kp Km^T (strict lower, times
-        // beta_r), eliminated in the next interval 1; consumer wave 1 -> P = Qp Km^T
-        // (lower incl.)
-        const __bf16(*Xh)[OPP] = cw == 0 ? sm.kp[0] : sm.qp[0];
-        const __bf16(*Xl)[OPP] = cw == 0 ? sm.kp[1] : sm.qp[1];
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < kHeadDim / 32; ++kb) {
-          const int o = 32 * kb + 8 * lq;
-          const bf16x8_t xh = ld<bf16x8_t>(&Xh[lm][o]), xl = ld<bf16x8_t>(&Xl[lm][o]);
-          const bf16x8_t mh = ld<bf16x8_t>(&sm.km[0][lm][o]), ml = ld<bf16x8_t>(&sm.km[1][lm][o]);
-          acc = mma32(xh, mh, acc);
-          a1 = mma32(xh, ml, a1);
-          a1 = mma32(xl, mh, a1);
-        }
-        acc += a1;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int r = 4 * lq + s, j = lm;
-          if (cw == 0) {
-            sm.A[r][j] = (j < r) ? KN.beta[r] * acc[s] : 0.f;
-          } else {
-            split_store(&KN.p[0][r][j], &KN.p[1][r][j], (j <= r) ? acc[s] : 0.f);
-          }
-        }
-      }
+      if (i >= 0) update_state(K);
       lds_barrier();
     }
 
