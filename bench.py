@@ -13,10 +13,17 @@ launch over the whole batch.  Printed as one JSON line with:
                 measurement matches the current kernel source, else null;
 * cpu_baseline -- the fp64 oracle timed on the host cores on a bounded sample of the
                 same workload;
-* prefill    -- the chunked prefill on the 1 x 4096 x 32-head and 2 x 8192 x 96-head
-                workloads: tokens/s, fraction of HBM and of dense bf16 MFMA peak.
+* prefill    -- the chunked prefill on the 1 x 4096 x 32-head, 2 x 8192 x 96-head and
+                16-sequence varlen x 64-head workloads (3 warm-up runs, median of 20, each
+                after a 768 MB write that flushes the 256 MB MALL): tokens/s, the fraction
+                of HBM and of dense bf16 MFMA peak at the algorithmic byte and flop counts,
+                and the roofline fraction max(bytes / HBM peak, flops / MFMA peak) / time;
+                counter readings (HBM traffic, issued MFMA work) are attached from
+                profiles/ when they were taken on the current kernel source.  The varlen
+                entry also times its 32 decode steps from the returned states.
 
-`--summarize-pmc DIR` turns rocprofv3 counter output into profiles/ summaries.
+`--only-prefill` runs just the prefill part (for profiling); `--summarize-pmc` turns
+rocprofv3 counter output into profiles/ summaries.
 """
 from __future__ import annotations
 
@@ -46,7 +53,8 @@ PREFILL_BYTES_PER_TOKEN_HEAD = 5 * D * 2 + 2 + D * 2
 PREFILL_FLOPS_PER_TOKEN_HEAD = 6 * D * D + 5 * 64 * D + 64 * 64 // 3
 METRIC = "KDA tokens/s per layer (chunked prefill, decode); % of MFMA / HBM roofline"
 DECODE_KERNEL = "decode_kernel"
-PREFILL_KERNEL = "prefill_kernel"
+PREFILL_KERNEL = "prefill_pc_kernel"  # the bf16 prefill kernel
+PREFILL_WORKLOADS = ("prefill_t4096_h32", "prefill_2x8192_h96", "varlen16_h64")
 
 
 def kernel_source_hash(name: str) -> str:
@@ -135,7 +143,7 @@ def decode_traffic(steps_hash: str):
 
 # --------------------------------------------------------------------------- prefill
 
-def bench_prefill(name: str, reps: int):
+def bench_prefill(name: str, reps: int, warmup: int = 3):
     import torch
 
     import gated_delta_rule_05_amd as kda
@@ -159,7 +167,8 @@ def bench_prefill(name: str, reps: int):
                     cu_dev, prob["cu_seqlens"], state_in=prob["state_in"], ring_in=prob["ring_in"],
                     out=out, state_out=st, ring_out=rg, stream=stream)
 
-    run()
+    for _ in range(warmup):
+        run()
     torch.cuda.synchronize()
     times = []
     for _ in range(reps):
@@ -178,11 +187,60 @@ def bench_prefill(name: str, reps: int):
               + N * 3 * H * D * 3 * 4 * (2 if w.init_ring else 1))
     flops = PREFILL_FLOPS_PER_TOKEN_HEAD * T * H
     s = ms / 1e3
-    return dict(workload=name, tokens=T, heads=H, ms=ms, tokens_per_s=T / s,
-                hbm_gbs=nbytes / s / 1e9, hbm_frac=nbytes / s / 1e9 / HBM_PEAK_GBS,
-                mfma_tflops=flops / s / 1e12, mfma_frac=flops / s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                algorithmic_bytes=nbytes, algorithmic_flops=flops,
-                finite=bool(torch.isfinite(out.float()).all()))
+    res = dict(workload=name, sequences=N, tokens=T, heads=H, ms=ms, ms_min=times[0], reps=reps,
+               tokens_per_s=T / s, hbm_gbs=nbytes / s / 1e9, hbm_frac=nbytes / s / 1e9 / HBM_PEAK_GBS,
+               mfma_tflops=flops / s / 1e12, mfma_frac=flops / s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+               roofline_frac=max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) / s,
+               algorithmic_bytes=nbytes, algorithmic_flops=flops,
+               finite=bool(torch.isfinite(out.float()).all()))
+    counters = prefill_counters(name)
+    if counters:
+        res["counters"] = counters
+    if w.decode_after:
+        res["decode_continuation"] = bench_decode_after(w, layer, st, rg, stream)
+    del prob, out, flush
+    return res
+
+
+def bench_decode_after(w, layer, st, rg, stream):
+    """The workload's decode continuation: w.decode_after steps over all its sequences from
+    the returned states and rings (fresh activations per step, resident before timing)."""
+    import torch
+
+    import gated_delta_rule_05_amd as kda
+    import synthetic
+
+    N, H, steps = len(w.seqlens), w.heads, w.decode_after
+    g = synthetic.gen(w.seed + 1, "cuda:0")
+    acts = synthetic.activations(N, H, w.io, g, "cuda:0", lead=(steps,))
+    out = torch.empty((N, H * D), dtype=torch.bfloat16, device="cuda:0")
+    kda.decode_step(layer, acts["q"][0], acts["k"][0], acts["v"][0], acts["z"][0], acts["beta"][0],
+                    acts["gate"][0], st, rg, out=out, stream=stream)  # warm-up
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        kda.decode_step(layer, acts["q"][i], acts["k"][i], acts["v"][i], acts["z"][i],
+                        acts["beta"][i], acts["gate"][i], st, rg, out=out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = DECODE_BYTES_PER_TOKEN_HEAD * N * H
+    return dict(batch=N, heads=H, steps=steps, ms_per_step=ms, tokens_per_s=N / (ms / 1e3),
+                hbm_gbs=nbytes / (ms / 1e3) / 1e9, hbm_frac=nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS)
+
+
+def prefill_counters(name: str):
+    """Stored counter readings for a prefill workload, if taken on the current source."""
+    p = os.path.join(ROOT, "profiles", "prefill_pmc.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        doc = json.load(f)
+    if doc.get("source_hash") != kernel_source_hash("prefill"):
+        return None
+    return doc.get("workloads", {}).get(name)
 
 
 # --------------------------------------------------------------------------- CPU baseline
@@ -230,36 +288,40 @@ def cpu_baseline(dec, target_s: float = 10.0):
 
 # --------------------------------------------------------------------------- PMC summaries
 
-def summarize_pmc(fetch_dir: str, write_dir: str, out_name: str = "decode_b256_h32_pmc"):
-    """Reads two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) of
-    `bench.py --calibrate-copy`, scales each by the same counter's reading on the 1 GiB
-    copy kernel, and writes profiles/<out_name>.{md,json}."""
+def _read_pmc(d: str, counter: str):
+    """(kernel name, grid size, value) for every dispatch row of one counter."""
     import csv
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], int(r.get("Grid_Size", 0) or 0),
+                                 float(r["Counter_Value"])))
+    return rows
 
-    def read(d, counter):
-        rows = []
-        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            with open(f) as fh:
-                for r in csv.DictReader(fh):
-                    if r.get("Counter_Name") == counter:
-                        rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
-        return rows
 
-    fetch = read(fetch_dir, "FETCH_SIZE")
-    write = read(write_dir, "WRITE_SIZE")
+def _copy_scale(rows):
+    """Bytes per counted KiB, from the 1 GiB device copy (the largest copy dispatch)."""
+    c = max((x for k, _, x in rows if "copyBuffer" in k), default=None)
+    return (float(1 << 30) / (c * 1024), c) if c else (None, None)
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str):
+    """Reads two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) of
+    `bench.py --no-prefill --no-cpu-baseline --calibrate-copy`, scales each by the same
+    counter's reading on the 1 GiB copy kernel, and writes profiles/decode_b256_h32_pmc.json."""
+    fetch = _read_pmc(fetch_dir, "FETCH_SIZE")
+    write = _read_pmc(write_dir, "WRITE_SIZE")
 
     def mean_for(rows, pat):
-        v = [x for k, x in rows if pat in k]
+        v = [x for k, _, x in rows if pat in k]
         return (sum(v) / len(v), len(v)) if v else (None, 0)
 
-    copy_bytes = float(1 << 30)
     f_dec, nf = mean_for(fetch, DECODE_KERNEL)
     w_dec, nw = mean_for(write, DECODE_KERNEL)
-    # the 1 GiB device copy: the largest copy dispatch in each run
-    f_copy = max((x for k, x in fetch if "copyBuffer" in k), default=None)
-    w_copy = max((x for k, x in write if "copyBuffer" in k), default=None)
-    f_scale = copy_bytes / (f_copy * 1024) if f_copy else None
-    w_scale = copy_bytes / (w_copy * 1024) if w_copy else None
+    f_scale, f_copy = _copy_scale(fetch)
+    w_scale, w_copy = _copy_scale(write)
     fetched = f_dec * 1024 * f_scale if (f_dec and f_scale) else None
     written = w_dec * 1024 * w_scale if (w_dec and w_scale) else None
     alg = DECODE_BYTES_PER_TOKEN_HEAD * 256 * 32
@@ -270,7 +332,51 @@ def summarize_pmc(fetch_dir: str, write_dir: str, out_name: str = "decode_b256_h
                write_scale=w_scale, fetched_bytes=fetched, written_bytes=written,
                bytes_per_launch=total, algorithmic_bytes_per_launch=alg,
                traffic_over_algorithmic=(total / alg) if total else None)
-    with open(os.path.join(ROOT, "profiles", out_name + ".json"), "w") as fh:
+    with open(os.path.join(ROOT, "profiles", "decode_b256_h32_pmc.json"), "w") as fh:
+        json.dump(doc, fh, indent=1)
+    print(json.dumps(doc, indent=1))
+
+
+def summarize_prefill_pmc(fetch_dir: str, write_dir: str, mfma_dir: str):
+    """Reads three rocprofv3 --pmc runs of `bench.py --only-prefill --prefill-reps 1
+    --calibrate-copy` (FETCH_SIZE; WRITE_SIZE; SQ_INSTS_VALU_MFMA_MOPS_BF16 with
+    SQ_INSTS_VALU and SQ_INSTS_MFMA), identifies each workload's dispatches by grid size,
+    and writes profiles/prefill_pmc.json: measured HBM bytes (copy-calibrated) against the
+    algorithmic bytes, and the bf16 MFMA work the kernel issued (512 flops per MOPS unit)
+    against the algorithmic flops."""
+    import synthetic
+
+    fetch = _read_pmc(fetch_dir, "FETCH_SIZE")
+    write = _read_pmc(write_dir, "WRITE_SIZE")
+    mops = _read_pmc(mfma_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    valu = _read_pmc(mfma_dir, "SQ_INSTS_VALU")
+    mfma = _read_pmc(mfma_dir, "SQ_INSTS_MFMA")
+    f_scale, f_copy = _copy_scale(fetch)
+    w_scale, w_copy = _copy_scale(write)
+    out = {}
+    for name in PREFILL_WORKLOADS:
+        w = synthetic.WORKLOADS[name]
+        N, H, T = len(w.seqlens), w.heads, sum(w.seqlens)
+        grid = N * H * 1024
+
+        def mean(rows):
+            v = [x for k, g, x in rows if PREFILL_KERNEL in k and g == grid]
+            return sum(v) / len(v) if v else None
+
+        f, wr, m, va, mf = mean(fetch), mean(write), mean(mops), mean(valu), mean(mfma)
+        alg = (PREFILL_BYTES_PER_TOKEN_HEAD * T * H + N * H * D * D * 4 * (2 if w.init_state else 1)
+               + N * 3 * H * D * 3 * 4 * (2 if w.init_ring else 1))
+        traffic = (f * 1024 * f_scale + wr * 1024 * w_scale) if (f and wr and f_scale and w_scale) else None
+        out[name] = dict(hbm_bytes=traffic, algorithmic_bytes=alg,
+                         traffic_over_algorithmic=(traffic / alg) if traffic else None,
+                         mfma_flops_issued=(m * 512) if m else None,
+                         algorithmic_flops=PREFILL_FLOPS_PER_TOKEN_HEAD * T * H,
+                         valu_insts_per_token_head=(va / (T * H)) if va else None,
+                         mfma_insts_per_token_head=(mf / (T * H)) if mf else None)
+    doc = dict(kernel=PREFILL_KERNEL, source_hash=kernel_source_hash("prefill"),
+               copy_fetch_kib=f_copy, copy_write_kib=w_copy, fetch_scale=f_scale,
+               write_scale=w_scale, workloads=out)
+    with open(os.path.join(ROOT, "profiles", "prefill_pmc.json"), "w") as fh:
         json.dump(doc, fh, indent=1)
     print(json.dumps(doc, indent=1))
 
@@ -284,14 +390,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--prefill-reps", type=int, default=10)
+    ap.add_argument("--prefill-reps", type=int, default=20)
+    ap.add_argument("--prefill-warmup", type=int, default=3)
+    ap.add_argument("--prefill-workloads", default=",".join(PREFILL_WORKLOADS))
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="run only the prefill workloads and print their list")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-prefill-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "MFMA_DIR"))
     args = ap.parse_args()
 
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return 0
+    if args.summarize_prefill_pmc:
+        summarize_prefill_pmc(*args.summarize_prefill_pmc)
         return 0
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -305,6 +419,22 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
+
+    workloads = [x for x in args.prefill_workloads.split(",") if x]
+
+    def prefill_list():
+        pf = []
+        for name in workloads:
+            pf.append(bench_prefill(name, args.prefill_reps, args.prefill_warmup))
+            torch.cuda.empty_cache()
+        return pf
+
+    if args.only_prefill:
+        pf = prefill_list()
+        if args.calibrate_copy:
+            copy_calibration()
+        print(json.dumps({"prefill": pf}), flush=True)
+        return 0
 
     dres, dec = bench_decode(args.steps, args.warmup, args.calibrate_copy)
     B, H = dres["B"], dres["H"]
@@ -332,11 +462,7 @@ def main():
                      "kernel": DECODE_KERNEL, "algorithmic_bytes_per_launch": bytes_launch},
     }
     if not args.no_prefill:
-        pf = []
-        for name in ("prefill_t4096_h32", "prefill_2x8192_h96"):
-            pf.append(bench_prefill(name, args.prefill_reps))
-            torch.cuda.empty_cache()
-        line["prefill"] = pf
+        line["prefill"] = prefill_list()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(dec)
     print(json.dumps(line), flush=True)
