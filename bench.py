@@ -13,6 +13,9 @@ launch over the whole batch.  Printed as one JSON line with:
                 measurement matches the current kernel source, else null;
 * cpu_baseline -- the fp64 oracle timed on the host cores on a bounded sample of the
                 same workload;
+* verify     -- the batched verify of speculative decoding on the same shape: 4 rows per
+                sequence in one kda_decode_multi launch (tokens/s over all rows, HBM
+                fraction at its algorithmic bytes);
 * prefill    -- the chunked prefill on the 1 x 4096 x 32-head, 2 x 8192 x 96-head and
                 16-sequence varlen x 64-head workloads (3 warm-up runs, median of 20, each
                 after a 768 MB write that flushes the 256 MB MALL): tokens/s, the fraction
@@ -116,6 +119,50 @@ def bench_decode(steps: int, warmup: int, calibrate_copy: bool):
     res = dict(B=B, H=H, ms_total=ms, ms_per_step=ms / steps,
                finite=bool(torch.isfinite(out.float()).all()))
     return res, dec
+
+
+def bench_verify(dec, t: int = 4, reps: int = 32):
+    """The batched verify of speculative decoding on the decode workload's shape: t rows
+    per sequence in one kda_decode_multi launch (state and conv history stay in registers
+    across the rows), ping-pong state buffers, median of `reps` launches.  Tokens/s counts
+    all B * t rows; the algorithmic bytes are the state and ring once plus t rows of
+    activations per (sequence, head)."""
+    import torch
+
+    import gated_delta_rule_05_amd as kda
+
+    B, H = dec["q"].shape[1], dec["layer"]["num_heads"]
+    layer = kda.Layer(**dec["layer"])
+    rows = {n: dec[n][:t].transpose(0, 1).contiguous()
+            for n in ("q", "k", "v", "z", "beta", "gate")}
+    s0, r0 = dec["state"].clone(), dec["ring"].clone()
+    s1, r1 = torch.empty_like(s0), torch.empty_like(r0)
+    out = torch.empty((B, t, H * D), dtype=dec["q"].dtype, device=s0.device)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        kda.decode_multi(layer, rows["q"], rows["k"], rows["v"], rows["z"], rows["beta"],
+                         rows["gate"], s0, r0, s1, r1, out=out, stream=stream)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    ms = times[len(times) // 2]
+    act = 5 * D * 2 + 2 + D * 2
+    nbytes = B * H * (2 * D * D * 4 + 2 * 3 * D * 3 * 4 + t * act)
+    return dict(rows_per_sequence=t, batch=B, heads=H, ms=ms, tokens_per_s=B * t / (ms / 1e3),
+                hbm_gbs=nbytes / (ms / 1e3) / 1e9, hbm_frac=nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                algorithmic_bytes=nbytes)
 
 
 def copy_calibration(nbytes: int = 1 << 30):
@@ -461,6 +508,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": DECODE_KERNEL, "algorithmic_bytes_per_launch": bytes_launch},
     }
+    line["verify"] = bench_verify(dec)
     if not args.no_prefill:
         line["prefill"] = prefill_list()
     if not args.no_cpu_baseline:

@@ -18,11 +18,11 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 HEAD_DIM = 128
 CONV_KERNEL = 4
 
-EXPORTED = ("kda_prefill_workspace_bytes", "kda_prefill", "kda_decode_step",
+EXPORTED = ("kda_prefill_workspace_bytes", "kda_prefill", "kda_decode_step", "kda_decode_multi",
             "kda_status_string", "kda_last_error", "kda_abi_version")
 
 
@@ -68,6 +68,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.kda_prefill.argtypes = [lp, ctypes.c_int, i32, vp, vp, i64] + [vp] * 11 + [vp, sz, vp]
         lib.kda_decode_step.restype = ctypes.c_int
         lib.kda_decode_step.argtypes = [lp, ctypes.c_int, i32] + [vp] * 9 + [vp]
+        lib.kda_decode_multi.restype = ctypes.c_int
+        lib.kda_decode_multi.argtypes = [lp, ctypes.c_int, i32, i32, vp] + [vp] * 6 + [vp] * 5 + [vp]
         if lib.kda_abi_version() != ABI_VERSION:
             raise RuntimeError(f"libkda ABI {lib.kda_abi_version()} != binding ABI {ABI_VERSION}")
         _lib = lib
@@ -210,4 +212,47 @@ def decode_step(layer: Layer, q, k, v, z, beta, gate, state, ring, out=None, str
     _check(lib.kda_decode_step(ctypes.byref(layer.c), io, B, _ptr(q), _ptr(k), _ptr(v), _ptr(z),
                                _ptr(beta), _ptr(gate), _ptr(state), _ptr(ring), _ptr(out),
                                _stream_handle(stream)))
+    return out
+
+
+def decode_multi(layer: Layer, q, k, v, z, beta, gate, state_in, ring_in, state_out=None,
+                 ring_out=None, ntok=None, out=None, write_out=True, stream=None):
+    """Several consecutive decode tokens per sequence in one launch (batched verify of
+    speculative decoding; also its rollback by replay).
+
+    q, k, v, z, gate [B, t, H*128] io, beta [B, t, H] io.  state_in [B, H, 128, 128] fp32 and
+    ring_in [B, 3*H*128, 3] fp32 are the state and conv history before the first token;
+    state_out / ring_out receive them after each sequence's last token (default: in place,
+    i.e. the input buffers).  ntok: int32 [B] on the device with each sequence's token count
+    (clamped to [0, t]), or None for all t.  Returns out [B, t, H*128] io (rows past a
+    sequence's count are left as they were), or None when write_out is False.  Bit-identical
+    row by row to chaining decode_step."""
+    lib = load()
+    dev = layer.device
+    H = layer.H
+    Hd = H * HEAD_DIM
+    dt = q.dtype
+    io = io_code(dt)
+    B, t = q.shape[0], q.shape[1]
+    for name, x in (("q", q), ("k", k), ("v", v), ("z", z), ("gate", gate)):
+        _need(x, name, (B, t, Hd), dt, dev)
+    _need(beta, "beta", (B, t, H), dt, dev)
+    _need(state_in, "state_in", (B, H, HEAD_DIM, HEAD_DIM), torch.float32, dev)
+    _need(ring_in, "ring_in", (B, 3 * Hd, CONV_KERNEL - 1), torch.float32, dev)
+    state_out = state_in if state_out is None else state_out
+    ring_out = ring_in if ring_out is None else ring_out
+    _need(state_out, "state_out", (B, H, HEAD_DIM, HEAD_DIM), torch.float32, dev)
+    _need(ring_out, "ring_out", (B, 3 * Hd, CONV_KERNEL - 1), torch.float32, dev)
+    if ntok is not None:
+        _need(ntok, "ntok", (B,), torch.int32, dev)
+    if write_out:
+        if out is None:
+            out = torch.empty((B, t, Hd), dtype=dt, device=dev)
+        _need(out, "out", (B, t, Hd), dt, dev)
+    else:
+        out = None
+    _check(lib.kda_decode_multi(ctypes.byref(layer.c), io, B, t, _ptr(ntok), _ptr(q), _ptr(k),
+                                _ptr(v), _ptr(z), _ptr(beta), _ptr(gate), _ptr(state_in),
+                                _ptr(ring_in), _ptr(state_out), _ptr(ring_out), _ptr(out),
+                                _stream_handle(stream)))
     return out

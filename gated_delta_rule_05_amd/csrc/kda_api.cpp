@@ -90,22 +90,53 @@ kda_status kda_decode_step(const kda_layer* layer, kda_dtype io, int32_t batch, 
                            const void* k, const void* v, const void* z, const void* beta,
                            const void* gate, float* state, float* ring, void* out,
                            hipStream_t stream) {
+  if (!out && batch > 0) return fail(KDA_ERR_INVALID_ARG, "out is NULL");
+  return kda_decode_multi(layer, io, batch, 1, nullptr, q, k, v, z, beta, gate, state, ring,
+                          state, ring, out, stream);
+}
+
+kda_status kda_decode_multi(const kda_layer* layer, kda_dtype io, int32_t batch, int32_t tokens,
+                            const int32_t* ntok_dev, const void* q, const void* k, const void* v,
+                            const void* z, const void* beta, const void* gate,
+                            const float* state_in, const float* ring_in, float* state_out,
+                            float* ring_out, void* out, hipStream_t stream) {
   kda_status st = check_layer(layer, false);
   if (st != KDA_OK) return st;
   if (!io_ok(io)) return fail(KDA_ERR_INVALID_ARG, "unknown io dtype %d", static_cast<int>(io));
   if (batch < 0) return fail(KDA_ERR_INVALID_ARG, "batch must be >= 0");
+  if (tokens < 0) return fail(KDA_ERR_INVALID_ARG, "tokens must be >= 0");
   if (batch == 0) return ok();
-  if (!q || !k || !v || !z || !beta || !gate || !state || !ring || !out)
+  if (!state_in || !ring_in || !state_out || !ring_out)
+    return fail(KDA_ERR_INVALID_ARG, "a state or ring pointer is NULL");
+  if (tokens > 0 && (!q || !k || !v || !z || !beta || !gate))
     return fail(KDA_ERR_INVALID_ARG, "a tensor pointer is NULL");
-  if (!aligned16(state)) return fail(KDA_ERR_INVALID_ARG, "state must be 16-byte aligned");
-  if (static_cast<int64_t>(batch) * layer->num_heads > 0x7fffffffLL)
+  if (!aligned16(state_in) || !aligned16(state_out))
+    return fail(KDA_ERR_INVALID_ARG, "state buffers must be 16-byte aligned");
+  const int64_t units = static_cast<int64_t>(batch) * layer->num_heads;
+  if (units > 0x7fffffffLL)
     return fail(KDA_ERR_INVALID_ARG, "batch * num_heads exceeds the grid limit");
+  {
+    // exact aliasing is allowed (in place); partial overlap is not
+    const int64_t sbytes = units * kda::kHeadDimHost * kda::kHeadDimHost * 4;
+    const int64_t rbytes = static_cast<int64_t>(batch) * 3 * layer->num_heads * kda::kHeadDimHost * 3 * 4;
+    auto overlap = [](const void* a, const void* b, int64_t n) {
+      const char* x = static_cast<const char*>(a);
+      const char* y = static_cast<const char*>(b);
+      return x != y && x < y + n && y < x + n;
+    };
+    if (overlap(state_in, state_out, sbytes) || overlap(ring_in, ring_out, rbytes))
+      return fail(KDA_ERR_INVALID_ARG, "state or ring buffers overlap partially");
+  }
   kda::DecodeArgs a;
   a.L = layer_params(layer);
   a.batch = batch;
+  a.tokens = tokens;
+  a.ntok = ntok_dev;
   a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.gate = gate;
-  a.state = state;
-  a.ring = ring;
+  a.state_in = state_in;
+  a.ring_in = ring_in;
+  a.state_out = state_out;
+  a.ring_out = ring_out;
   a.out = out;
   hipError_t e = kda::launch_decode(a, io, stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));

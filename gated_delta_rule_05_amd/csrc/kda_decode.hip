@@ -1,5 +1,5 @@
-// Recurrent decode step of the KDA core: one token per sequence, fp32 state streamed
-// through HBM once.
+// Recurrent decode of the KDA core: one or more consecutive tokens per sequence, the fp32
+// state streamed through HBM once per launch.
 //
 // Math ("Kimi Delta Attention (KDA) -- analysis & C kernel plan", section "Recurrence",
 // and its "C kernel plan / Decode" outline): S' = Diag(exp(g)) S; u = S'^T k;
@@ -8,11 +8,20 @@
 //
 // One workgroup of 256 threads per (sequence, head).  Thread t owns value columns
 // 4*(t%32) .. +3 and key rows (t/32) + 8m, m = 0..15: 64 fp32 of state in registers,
-// loaded and stored as float4 so each wave moves two whole 512-byte rows per access.
-// The prologue (conv + ring roll, L2 norms, gate, beta) runs while those loads are in
+// loaded and stored 16 bytes at a time (buffer instructions: one offset register) so each
+// wave moves two whole 512-byte rows per access.
+// The first token's prologue (conv, L2 norms, gate, beta) runs while those loads are in
 // flight; the epilogue is the sigmoid-gated RMSNorm over the head's 128 outputs.  State
 // stores are non-temporal: on MI355X that lifts the read+write stream from about 5.0 to
 // about 6.6 TB/s for this kernel (measured), with identical results.
+//
+// Several tokens per launch (the batched verify of speculative decoding, docs.rs
+// "memra_engine::kda" kda_verify_rows_cached): the token loop runs over the
+// register-resident state and conv history, and its body is compiled once (no unrolling
+// or peeling), so each token's arithmetic is the very instruction sequence a one-token
+// launch executes.  A t-token launch is therefore bit-identical, row by row, to t chained
+// one-token launches, and a rollback is a replay of the same launch from the pre-round
+// state over the first `keep` tokens (kda_verify_rollback_rows, kda_scan_replay).
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -29,6 +38,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int cg = t & 31;
   const int rg = t >> 5;
   const int64_t Hd = static_cast<int64_t>(H) * kHeadDim;
+  const int n = a.ntok ? min(max(a.ntok[b], 0), a.tokens) : a.tokens;
 
   __shared__ float a_q[kHeadDim], a_k[kHeadDim], a_v[kHeadDim], eg[kHeadDim], sg[kHeadDim];
   __shared__ float dlt[kHeadDim];
@@ -36,13 +46,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ float red[4][2][kHeadDim];
   __shared__ float part2[2];
 
-  // 1. state loads first, so their latency overlaps the prologue
-  float4* Sg = reinterpret_cast<float4*>(a.state + static_cast<int64_t>(unit) * kHeadDim * kHeadDim);
-  float4 s[16];
-#pragma unroll
-  for (int m = 0; m < 16; ++m) s[m] = Sg[(rg + 8 * m) * (kHeadDim / 4) + cg];
-
-  // 2. prologue: conv + SiLU with the ring as history, ring roll, gate, beta
   const IO* x_q = static_cast<const IO*>(a.q);
   const IO* x_k = static_cast<const IO*>(a.k);
   const IO* x_v = static_cast<const IO*>(a.v);
@@ -51,120 +54,184 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const IO* x_b = static_cast<const IO*>(a.beta);
   const int i = t & (kHeadDim - 1);
   const int64_t c = static_cast<int64_t>(h) * kHeadDim + i;
-  const int64_t xrow = static_cast<int64_t>(b) * Hd;
-  float* ring = a.ring + static_cast<int64_t>(b) * 3 * Hd * kRingTaps;
-  const float beta = sigmoidf_(load_io(x_b, static_cast<int64_t>(b) * H + h));
 
-  if (t < kHeadDim) {
-    float sums[3];
-    float act[2];
+  // 1. the state loads first: the 64 KiB stream bounds the kernel, and issuing it ahead
+  // of everything else measured fastest.  Then the first token's activations and the conv
+  // history; each later token's activations are fetched one token ahead.  Threads < 128
+  // use planes q and k of channel i, the others plane v, the decay pre-activation and the
+  // output gate of channel i.  Raw io values are kept (converted only where used), and
+  // every thread loads the same way through its own plane pointers, so no load is waited
+  // for before it is needed.
+  const IO* pa = t < kHeadDim ? x_q : x_v;
+  const IO* pb = t < kHeadDim ? x_k : x_z;
+  IO xa{}, xb{}, xc{}, xbeta{};
+  auto fetch = [&](int tok) __attribute__((always_inline)) {
+    const int64_t row = static_cast<int64_t>(b) * a.tokens + tok;
+    xa = pa[row * Hd + c];
+    xb = pb[row * Hd + c];
+    xc = x_g[row * Hd + c];
+    xbeta = x_b[row * H + h];
+  };
+  // state rows rg + 8 m of this (sequence, head): byte offset 16 (32 rg + cg) + 4096 m
+  const int64_t soff = static_cast<int64_t>(unit) * kHeadDim * kHeadDim;
+  constexpr int kStateBytes = kHeadDim * kHeadDim * 4;
+  const __amdgpu_buffer_rsrc_t Sin = buffer_rsrc(a.state_in + soff, kStateBytes);
+  const __amdgpu_buffer_rsrc_t Sout = buffer_rsrc(a.state_out + soff, kStateBytes);
+  const int svoff = 16 * (32 * rg + cg);
+  float4 s[16];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {  // planes q, k
-      const float x = load_io(p == 0 ? x_q : x_k, xrow + c);
-      const float* w = a.L.conv_w + (p * Hd + c) * kConvTaps;
-      float* r = ring + (p * Hd + c) * kRingTaps;
-      const float h0 = r[0], h1 = r[1], h2 = r[2];
-      const float y = w[3] * x + w[0] * h0 + w[1] * h1 + w[2] * h2;
-      r[0] = h1;
-      r[1] = h2;
-      r[2] = x;
-      act[p] = siluf_(y);
+  for (int m = 0; m < 16; ++m) s[m] = buffer_load16(Sin, svoff, 4096 * m);
+
+  if (n > 0) fetch(0);
+
+  const int64_t roff = static_cast<int64_t>(b) * 3 * Hd * kRingTaps;
+  const int p0 = t < kHeadDim ? 0 : 2;  // first plane this thread holds
+  float hist[2][3];
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp) {
+    const int p = p0 + pp;
+    if (p < 3) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) hist[pp][j] = a.ring_in[roff + (p * Hd + c) * kRingTaps + j];
     }
-    a_q[i] = act[0];
-    a_k[i] = act[1];
-    sums[0] = wave_sum(act[0] * act[0]);
-    sums[1] = wave_sum(act[1] * act[1]);
-    sums[2] = wave_sum(act[0] * act[1]);
-    if ((t & 63) == 0) {
-      part[wave][0] = sums[0];
-      part[wave][1] = sums[1];
-      part[wave][2] = sums[2];
+  }
+  const float ascale = expf(a.L.A_log[h]);
+  const float dtb = a.L.dt_bias[c];
+  const float nw = a.L.norm_w[i];
+
+#pragma clang loop unroll(disable)
+  for (int tok = 0; tok < n; ++tok) {
+    const int64_t xrow = (static_cast<int64_t>(b) * a.tokens + tok) * Hd;
+    const float beta = sigmoidf_(io_to_f32(xbeta));
+
+    // 2. prologue: conv + SiLU with the history, history roll, gate, beta
+    if (t < kHeadDim) {
+      float sums[3];
+      float act[2];
+      const float xs[2] = {io_to_f32(xa), io_to_f32(xb)};
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {  // planes q, k
+        const float x = xs[p];
+        const float* w = a.L.conv_w + (p * Hd + c) * kConvTaps;  // re-read per token (L2)
+        const float y = w[3] * x + w[0] * hist[p][0] + w[1] * hist[p][1] + w[2] * hist[p][2];
+        hist[p][0] = hist[p][1];
+        hist[p][1] = hist[p][2];
+        hist[p][2] = x;
+        act[p] = siluf_(y);
+      }
+      a_q[i] = act[0];
+      a_k[i] = act[1];
+      sums[0] = wave_sum(act[0] * act[0]);
+      sums[1] = wave_sum(act[1] * act[1]);
+      sums[2] = wave_sum(act[0] * act[1]);
+      if ((t & 63) == 0) {
+        part[wave][0] = sums[0];
+        part[wave][1] = sums[1];
+        part[wave][2] = sums[2];
+      }
+    } else {
+      const float x = io_to_f32(xa);
+      const float* w = a.L.conv_w + (2 * Hd + c) * kConvTaps;
+      const float y = w[3] * x + w[0] * hist[0][0] + w[1] * hist[0][1] + w[2] * hist[0][2];
+      hist[0][0] = hist[0][1];
+      hist[0][1] = hist[0][2];
+      hist[0][2] = x;
+      a_v[i] = siluf_(y);
+      const float g = kda_gate(io_to_f32(xb), dtb, ascale, a.L.lower_bound);
+      eg[i] = expf(g);
+      sg[i] = sigmoidf_(io_to_f32(xc));
     }
-  } else {
-    const float x = load_io(x_v, xrow + c);
-    const float* w = a.L.conv_w + (2 * Hd + c) * kConvTaps;
-    float* r = ring + (2 * Hd + c) * kRingTaps;
-    const float h0 = r[0], h1 = r[1], h2 = r[2];
-    const float y = w[3] * x + w[0] * h0 + w[1] * h1 + w[2] * h2;
-    r[0] = h1;
-    r[1] = h2;
-    r[2] = x;
-    a_v[i] = siluf_(y);
-    const float g = kda_gate(load_io(x_z, xrow + c), a.L.dt_bias[c], expf(a.L.A_log[h]),
-                             a.L.lower_bound);
-    eg[i] = expf(g);
-    sg[i] = sigmoidf_(load_io(x_g, xrow + c));
-  }
-  __syncthreads();
+    if (tok + 1 < n) fetch(tok + 1);
+    __syncthreads();
 
-  // 3. decay the state and form both GEMVs, u = S'^T k-hat and w = S'^T q-hat
-  const float rq = 1.0f / sqrtf(part[0][0] + part[1][0] + a.L.l2_eps) * 0.08838834764831845f;
-  const float rk = 1.0f / sqrtf(part[0][1] + part[1][1] + a.L.l2_eps);
-  const float qk = (part[0][2] + part[1][2]) * rq * rk;  // k-hat . q-hat
-  float kh[16];
-  float u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f, w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
+    // 3. decay the state and form both GEMVs, u = S'^T k-hat and w = S'^T q-hat
+    const float rq = 1.0f / sqrtf(part[0][0] + part[1][0] + a.L.l2_eps) * 0.08838834764831845f;
+    const float rk = 1.0f / sqrtf(part[0][1] + part[1][1] + a.L.l2_eps);
+    const float qk = (part[0][2] + part[1][2]) * rq * rk;  // k-hat . q-hat
+    float kh[16];
+    float u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f, w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const int r = rg + 8 * m;
-    kh[m] = a_k[r] * rk;
-    const float qh = a_q[r] * rq;
-    const float e = eg[r];
-    s[m].x *= e;
-    s[m].y *= e;
-    s[m].z *= e;
-    s[m].w *= e;
-    u0 += s[m].x * kh[m];
-    u1 += s[m].y * kh[m];
-    u2 += s[m].z * kh[m];
-    u3 += s[m].w * kh[m];
-    w0 += s[m].x * qh;
-    w1 += s[m].y * qh;
-    w2 += s[m].z * qh;
-    w3 += s[m].w * qh;
-  }
-  u0 += __shfl_xor(u0, 32, 64);
-  u1 += __shfl_xor(u1, 32, 64);
-  u2 += __shfl_xor(u2, 32, 64);
-  u3 += __shfl_xor(u3, 32, 64);
-  w0 += __shfl_xor(w0, 32, 64);
-  w1 += __shfl_xor(w1, 32, 64);
-  w2 += __shfl_xor(w2, 32, 64);
-  w3 += __shfl_xor(w3, 32, 64);
-  if ((t & 32) == 0) {
-    *reinterpret_cast<float4*>(&red[wave][0][cg * 4]) = make_float4(u0, u1, u2, u3);
-    *reinterpret_cast<float4*>(&red[wave][1][cg * 4]) = make_float4(w0, w1, w2, w3);
-  }
-  __syncthreads();
+    for (int m = 0; m < 16; ++m) {
+      const int r = rg + 8 * m;
+      kh[m] = a_k[r] * rk;
+      const float qh = a_q[r] * rq;
+      const float e = eg[r];
+      s[m].x *= e;
+      s[m].y *= e;
+      s[m].z *= e;
+      s[m].w *= e;
+      u0 += s[m].x * kh[m];
+      u1 += s[m].y * kh[m];
+      u2 += s[m].z * kh[m];
+      u3 += s[m].w * kh[m];
+      w0 += s[m].x * qh;
+      w1 += s[m].y * qh;
+      w2 += s[m].z * qh;
+      w3 += s[m].w * qh;
+    }
+    u0 += __shfl_xor(u0, 32, 64);
+    u1 += __shfl_xor(u1, 32, 64);
+    u2 += __shfl_xor(u2, 32, 64);
+    u3 += __shfl_xor(u3, 32, 64);
+    w0 += __shfl_xor(w0, 32, 64);
+    w1 += __shfl_xor(w1, 32, 64);
+    w2 += __shfl_xor(w2, 32, 64);
+    w3 += __shfl_xor(w3, 32, 64);
+    if ((t & 32) == 0) {
+      *reinterpret_cast<float4*>(&red[wave][0][cg * 4]) = make_float4(u0, u1, u2, u3);
+      *reinterpret_cast<float4*>(&red[wave][1][cg * 4]) = make_float4(w0, w1, w2, w3);
+    }
+    __syncthreads();
 
-  // 4. delta and the readout for column j = t
-  float o = 0.f;
-  if (t < kHeadDim) {
-    const int j = t;
-    const float uj = red[0][0][j] + red[1][0][j] + red[2][0][j] + red[3][0][j];
-    const float wj = red[0][1][j] + red[1][1][j] + red[2][1][j] + red[3][1][j];
-    const float d = beta * (a_v[j] - uj);
-    dlt[j] = d;
-    o = wj + qk * d;
-    const float so = wave_sum(o * o);
-    if ((t & 63) == 0) part2[wave] = so;
-  }
-  __syncthreads();
+    // 4. delta and the readout for column j = t
+    float o = 0.f;
+    if (t < kHeadDim) {
+      const int j = t;
+      const float uj = red[0][0][j] + red[1][0][j] + red[2][0][j] + red[3][0][j];
+      const float wj = red[0][1][j] + red[1][1][j] + red[2][1][j] + red[3][1][j];
+      const float d = beta * (a_v[j] - uj);
+      dlt[j] = d;
+      o = wj + qk * d;
+      const float so = wave_sum(o * o);
+      if ((t & 63) == 0) part2[wave] = so;
+    }
+    __syncthreads();
 
-  // 5. rank-1 update and the single state write; gated RMSNorm on the output
-  const float4 d4 = *reinterpret_cast<const float4*>(&dlt[cg * 4]);
+    // 5. rank-1 update in registers, and after the last token the single state write;
+    // gated RMSNorm on the output
+    const float4 d4 = *reinterpret_cast<const float4*>(&dlt[cg * 4]);
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    s[m].x += kh[m] * d4.x;
-    s[m].y += kh[m] * d4.y;
-    s[m].z += kh[m] * d4.z;
-    s[m].w += kh[m] * d4.w;
-    store_streaming(&Sg[(rg + 8 * m) * (kHeadDim / 4) + cg], s[m]);
+    for (int m = 0; m < 16; ++m) {
+      s[m].x += kh[m] * d4.x;
+      s[m].y += kh[m] * d4.y;
+      s[m].z += kh[m] * d4.z;
+      s[m].w += kh[m] * d4.w;
+    }
+    if (tok + 1 == n) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) buffer_store16_nt(Sout, svoff, 4096 * m, s[m]);
+    }
+    if (t < kHeadDim && a.out) {
+      const int j = t;
+      const float r = 1.0f / sqrtf((part2[0] + part2[1]) * (1.0f / kHeadDim) + a.L.rms_eps);
+      store_io(static_cast<IO*>(a.out), xrow + static_cast<int64_t>(h) * kHeadDim + j,
+               nw * o * r * sg[j]);
+    }
+    if (tok + 1 < n) __syncthreads();  // the next token rewrites the LDS rows read above
   }
-  if (t < kHeadDim) {
-    const int j = t;
-    const float r = 1.0f / sqrtf((part2[0] + part2[1]) * (1.0f / kHeadDim) + a.L.rms_eps);
-    store_io(static_cast<IO*>(a.out), xrow + static_cast<int64_t>(h) * kHeadDim + j,
-             a.L.norm_w[j] * o * r * sg[j]);
+
+  // 6. no token: the state passes through; then the conv history
+  if (n == 0) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) buffer_store16_nt(Sout, svoff, 4096 * m, s[m]);
+  }
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp) {
+    const int p = p0 + pp;
+    if (p < 3) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) a.ring_out[roff + (p * Hd + c) * kRingTaps + j] = hist[pp][j];
+    }
   }
 }
 

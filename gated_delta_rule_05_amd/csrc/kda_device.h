@@ -25,6 +25,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// An io value already in a register, as fp32.
+__device__ __forceinline__ float io_to_f32(float x) { return x; }
+__device__ __forceinline__ float io_to_f32(bf16_t x) { return bf16_to_f32(x.bits); }
+
 template <typename IO>
 __device__ __forceinline__ float load_io(const IO* p, int64_t i);
 template <>
@@ -45,6 +49,27 @@ __device__ __forceinline__ void store_io<float>(float* p, int64_t i, float x) {
 template <>
 __device__ __forceinline__ void store_io<bf16_t>(bf16_t* p, int64_t i, float x) {
   p[i].bits = f32_to_bf16(x);
+}
+
+// Raw buffer access (CDNA buffer instructions): a resource of `bytes` bytes at `base` in
+// four SGPRs, one 32-bit VGPR offset per lane and a scalar offset per access, so a
+// thread's 16 rows of state cost one address register instead of 16 64-bit pointers.
+// Accesses past `bytes` read 0 and are dropped on write.
+typedef float f32x4_raw __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_raw __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  // word 3: 32-bit data format, the raw-buffer setting for this architecture family
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ float4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const f32x4_raw v = __builtin_bit_cast(f32x4_raw, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+// Non-temporal 16-byte store (cache policy bit 1: nt).
+__device__ __forceinline__ void buffer_store16_nt(__amdgpu_buffer_rsrc_t r, int voff, int soff, const float4& v) {
+  const f32x4_raw x = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_raw, x), r, voff, soff, 2);
 }
 
 // Streaming store of 16 bytes: marked non-temporal so that a buffer written once per

@@ -19,12 +19,19 @@ struct LayerParams {
   const float* norm_w;
 };
 
+// Decode of up to `tokens` consecutive tokens per sequence (one token: the decode step).
+// Activations are [batch][tokens][...]; ntok (device, or null for all) gives each
+// sequence's count.  state_out / ring_out may equal state_in / ring_in; out may be null.
 struct DecodeArgs {
   LayerParams L;
   int32_t batch;
+  int32_t tokens;
+  const int32_t* ntok;
   const void *q, *k, *v, *z, *beta, *gate;
-  float* state;
-  float* ring;
+  const float* state_in;
+  const float* ring_in;
+  float* state_out;
+  float* ring_out;
   void* out;
 };
 

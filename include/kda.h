@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
   KDA_OK = 0,
@@ -121,12 +121,43 @@ kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
  * same math as a one-token prime).  q, k, v, z, gate [batch][H * d] io; beta [batch][H] io.
  * state fp32 [batch][H][d][d] and ring fp32 [batch][3 * H * d][kernel - 1] are read and
  * updated in place (the ring shifts by one token).  out [batch][H * d] io.  batch = 0 is a
- * no-op.  state must be 16-byte aligned.
+ * no-op.  state must be 16-byte aligned.  Runs the kernel of kda_decode_multi with one row.
  */
 kda_status kda_decode_step(const kda_layer* layer, kda_dtype io, int32_t batch, const void* q,
                            const void* k, const void* v, const void* z, const void* beta,
                            const void* gate, float* state, float* ring, void* out,
                            hipStream_t stream);
+
+/*
+ * Several consecutive decode tokens per sequence in one launch: the batched verify of
+ * speculative decoding, and its rollback by replay (docs.rs "memra_engine::kda":
+ * kda_verify_rows_cached runs t = K + 1 rows of every sequence with the recurrence
+ * sequential inside one launch over register-resident state; kda_verify_rollback_rows and
+ * kda_scan_replay rebuild the state after the first `keep` rows by replaying the same
+ * launch from the pre-round state).
+ *   tokens     rows per sequence, >= 0; activations are [batch][tokens][H * d] io (row
+ *              b * tokens + s), beta [batch][tokens][H] io.
+ *   ntok_dev   int32 [batch] device, the number of rows to run for each sequence (values
+ *              are clamped to [0, tokens]); NULL runs all `tokens` rows.
+ *   state_in / ring_in    fp32 [batch][H][d][d] / [batch][3 * H * d][kernel - 1]: the state
+ *              and conv history before the first row (read only).
+ *   state_out / ring_out  the same shapes: after the sequence's last row run.  They may
+ *              equal state_in / ring_in (in place); partial overlap is invalid.
+ *   out        [batch][tokens][H * d] io, or NULL to skip the outputs (a replay); rows at or
+ *              past a sequence's count are not written.
+ * Each row's arithmetic is the same instruction sequence a one-token launch executes, so
+ * the outputs and final states are bit-identical to chaining one-token steps; that is what
+ * makes rollback exact: keep the pre-round buffers (ping-pong: state_out != state_in), run
+ * all rows, and if sequence b accepts only keep[b] rows, call again from the pre-round
+ * buffers with ntok = keep.  kda_decode_step is this call with tokens = 1.  batch = 0 is a
+ * no-op; a sequence with 0 rows copies its state and ring through.  state buffers must be
+ * 16-byte aligned.
+ */
+kda_status kda_decode_multi(const kda_layer* layer, kda_dtype io, int32_t batch, int32_t tokens,
+                            const int32_t* ntok_dev, const void* q, const void* k, const void* v,
+                            const void* z, const void* beta, const void* gate,
+                            const float* state_in, const float* ring_in, float* state_out,
+                            float* ring_out, void* out, hipStream_t stream);
 
 /* Short name of a status code. */
 const char* kda_status_string(kda_status status);

@@ -27,7 +27,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert names == sorted(["kda_prefill_workspace_bytes", "kda_prefill", "kda_decode_step",
-                            "kda_status_string", "kda_last_error", "kda_abi_version"])
+                            "kda_decode_multi", "kda_status_string", "kda_last_error",
+                            "kda_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -71,6 +72,33 @@ def test_decode_validation():
     assert _decode(lib, _layer(kda), batch=0) == 0  # no-op, nothing launched
     assert lib.kda_last_error() == b""
     assert lib.kda_decode_step(ctypes.byref(_layer(kda)), 7, 1, *([FAKE] * 9), None) == 1
+
+
+def _multi(lib, layer, batch=2, tokens=3, q=FAKE, s_in=FAKE, r_in=FAKE, s_out=FAKE, r_out=FAKE):
+    return lib.kda_decode_multi(ctypes.byref(layer), 1, batch, tokens, None, q, FAKE, FAKE, FAKE,
+                                FAKE, FAKE, s_in, r_in, s_out, r_out, FAKE, None)
+
+
+def test_decode_multi_validation():
+    """Rejections happen before any launch (nothing reaches the GPU on these paths)."""
+    kda, lib = _lib()
+    H, d = 2, 128
+    sbytes = 2 * H * d * d * 4
+    rbytes = 2 * 3 * H * d * 3 * 4
+    assert _multi(lib, _layer(kda, head_dim=64)) == 2
+    assert _multi(lib, _layer(kda), tokens=-1) == 1
+    assert b"tokens" in lib.kda_last_error()
+    assert _multi(lib, _layer(kda), batch=-1) == 1
+    assert _multi(lib, _layer(kda), s_in=0) == 1
+    assert _multi(lib, _layer(kda), r_out=0) == 1
+    assert _multi(lib, _layer(kda), q=0) == 1                    # activations needed when tokens > 0
+    assert _multi(lib, _layer(kda), s_out=FAKE + 8) == 1         # misaligned state_out
+    assert _multi(lib, _layer(kda), s_out=FAKE + sbytes // 2) == 1  # partial overlap with state_in
+    assert b"overlap" in lib.kda_last_error()
+    assert _multi(lib, _layer(kda), r_out=FAKE + rbytes // 2) == 1  # partial overlap of the rings
+    assert _multi(lib, _layer(kda), batch=0) == 0                 # no-op, nothing launched
+    assert lib.kda_last_error() == b""
+    assert lib.kda_decode_multi(ctypes.byref(_layer(kda)), 7, 1, 1, None, *([FAKE] * 11), None) == 1
 
 
 def _prefill(lib, layer, cu, total, ws_bytes=0, lb_ok=True):
