@@ -16,6 +16,8 @@ constexpr int C = 16;  // chunk = exponent tile
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 // exp(x) through the hardware base-2 exponential; relative error ~1e-6 over the ranges
 // used here (|x| <= 80).
@@ -101,6 +103,11 @@ __device__ __forceinline__ void split_vec(const float* x, V& hi, V& lo) {
 __device__ __forceinline__ f32x4_t mma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// fp16 operands: 3 more mantissa bits than bf16, for the products whose operands stay
+// inside fp16's range (the state pass against the state, see the prefill kernel)
+__device__ __forceinline__ f32x4_t mma32h(f16x8_t a, f16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4_t mma16(bf16x4_t a, bf16x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
@@ -161,6 +168,12 @@ __device__ __forceinline__ void store4(__bf16* hi, __bf16* lo, const float* x) {
   split_vec<4>(x, h, l);
   *reinterpret_cast<bf16x4_t*>(hi) = h;
   *reinterpret_cast<bf16x4_t*>(lo) = l;
+}
+__device__ __forceinline__ void store4_f16(_Float16* dst, const float* x) {
+  f16x4_t h;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) h[v] = static_cast<_Float16>(x[v]);
+  *reinterpret_cast<f16x4_t*>(dst) = h;
 }
 __device__ __forceinline__ void store4_hi(__bf16* hi, const float* x) {
   bf16x4_t h;

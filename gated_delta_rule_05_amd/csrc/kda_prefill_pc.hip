@@ -8,10 +8,11 @@
 //   * 8 producer waves build everything chunk c+1 needs from its raw rows alone: short
 //     conv + SiLU, gate and Gcum, q/k norms, MFMA-ready operands (bf16 hi/lo) and the
 //     Gram tiles A and P, while the next-but-one chunk's raw rows stream from HBM straight
-//     into LDS; one of them also forms chunk c's T = (I + A)^-1 Diag(beta) (DPP
-//     elimination, once per chunk);
+//     into LDS;
 //   * 8 consumer waves run chunk c's state pass, one 16-column value tile of the fp32
-//     128x128 state each, held in MFMA accumulators for the whole sequence: O = Qa S;
+//     128x128 state each, held in MFMA accumulators for the whole sequence: O = Qa S,
+//     beside which one of them forms T = (I + A)^-1 Diag(beta) (DPP elimination, once
+//     per chunk);
 //     then U~ = T V, W^T = Ka^T T^T (landing in the A-operand layout of W.S),
 //     U = U~ - W S, O += P U; then the gated RMSNorm epilogue; then
 //     S <- Diag(e^Gcum_C) S + Kl^T U.
@@ -33,11 +34,10 @@ using namespace mf;
 constexpr int PW = 8;                  // producer waves
 constexpr int CWN = 8;                 // consumer waves
 constexpr int PT = 64 * PW;            // producer threads
-// Producer waves that also run the once-per-chunk jobs: the T elimination goes to a gate
-// wave (the lightest role of the conv interval, on SIMD 3), the two Gram tiles to the v
-// waves (SIMDs 0 and 1), which are otherwise idle in interval 4.  Wave w runs on SIMD
-// w % 4.
-constexpr int kElimWave = 7;
+// Waves that also run the once-per-chunk jobs (wave w runs on SIMD w % 4): the T
+// elimination goes to a consumer wave, whose interval 1 is light; the two Gram tiles to
+// the v producer waves (SIMDs 0 and 1), which are otherwise idle in interval 4.
+constexpr int kElimCw = 2;  // consumer wave PW + 2, on SIMD 2
 constexpr int kGramAWave = 4;
 constexpr int kGramPWave = 5;
 constexpr int NT = 64 * (PW + CWN);
@@ -51,7 +51,7 @@ struct PcOrder {
 
 // What consumers read for one chunk (double-buffered by chunk parity).
 struct alignas(16) KBuf {
-  __bf16 qa[2][C][OPP];         // Qa = q-hat exp(Gcum), hi/lo, key order of the .S products
+  _Float16 qa[C][OPP];          // Qa = q-hat exp(Gcum), fp16, key order of the .S products
   __bf16 kat[kHeadDim][KTP];    // Ka^T, hi
   __bf16 klt[2][kHeadDim][KTP]; // Kl^T, hi/lo
   __bf16 p[2][C][20];           // P (lower incl.), hi/lo
@@ -273,27 +273,6 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         }
         if (t < C) KN.beta[t] = (t < Ln) ? fsigmoid(bf16_to_f32(sm.braw[t])) : 0.f;
       }
-      if (i >= 0 && uwave == kElimWave) {
-        KBuf& K = sm.kb[i & 1];  // chunk i, whose state pass runs now
-        // T = (I + A)^-1 Diag(beta) by elimination with rows spread over lanes (DPP
-        // broadcasts inside each 16-lane row); A[r][j] = 0 for j >= r, so the update
-        // is unconditional.  Lane (lm, lq) ends up with T[lm][lq + 4 s].
-        float arow[C], tt[4];
-#pragma unroll
-        for (int j = 0; j < C; j += 4) {
-          const float4 v4 = *reinterpret_cast<const float4*>(&sm.A[lm][j]);
-          arow[j] = v4.x;
-          arow[j + 1] = v4.y;
-          arow[j + 2] = v4.z;
-          arow[j + 3] = v4.w;
-        }
-        const float bl = K.beta[lm];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) tt[s] = (lq + 4 * s == lm) ? bl : 0.f;
-        eliminate_strided<0>(tt, arow);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) split_store(&K.tm[0][lm][lq + 4 * s], &K.tm[1][lm][lq + 4 * s], tt[s]);
-      }
       lds_barrier();
 
       // ---------------------------------------------------------- interval 2
@@ -353,7 +332,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         // Qa in the key order of the .S products: channels 32 kb + 4 m .. + 3 sit at
         // 32 kb + 8 (m % 4) + 4 (m / 4)
         const int pa = 32 * (c4 >> 5) + 8 * ((c4 >> 2) & 3) + 4 * ((c4 >> 4) & 1);
-        store4(&KN.qa[0][r][pa], &KN.qa[1][r][pa], qa);
+        store4_f16(&KN.qa[r][pa], qa);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           KN.kat[c4 + v][r] = static_cast<__bf16>(ka[v]);
@@ -366,7 +345,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       if (has_next && (uwave == kGramAWave || uwave == kGramPWave)) {
         const bool gram_a = uwave == kGramAWave;
         // Gram tiles of chunk i + 1: A = Kp Km^T (strict lower, times beta_r), eliminated
-        // by wave kElimWave in the next interval 1; P = Qp Km^T (lower incl.)
+        // by consumer wave kElimCw in the next interval 1; P = Qp Km^T (lower incl.)
         const __bf16(*Xh)[OPP] = gram_a ? sm.kp[0] : sm.qp[0];
         const __bf16(*Xl)[OPP] = gram_a ? sm.kp[1] : sm.qp[1];
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
@@ -443,33 +422,43 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       KBuf& K = sm.kb[i & 1];
       KBuf& KN = sm.kb[(i + 1) & 1];
       f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-      bf16x8_t sh[4], sl[4];
+      f16x8_t sf[4];
 
       // ---------------------------------------------------------- interval 1
       if (i >= 0) {
-        // S as bf16 hi/lo B operands (per 32 keys: 4 lq + s, then 16 + 4 lq + s)
+        if (cw == kElimCw) {
+          // T = (I + A)^-1 Diag(beta) by elimination with rows spread over lanes (DPP
+          // broadcasts inside each 16-lane row); A[r][j] = 0 for j >= r, so the update
+          // is unconditional.  Lane (lm, lq) ends up with T[lm][lq + 4 s].
+          float arow[C], tt[4];
+  #pragma unroll
+          for (int j = 0; j < C; j += 4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(&sm.A[lm][j]);
+            arow[j] = v4.x;
+            arow[j + 1] = v4.y;
+            arow[j + 2] = v4.z;
+            arow[j + 3] = v4.w;
+          }
+          const float bl = K.beta[lm];
+  #pragma unroll
+          for (int s = 0; s < 4; ++s) tt[s] = (lq + 4 * s == lm) ? bl : 0.f;
+          eliminate_strided<0>(tt, arow);
+  #pragma unroll
+          for (int s = 0; s < 4; ++s) split_store(&K.tm[0][lm][lq + 4 * s], &K.tm[1][lm][lq + 4 * s], tt[s]);
+        }
+        // S as fp16 B operands (per 32 keys: 4 lq + s, then 16 + 4 lq + s)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          float b8[8];
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            b8[s] = S[2 * kb][s];
-            b8[4 + s] = S[2 * kb + 1][s];
+            sf[kb][s] = static_cast<_Float16>(S[2 * kb][s]);
+            sf[kb][4 + s] = static_cast<_Float16>(S[2 * kb + 1][s]);
           }
-          split_vec<8>(b8, sh[kb], sl[kb]);
         }
-        // O = Qa S, both split
-        f32x4_t o1 = {0.f, 0.f, 0.f, 0.f};
+        // O = Qa S
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const int o = 32 * kb + 8 * lq;
-          const bf16x8_t qh = ld<bf16x8_t>(&K.qa[0][lm][o]);
-          const bf16x8_t ql = ld<bf16x8_t>(&K.qa[1][lm][o]);
-          O = mma32(qh, sh[kb], O);
-          o1 = mma32(qh, sl[kb], o1);
-          o1 = mma32(ql, sh[kb], o1);
-        }
-        O += o1;
+        for (int kb = 0; kb < 4; ++kb)
+          O = mma32h(ld<f16x8_t>(&K.qa[lm][32 * kb + 8 * lq]), sf[kb], O);
       }
       lds_barrier();
 
@@ -496,13 +485,13 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
                                    f32x4_t{0.f, 0.f, 0.f, 0.f});
           const f32x4_t w1 = mma16(ld<bf16x4_t>(&K.kat[32 * kb + 16 + lm][4 * lq]), th,
                                    f32x4_t{0.f, 0.f, 0.f, 0.f});
-          bf16x8_t wb;
+          f16x8_t wb;
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            wb[s] = static_cast<__bf16>(w0[s]);
-            wb[4 + s] = static_cast<__bf16>(w1[s]);
+            wb[s] = static_cast<_Float16>(w0[s]);
+            wb[4 + s] = static_cast<_Float16>(w1[s]);
           }
-          ws = mma32(wb, sh[kb], ws);
+          ws = mma32h(wb, sf[kb], ws);
         }
         const f32x4_t U = Ut - ws;
         {
