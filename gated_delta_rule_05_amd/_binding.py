@@ -141,13 +141,15 @@ def prefill_workspace_bytes(layer: Layer, io_dtype: torch.dtype, cu_seqlens_host
 
 def prefill(layer: Layer, q, k, v, z, beta, gate, cu_seqlens, cu_seqlens_host=None,
             state_in=None, ring_in=None, out=None, state_out=None, ring_out=None,
-            final_state: bool = True, workspace=None, stream=None):
+            final_state: bool = True, workspace=None, allow_split: bool = True, stream=None):
     """Chunked prefill over packed sequences (see kda_prefill in include/kda.h).
 
     q, k, v, z, gate: [T, H*128] io (fp32 or bf16); beta: [T, H] io.  cu_seqlens: int32
     [N+1] on the GPU; cu_seqlens_host: the same on the CPU (copied from the GPU, with a
     sync, when omitted).  Returns (out, state_out, ring_out); the last two are None when
-    final_state is False and no buffers were passed.
+    final_state is False and no buffers were passed.  The workspace the library asks for
+    (segment-parallel path for few (sequence, head) units) is allocated when not given;
+    allow_split=False passes none, so the whole-sequence path runs.
     """
     lib = load()
     dev = layer.device
@@ -180,7 +182,9 @@ def prefill(layer: Layer, q, k, v, z, beta, gate, cu_seqlens, cu_seqlens_host=No
     if ring_out is not None:
         _need(ring_out, "ring_out", (N, 3 * Hd, CONV_KERNEL - 1), torch.float32, dev)
     need = int(lib.kda_prefill_workspace_bytes(ctypes.byref(layer.c), io, N, _ptr(cu_h), T))
-    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+    if not allow_split:
+        workspace = None
+    elif need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.kda_prefill(ctypes.byref(layer.c), io, N, _ptr(cu_seqlens), _ptr(cu_h), T,

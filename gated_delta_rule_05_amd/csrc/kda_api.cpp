@@ -67,6 +67,40 @@ kda::LayerParams layer_params(const kda_layer* L) {
 
 bool io_ok(kda_dtype io) { return io == KDA_F32 || io == KDA_BF16; }
 
+// Splitting sequences into segments pays when there are too few (sequence, head) units to
+// fill the chip's 256 compute units: each sequence is cut into about 256 / units segments
+// of at least 256 tokens (a multiple of the 16-token chunk), and the three passes then run
+// about 3 segment-times instead of one sequence-time.
+constexpr int64_t kSplitMaxUnits = 96;
+constexpr int32_t kSplitMinSeg = 256;
+constexpr int32_t kSplitTarget = 256;
+
+bool make_split_plan(const kda_layer* L, kda_dtype io, int32_t N, const int32_t* cu,
+                     kda::SplitPlan* plan, size_t* bytes) {
+  *bytes = 0;
+  if (io != KDA_BF16 || N <= 0 || N > kda::kMaxSplitSeqs || !L || L->num_heads <= 0) return false;
+  const int64_t units = static_cast<int64_t>(N) * L->num_heads;
+  if (units >= kSplitMaxUnits) return false;
+  int32_t tmax = 0;
+  for (int32_t n = 0; n < N; ++n) tmax = std::max(tmax, cu[n + 1] - cu[n]);
+  const int64_t kwant = (kSplitTarget + units - 1) / units;
+  int64_t seg = (tmax + kwant - 1) / kwant;
+  seg = std::max<int64_t>(kSplitMinSeg, (seg + 15) / 16 * 16);
+  if (seg >= tmax) return false;  // nothing would be split
+  plan->seg_len = static_cast<int32_t>(seg);
+  int32_t total = 0;
+  for (int32_t n = 0; n < N; ++n) {
+    plan->first[n] = total;
+    const int32_t len = cu[n + 1] - cu[n];
+    total += std::max<int32_t>(1, static_cast<int32_t>((len + seg - 1) / seg));
+  }
+  plan->first[N] = total;
+  plan->nseg = total;
+  *bytes = 3ull * static_cast<size_t>(total) * static_cast<size_t>(L->num_heads) *
+           kda::kHeadDimHost * kda::kHeadDimHost * sizeof(float);
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -145,8 +179,11 @@ kda_status kda_decode_multi(const kda_layer* layer, kda_dtype io, int32_t batch,
 
 size_t kda_prefill_workspace_bytes(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
                                    const int32_t* cu_seqlens_host, int64_t total_tokens) {
-  (void)layer; (void)io; (void)num_seqs; (void)cu_seqlens_host; (void)total_tokens;
-  return 0;
+  (void)total_tokens;
+  if (!cu_seqlens_host || num_seqs <= 0) return 0;
+  kda::SplitPlan plan;
+  size_t bytes = 0;
+  return make_split_plan(layer, io, num_seqs, cu_seqlens_host, &plan, &bytes) ? bytes : 0;
 }
 
 kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
@@ -179,10 +216,10 @@ kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
   if (total_tokens > 0 &&
       (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(gate)))
     return fail(KDA_ERR_INVALID_ARG, "q, k, v, z and gate must be 16-byte aligned");
-  const size_t need = kda_prefill_workspace_bytes(layer, io, num_seqs, cu_seqlens_host, total_tokens);
-  if (workspace_bytes < need || (need > 0 && !workspace))
-    return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
-                workspace_bytes, need);
+  if (workspace_bytes > 0 && !workspace)
+    return fail(KDA_ERR_WORKSPACE, "workspace is NULL but workspace_bytes = %zu", workspace_bytes);
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (static_cast<int64_t>(num_seqs) * layer->num_heads > 0x7fffffffLL)
     return fail(KDA_ERR_INVALID_ARG, "num_seqs * num_heads exceeds the grid limit");
 
@@ -204,7 +241,23 @@ kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
   a.out = out;
   a.state_out = state_out;
   a.ring_out = ring_out;
-  hipError_t e = kda::launch_prefill(a, io, order.data(), stream);
+  a.pass = kda::kPassWhole;
+  a.seg_b = a.seg_m = a.seg_start = nullptr;
+
+  kda::SplitPlan plan;
+  size_t need = 0;
+  hipError_t e;
+  if (make_split_plan(layer, io, num_seqs, cu_seqlens_host, &plan, &need) && workspace_bytes >= need) {
+    const size_t plane = static_cast<size_t>(plan.nseg) * layer->num_heads * kda::kHeadDimHost *
+                         kda::kHeadDimHost;
+    float* ws = static_cast<float*>(workspace);
+    a.seg_b = ws;
+    a.seg_m = ws + plane;
+    a.seg_start = ws + 2 * plane;
+    e = kda::launch_prefill_bf16_split(a, plan, stream);
+  } else {
+    e = kda::launch_prefill(a, io, order.data(), stream);
+  }
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -38,6 +38,17 @@ struct DecodeArgs {
 // Longest-first order of the sequences for the prefill grid, passed by value.
 constexpr int kMaxOrdered = 512;
 
+// Prefill passes.  Whole: one workgroup per (sequence, head).  With few (sequence, head)
+// units the sequences are cut into segments that run in parallel, using that the state
+// recurrence is affine in its start state, S_end = M S_start + B:
+//   Transfer: for every segment but a sequence's last, B (from a zero start; the first
+//             segment from the true start) and M (from the identity start with v = 0),
+//             no outputs;
+//   Final:    every segment from its true start state (segment 0: the sequence's, later
+//             ones: S_{k+1} = M_k S_k + B_k, formed in between), with outputs; the last
+//             segment writes the final state and ring.
+enum : int32_t { kPassWhole = 0, kPassTransfer = 1, kPassFinal = 2 };
+
 struct PrefillArgs {
   LayerParams L;
   int32_t num_seqs;
@@ -48,6 +59,18 @@ struct PrefillArgs {
   void* out;
   float* state_out;
   float* ring_out;
+  int32_t pass;
+  float* seg_b;            // [segments][H][d][d]
+  float* seg_m;            // [segments][H][d][d]
+  float* seg_start;        // [segments][H][d][d]
+};
+
+// Segment k of sequence n covers tokens [cu[n] + k L, min(cu[n + 1], cu[n] + (k + 1) L)).
+constexpr int kMaxSplitSeqs = 64;
+struct SplitPlan {
+  int32_t seg_len;                   // L, a multiple of the 16-token chunk
+  int32_t nseg;                      // segments in total
+  int32_t first[kMaxSplitSeqs + 1];  // first segment of each sequence; first[N] = nseg
 };
 
 hipError_t launch_decode(const DecodeArgs& a, kda_dtype io, hipStream_t stream);
@@ -55,5 +78,7 @@ hipError_t launch_prefill(const PrefillArgs& a, kda_dtype io, const int32_t* ord
                           hipStream_t stream);
 // bf16 io: the producer/consumer kernel of kda_prefill_pc.hip
 hipError_t launch_prefill_bf16(const PrefillArgs& a, const int32_t* order_host, hipStream_t stream);
+// bf16 io, split into segments: Transfer pass, combine, Final pass (a.seg_* set)
+hipError_t launch_prefill_bf16_split(const PrefillArgs& a, const SplitPlan& plan, hipStream_t stream);
 
 }  // namespace kda

@@ -94,19 +94,45 @@ static_assert(offsetof(PcSmem, kb) % 16 == 0 && sizeof(KBuf) % 16 == 0 &&
                   offsetof(PcSmem, kp) % 16 == 0 && offsetof(PcSmem, km) % 16 == 0,
               "16-byte aligned LDS members");
 
-__global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder order) {
+__global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder order, SplitPlan plan) {
   __shared__ PcSmem sm;
   // raw rows of q, k, v, z of the next-but-one chunk, unpadded
   __shared__ __attribute__((aligned(16))) uint16_t raw_lds[4][C][kHeadDim];
   // raw output-gate rows, double-buffered by chunk parity (read by the epilogue)
   __shared__ __attribute__((aligned(16))) uint16_t graw_lds[2][C][kHeadDim];
 
+  // This workgroup's (sequence n, head h) and tokens [t0, t0 + T): a whole sequence, or
+  // segment kseg of nsegs (see the passes in kda_internal.h).
   const int H = a.L.H;
-  const int rank = blockIdx.x / H;
-  const int h = blockIdx.x - rank * H;
-  const int n = (a.num_seqs <= kMaxOrdered) ? order.idx[rank] : rank;
-  const int64_t t0 = a.cu_seqlens[n];
-  const int T = a.cu_seqlens[n + 1] - static_cast<int>(t0);
+  int n, h, seg = 0, kseg = 0, nsegs = 1;
+  bool transfer_m = false;  // Transfer pass, M half: identity start, v = 0
+  int64_t t0;
+  int T;
+  if (a.pass == kPassWhole) {
+    const int rank = blockIdx.x / H;
+    h = blockIdx.x - rank * H;
+    n = (a.num_seqs <= kMaxOrdered) ? order.idx[rank] : rank;
+    t0 = a.cu_seqlens[n];
+    T = a.cu_seqlens[n + 1] - static_cast<int>(t0);
+  } else {
+    int blk = blockIdx.x;
+    if (a.pass == kPassTransfer && blk >= plan.nseg * H) {
+      transfer_m = true;
+      blk -= plan.nseg * H;
+    }
+    seg = blk / H;
+    h = blk - seg * H;
+    n = 0;
+    while (plan.first[n + 1] <= seg) ++n;
+    kseg = seg - plan.first[n];
+    nsegs = plan.first[n + 1] - plan.first[n];
+    t0 = a.cu_seqlens[n] + static_cast<int64_t>(kseg) * plan.seg_len;
+    T = min(static_cast<int>(a.cu_seqlens[n + 1] - t0), plan.seg_len);
+    // the Transfer pass needs neither the last segment's end state nor the first's M
+    if (a.pass == kPassTransfer && (kseg == nsegs - 1 || (transfer_m && kseg == 0))) return;
+  }
+  const bool write_out = a.pass != kPassTransfer;
+  const bool last_seg = kseg == nsegs - 1;
   const int64_t Hd = static_cast<int64_t>(H) * kHeadDim;
   const int nch = (T + C - 1) / C;
 
@@ -133,7 +159,13 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     if (urole < 3) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) w[j] = a.L.conv_w[(role * Hd + c) * kConvTaps + j];
-      if (a.ring_in) {
+      if (kseg > 0) {
+        // a later segment: the conv history is the previous segment's last raw rows
+        // (segments before the last are at least one chunk long)
+        const bf16_t* pl = static_cast<const bf16_t*>(urole == 0 ? a.q : urole == 1 ? a.k : a.v);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) hist[j] = bf16_to_f32(pl[(t0 - 3 + j) * Hd + c].bits);
+      } else if (a.ring_in) {
         const float* rin = a.ring_in + static_cast<int64_t>(n) * 3 * Hd * kRingTaps;
 #pragma unroll
         for (int j = 0; j < 3; ++j) hist[j] = rin[(role * Hd + c) * kRingTaps + j];
@@ -221,7 +253,11 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 #pragma unroll
         for (int r = 0; r < C; ++r) xr[r] = raw_lds[urole][r][ch];
         const bool full = Ln == C;
-        if (urole < 3) {
+        if (urole == 2 && transfer_m) {
+          // the transfer matrix is the end state from the identity with v = 0
+#pragma unroll
+          for (int r = 0; r < C; ++r) KN.V[r][ch] = 0.f;
+        } else if (urole < 3) {
           float(*dst)[LDP] = urole == 0 ? sm.aq : urole == 1 ? sm.ak : KN.V;
           if (full) {
 #pragma unroll
@@ -379,7 +415,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     }
 
     // conv history of q, k, v -> ring
-    if (a.ring_out && urole < 3) {
+    if (a.ring_out && urole < 3 && write_out && last_seg) {
       float* rout = a.ring_out + static_cast<int64_t>(n) * 3 * Hd * kRingTaps;
 #pragma unroll
       for (int j = 0; j < 3; ++j) rout[(role * Hd + c) * kRingTaps + j] = hist[j];
@@ -387,16 +423,25 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
   } else {
     // ============================================================== consumer waves
     f32x4_t S[8];
-    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * kHeadDim * kHeadDim;
-    if (a.state_in) {
-      const float* sp = a.state_in + sbase + opaque(4 * lq * kHeadDim + col);
+    constexpr int64_t kDD = kHeadDim * kHeadDim;
+    const int64_t nbase = (static_cast<int64_t>(n) * H + h) * kDD;    // [N][H] planes
+    const int64_t sgbase = (static_cast<int64_t>(seg) * H + h) * kDD; // [segments][H] planes
+    const float* src = nullptr;
+    if (a.pass == kPassFinal && kseg > 0)
+      src = a.seg_start + sgbase;
+    else if (kseg == 0 && !transfer_m && a.state_in)
+      src = a.state_in + nbase;
+    if (src) {
+      const float* sp = src + opaque(4 * lq * kHeadDim + col);
 #pragma unroll
       for (int it = 0; it < 8; ++it)
 #pragma unroll
         for (int s = 0; s < 4; ++s) S[it][s] = sp[(16 * it + s) * kHeadDim];
     } else {
 #pragma unroll
-      for (int it = 0; it < 8; ++it) S[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int it = 0; it < 8; ++it)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) S[it][s] = (transfer_m && 16 * it + 4 * lq + s == col) ? 1.f : 0.f;
     }
     const float nw = a.L.norm_w[col];
     lds_barrier();
@@ -509,7 +554,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       lds_barrier();
 
       // ---------------------------------------------------------- interval 3
-      if (i >= 0) {
+      if (i >= 0 && write_out) {
         // gated RMSNorm of the chunk's output rows and the store
         const int L = min(C, T - i * C);
         float tot[4];
@@ -553,8 +598,13 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       lds_barrier();
     }
 
-    if (a.state_out) {
-      float* sp = a.state_out + sbase + opaque(4 * lq * kHeadDim + col);
+    float* dst = nullptr;
+    if (a.pass == kPassTransfer)
+      dst = (transfer_m ? a.seg_m : a.seg_b) + sgbase;
+    else if (last_seg && a.state_out)
+      dst = a.state_out + nbase;
+    if (dst) {
+      float* sp = dst + opaque(4 * lq * kHeadDim + col);
 #pragma unroll
       for (int it = 0; it < 8; ++it)
 #pragma unroll
@@ -569,8 +619,89 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, const int32_t* order_host, 
   PcOrder ord;
   const int nord = a.num_seqs < kMaxOrdered ? a.num_seqs : kMaxOrdered;
   for (int i = 0; i < kMaxOrdered; ++i) ord.idx[i] = i < nord ? order_host[i] : 0;
+  SplitPlan none{};
+  PrefillArgs w = a;
+  w.pass = kPassWhole;
   const dim3 grid(static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.L.H));
-  hipLaunchKernelGGL(prefill_pc_kernel, grid, dim3(NT), 0, stream, a, ord);
+  hipLaunchKernelGGL(prefill_pc_kernel, grid, dim3(NT), 0, stream, w, ord, none);
+  return hipGetLastError();
+}
+
+namespace {
+
+// S_{k+1} = M_k S_k + B_k over the segments of each sequence, for one 16-column block of
+// one head's state (value columns never mix, so the blocks are independent).  S_1 = B_0:
+// segment 0 started from the true state.  256 threads: thread t forms rows t / 2, columns
+// 8 (t % 2) .. + 7 of the block; the block itself sits in LDS.  fp32 FMAs in a fixed order.
+__global__ __launch_bounds__(256) void combine_kernel(PrefillArgs a, SplitPlan plan) {
+  constexpr int CB = 16;
+  __shared__ float sblk[kHeadDim][CB];
+  const int H = a.L.H;
+  const int nb = kHeadDim / CB;
+  const int unit = blockIdx.x / nb;
+  const int cb = blockIdx.x - unit * nb;
+  const int n = unit / H;
+  const int h = unit - n * H;
+  const int t = threadIdx.x;
+  const int r = t >> 1, c0 = 8 * (t & 1);
+  const int first = plan.first[n], nsegs = plan.first[n + 1] - plan.first[n];
+  if (nsegs < 2) return;
+  constexpr int64_t kDD = kHeadDim * kHeadDim;
+  auto plane = [&](float* base, int k) { return base + ((static_cast<int64_t>(first + k)) * H + h) * kDD; };
+  // S_1 = B_0
+  float acc[8];
+  {
+    const float* b0 = plane(a.seg_b, 0) + r * kHeadDim + cb * CB + c0;
+    float* s1 = plane(a.seg_start, 1) + r * kHeadDim + cb * CB + c0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[j] = b0[j];
+      s1[j] = acc[j];
+      sblk[r][c0 + j] = acc[j];
+    }
+  }
+  for (int k = 1; k + 1 < nsegs; ++k) {
+    __syncthreads();
+    const float* mrow = plane(a.seg_m, k) + r * kHeadDim;
+    const float* brow = plane(a.seg_b, k) + r * kHeadDim + cb * CB + c0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+    for (int l = 0; l < kHeadDim; l += 4) {
+      const float4 m4 = *reinterpret_cast<const float4*>(mrow + l);
+      const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(mv[u], sblk[l + u][c0 + j], acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] += brow[j];
+    __syncthreads();
+    float* snext = plane(a.seg_start, k + 1) + r * kHeadDim + cb * CB + c0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      sblk[r][c0 + j] = acc[j];
+      snext[j] = acc[j];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16_split(const PrefillArgs& a, const SplitPlan& plan, hipStream_t stream) {
+  PcOrder none{};
+  const unsigned H = static_cast<unsigned>(a.L.H);
+  PrefillArgs w = a;
+  w.pass = kPassTransfer;
+  hipLaunchKernelGGL(prefill_pc_kernel, dim3(2u * plan.nseg * H), dim3(NT), 0, stream, w, none, plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(a.num_seqs) * H * (kHeadDim / 16)),
+                     dim3(256), 0, stream, w, plan);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  w.pass = kPassFinal;
+  hipLaunchKernelGGL(prefill_pc_kernel, dim3(plan.nseg * H), dim3(NT), 0, stream, w, none, plan);
   return hipGetLastError();
 }
 

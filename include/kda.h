@@ -56,7 +56,7 @@ typedef enum {
   KDA_OK = 0,
   KDA_ERR_INVALID_ARG = 1, /* null or misaligned pointer, bad size, inconsistent cu_seqlens */
   KDA_ERR_UNSUPPORTED = 2, /* head_dim != 128, conv kernel != 4, lower bound outside [-5, 0] */
-  KDA_ERR_WORKSPACE = 3,   /* workspace smaller than kda_prefill_workspace_bytes() */
+  KDA_ERR_WORKSPACE = 3,   /* workspace NULL with a nonzero size, or not 256-byte aligned */
   KDA_ERR_HIP = 4          /* the HIP runtime refused a launch */
 } kda_status;
 
@@ -85,9 +85,12 @@ typedef struct kda_layer {
 } kda_layer;
 
 /*
- * Bytes of device workspace kda_prefill() needs for this problem (may be 0).  The
- * workspace holds per-chunk partial results when a head's value columns are split across
- * several workgroups.  Returns 0 also for invalid arguments (kda_prefill reports those).
+ * Bytes of device workspace with which kda_prefill() takes its fastest path for this
+ * problem (0 when that path needs none).  With few (sequence, head) units -- bf16 io,
+ * fewer than 96 of them, at most 64 sequences -- the fastest path cuts the sequences into
+ * segments that run in parallel (the state recurrence is affine in its start state); the
+ * workspace then holds three fp32 states per (segment, head).  Returns 0 also for invalid
+ * arguments (kda_prefill reports those).
  */
 size_t kda_prefill_workspace_bytes(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
                                    const int32_t* cu_seqlens_host, int64_t total_tokens);
@@ -104,8 +107,10 @@ size_t kda_prefill_workspace_bytes(const kda_layer* layer, kda_dtype io, int32_t
  *   out       [total_tokens][H * d] io
  *   state_out fp32 [num_seqs][H][d][d] or NULL (not written); may equal state_in
  *   ring_out  fp32 [num_seqs][3 * H * d][kernel - 1] or NULL; may equal ring_in
- *   workspace device buffer of at least kda_prefill_workspace_bytes() bytes (may be NULL
- *             when that is 0).
+ *   workspace device buffer, 256-byte aligned, or NULL with workspace_bytes = 0.  With at
+ *             least kda_prefill_workspace_bytes() bytes the segment-parallel path may run;
+ *             with less, the whole-sequence path runs (same results up to rounding).  The
+ *             library keeps nothing in it after the call's work completes.
  * Partial overlap between inputs and outputs is invalid.  State pointers and q, k, v, z,
  * gate must be 16-byte aligned (the kernel reads activation rows in 16-byte pieces).
  */

@@ -118,9 +118,50 @@ def test_extreme_gates(zval, bval):
 
 
 def test_prefill_t4096_h32():
-    """1 sequence x 4096 tokens, 32 heads, bf16 io: every unit against the oracle."""
+    """1 sequence x 4096 tokens, 32 heads, bf16 io: every unit against the oracle.  With 32
+    (sequence, head) units this runs the segment-parallel path (8 segments)."""
     prob = synthetic.make_workload("prefill_t4096_h32", device=DEV)
+    kda = _kda()
+    layer = kda.Layer(**prob["layer"])
+    assert kda.prefill_workspace_bytes(layer, torch.bfloat16, prob["cu_seqlens"]) > 0
     _check(prob, _prefill(prob), _all_units(prob), "prefill_t4096_h32")
+
+
+def _split_problem(seed):
+    """Ragged sequences long enough to be cut into 256-token segments (and two that are
+    not: an empty one and a 2-token one), carried state and ring, and a quarter of the
+    channels at g = 0 exactly (z = -1e4), so that state crosses every segment boundary
+    undecayed."""
+    lens = [1000, 2, 0, 700, 300]
+    prob = synthetic.make_prefill(lens, H=3, io="bf16", seed=seed, device=DEV, init_state=True,
+                                  init_ring=True)
+    z = prob["z"].view(sum(lens), 3, D)
+    z[:, :, ::4] = -1e4
+    return prob
+
+
+def test_segment_parallel_path():
+    """The segment-parallel path (Transfer pass, combine, Final pass) against the oracle on
+    every unit, final states and rings included."""
+    prob = _split_problem(206)
+    kda = _kda()
+    layer = kda.Layer(**prob["layer"])
+    assert kda.prefill_workspace_bytes(layer, torch.bfloat16, prob["cu_seqlens"]) > 0
+    _check(prob, _prefill(prob), _all_units(prob), "segment_parallel")
+    _ring_exact(prob, _prefill(prob)[2])
+
+
+def test_segment_parallel_matches_whole_path():
+    """Both paths meet the oracle; with the same inputs their outputs differ only by
+    rounding (the segment path forms start states as M S + B)."""
+    prob = _split_problem(207)
+    split = _prefill(prob)
+    whole = _prefill(prob, allow_split=False)
+    _check(prob, whole, _all_units(prob), "whole_path")
+    assert torch.equal(split[2], whole[2])  # rings: pure data movement
+    d = (split[0].float() - whole[0].float()).abs().max().item()
+    rms = whole[0].float().pow(2).mean().sqrt().item()
+    assert d <= 0.05 * rms, (d, rms)
 
 
 def _sampled(N, H, extra, seed):
