@@ -35,6 +35,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -64,7 +65,7 @@ def kernel_source_hash(name: str) -> str:
     """Hash of the sources a kernel is built from, to tell whether stored counters are stale."""
     files = {"decode": ["kda_decode.hip", "kda_device.h", "kda_internal.h"],
              "prefill": ["kda_prefill.hip", "kda_prefill_pc.hip", "kda_mfma.h", "kda_device.h",
-                         "kda_internal.h"]}[name]
+                         "kda_internal.h", "kda_api.cpp"]}[name]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "gated_delta_rule_05_amd", "csrc", f), "rb") as fh:
@@ -208,11 +209,13 @@ def bench_prefill(name: str, reps: int, warmup: int = 3):
     rg = torch.empty((N, 3 * w.heads * D, 3), dtype=torch.float32, device=dev)
     flush = torch.empty(768 << 20, dtype=torch.uint8, device=dev)  # larger than the 256 MB MALL
     stream = torch.cuda.current_stream()
+    ws_bytes = kda.prefill_workspace_bytes(layer, torch.bfloat16, prob["cu_seqlens"])
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
 
     def run():
         kda.prefill(layer, prob["q"], prob["k"], prob["v"], prob["z"], prob["beta"], prob["gate"],
                     cu_dev, prob["cu_seqlens"], state_in=prob["state_in"], ring_in=prob["ring_in"],
-                    out=out, state_out=st, ring_out=rg, stream=stream)
+                    out=out, state_out=st, ring_out=rg, workspace=ws, stream=stream)
 
     for _ in range(warmup):
         run()
@@ -234,7 +237,9 @@ def bench_prefill(name: str, reps: int, warmup: int = 3):
               + N * 3 * H * D * 3 * 4 * (2 if w.init_ring else 1))
     flops = PREFILL_FLOPS_PER_TOKEN_HEAD * T * H
     s = ms / 1e3
-    res = dict(workload=name, sequences=N, tokens=T, heads=H, ms=ms, ms_min=times[0], reps=reps,
+    res = dict(workload=name, sequences=N, tokens=T, heads=H,
+               path="segment-parallel" if ws_bytes else "whole-sequence", workspace_bytes=ws_bytes,
+               ms=ms, ms_min=times[0], reps=reps,
                tokens_per_s=T / s, hbm_gbs=nbytes / s / 1e9, hbm_frac=nbytes / s / 1e9 / HBM_PEAK_GBS,
                mfma_tflops=flops / s / 1e12, mfma_frac=flops / s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                roofline_frac=max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) / s,
@@ -384,45 +389,57 @@ def summarize_pmc(fetch_dir: str, write_dir: str):
     print(json.dumps(doc, indent=1))
 
 
-def summarize_prefill_pmc(fetch_dir: str, write_dir: str, mfma_dir: str):
-    """Reads three rocprofv3 --pmc runs of `bench.py --only-prefill --prefill-reps 1
-    --calibrate-copy` (FETCH_SIZE; WRITE_SIZE; SQ_INSTS_VALU_MFMA_MOPS_BF16 with
-    SQ_INSTS_VALU and SQ_INSTS_MFMA), identifies each workload's dispatches by grid size,
-    and writes profiles/prefill_pmc.json: measured HBM bytes (copy-calibrated) against the
-    algorithmic bytes, and the bf16 MFMA work the kernel issued (512 flops per MOPS unit)
-    against the algorithmic flops."""
+def summarize_prefill_pmc(root: str):
+    """Reads, for each prefill workload W, three rocprofv3 --pmc runs of
+    `bench.py --only-prefill --prefill-workloads W --prefill-reps 1 --prefill-warmup 0
+    --calibrate-copy` in ROOT/W_fetch (FETCH_SIZE), ROOT/W_write (WRITE_SIZE) and
+    ROOT/W_mfma (SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_INSTS_VALU, SQ_INSTS_MFMA).  Every
+    dispatch of this library's kernels in a run belongs to the one prefill call (all
+    passes of the segment-parallel path included); byte counters are scaled by the 1 GiB
+    copy calibration.  Writes profiles/prefill_pmc.json: measured HBM bytes against the
+    algorithmic bytes, and the bf16 MFMA work issued (512 flops per MOPS unit) against the
+    algorithmic flops."""
     import synthetic
 
-    fetch = _read_pmc(fetch_dir, "FETCH_SIZE")
-    write = _read_pmc(write_dir, "WRITE_SIZE")
-    mops = _read_pmc(mfma_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
-    valu = _read_pmc(mfma_dir, "SQ_INSTS_VALU")
-    mfma = _read_pmc(mfma_dir, "SQ_INSTS_MFMA")
-    f_scale, f_copy = _copy_scale(fetch)
-    w_scale, w_copy = _copy_scale(write)
     out = {}
+    scales = {}
     for name in PREFILL_WORKLOADS:
+        d = {k: os.path.join(root, f"{name}_{k}") for k in ("fetch", "write", "mfma")}
+        if not all(os.path.isdir(x) for x in d.values()):
+            continue
+        fetch = _read_pmc(d["fetch"], "FETCH_SIZE")
+        write = _read_pmc(d["write"], "WRITE_SIZE")
+        f_scale, f_copy = _copy_scale(fetch)
+        w_scale, w_copy = _copy_scale(write)
+        scales[name] = dict(fetch_scale=f_scale, write_scale=w_scale)
+
+        def mine(k):
+            return "kda::" in k and ("prefill" in k or "combine" in k)
+
+        def total(rows):
+            v = [x for k, _, x in rows if mine(k)]
+            return sum(v) if v else None
+
+        def kernels(rows):
+            return sorted({re.findall(r"(\w+)\(", k)[0] for k, _, _ in rows if mine(k)})
+
         w = synthetic.WORKLOADS[name]
         N, H, T = len(w.seqlens), w.heads, sum(w.seqlens)
-        grid = N * H * 1024
-
-        def mean(rows):
-            v = [x for k, g, x in rows if PREFILL_KERNEL in k and g == grid]
-            return sum(v) / len(v) if v else None
-
-        f, wr, m, va, mf = mean(fetch), mean(write), mean(mops), mean(valu), mean(mfma)
+        f, wr = total(fetch), total(write)
+        m = total(_read_pmc(d["mfma"], "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
+        va = total(_read_pmc(d["mfma"], "SQ_INSTS_VALU"))
+        mf = total(_read_pmc(d["mfma"], "SQ_INSTS_MFMA"))
         alg = (PREFILL_BYTES_PER_TOKEN_HEAD * T * H + N * H * D * D * 4 * (2 if w.init_state else 1)
                + N * 3 * H * D * 3 * 4 * (2 if w.init_ring else 1))
         traffic = (f * 1024 * f_scale + wr * 1024 * w_scale) if (f and wr and f_scale and w_scale) else None
-        out[name] = dict(hbm_bytes=traffic, algorithmic_bytes=alg,
+        out[name] = dict(kernels=kernels(fetch), hbm_bytes=traffic, algorithmic_bytes=alg,
                          traffic_over_algorithmic=(traffic / alg) if traffic else None,
                          mfma_flops_issued=(m * 512) if m else None,
                          algorithmic_flops=PREFILL_FLOPS_PER_TOKEN_HEAD * T * H,
                          valu_insts_per_token_head=(va / (T * H)) if va else None,
                          mfma_insts_per_token_head=(mf / (T * H)) if mf else None)
     doc = dict(kernel=PREFILL_KERNEL, source_hash=kernel_source_hash("prefill"),
-               copy_fetch_kib=f_copy, copy_write_kib=w_copy, fetch_scale=f_scale,
-               write_scale=w_scale, workloads=out)
+               calibration=scales, workloads=out)
     with open(os.path.join(ROOT, "profiles", "prefill_pmc.json"), "w") as fh:
         json.dump(doc, fh, indent=1)
     print(json.dumps(doc, indent=1))
@@ -445,14 +462,14 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
-    ap.add_argument("--summarize-prefill-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "MFMA_DIR"))
+    ap.add_argument("--summarize-prefill-pmc", metavar="ROOT_DIR")
     args = ap.parse_args()
 
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return 0
     if args.summarize_prefill_pmc:
-        summarize_prefill_pmc(*args.summarize_prefill_pmc)
+        summarize_prefill_pmc(args.summarize_prefill_pmc)
         return 0
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
