@@ -13,6 +13,8 @@ launch over the whole batch.  Printed as one JSON line with:
                 measurement matches the current kernel source, else null;
 * cpu_baseline -- the fp64 oracle timed on the host cores on a bounded sample of the
                 same workload;
+* prefill_scan_ab -- chunked prefill against the sequential-scan arm (kda_prefill_scan)
+                on 256 prompts x 64 tokens x 32 heads;
 * verify     -- the batched verify of speculative decoding on the same shape: 4 rows per
                 sequence in one kda_decode_multi launch (tokens/s over all rows, HBM
                 fraction at its algorithmic bytes);
@@ -251,6 +253,45 @@ def bench_prefill(name: str, reps: int, warmup: int = 3):
     if w.decode_after:
         res["decode_continuation"] = bench_decode_after(w, layer, st, rg, stream)
     del prob, out, flush
+    return res
+
+
+def bench_scan_ab(name: str = "short256x64_h32", reps: int = 20):
+    """The chunked prefill against the sequential-scan arm on a batch of short prompts:
+    median of `reps` calls each, MALL flushed before each."""
+    import torch
+
+    import gated_delta_rule_05_amd as kda
+    import synthetic
+
+    w = synthetic.WORKLOADS[name]
+    prob = synthetic.make_workload(name, device="cuda:0")
+    layer = kda.Layer(**prob["layer"])
+    cu_dev = prob["cu_seqlens"].to("cuda:0")
+    flush = torch.empty(768 << 20, dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    res = dict(workload=name, sequences=len(w.seqlens), tokens_per_sequence=w.seqlens[0], heads=w.heads)
+    for arm in ("chunked", "scan"):
+        def run():
+            kda.prefill(layer, prob["q"], prob["k"], prob["v"], prob["z"], prob["beta"], prob["gate"],
+                        cu_dev, prob["cu_seqlens"], state_in=prob["state_in"], ring_in=prob["ring_in"],
+                        scan=arm == "scan", stream=stream)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            flush.fill_(1)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        ms = times[len(times) // 2]
+        res[arm] = dict(ms=ms, tokens_per_s=sum(w.seqlens) / (ms / 1e3))
     return res
 
 
@@ -528,6 +569,7 @@ def main():
     line["verify"] = bench_verify(dec)
     if not args.no_prefill:
         line["prefill"] = prefill_list()
+        line["prefill_scan_ab"] = bench_scan_ab()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(dec)
     print(json.dumps(line), flush=True)

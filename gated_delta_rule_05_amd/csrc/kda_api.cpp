@@ -67,6 +67,30 @@ kda::LayerParams layer_params(const kda_layer* L) {
 
 bool io_ok(kda_dtype io) { return io == KDA_F32 || io == KDA_BF16; }
 
+// Packed varlen inputs of the prefill entry points (num_seqs > 0).
+kda_status check_packed(int32_t num_seqs, const int32_t* cu_dev, const int32_t* cu_host,
+                        int64_t total_tokens, const void* q, const void* k, const void* v,
+                        const void* z, const void* beta, const void* gate, const void* out,
+                        const float* state_in, const float* state_out) {
+  if (!cu_dev || !cu_host)
+    return fail(KDA_ERR_INVALID_ARG, "cu_seqlens (device and host copies) are required");
+  if (cu_host[0] != 0) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
+  for (int32_t n = 0; n < num_seqs; ++n)
+    if (cu_host[n + 1] < cu_host[n])
+      return fail(KDA_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing (at %d)", n);
+  if (static_cast<int64_t>(cu_host[num_seqs]) != total_tokens)
+    return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[num_seqs] = %d != total_tokens = %lld",
+                cu_host[num_seqs], static_cast<long long>(total_tokens));
+  if (total_tokens > 0 && (!q || !k || !v || !z || !beta || !gate || !out))
+    return fail(KDA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out)))
+    return fail(KDA_ERR_INVALID_ARG, "state buffers must be 16-byte aligned");
+  if (total_tokens > 0 &&
+      (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(gate)))
+    return fail(KDA_ERR_INVALID_ARG, "q, k, v, z and gate must be 16-byte aligned");
+  return KDA_OK;
+}
+
 // Splitting sequences into segments pays when there are too few (sequence, head) units to
 // fill the chip's 256 compute units: each sequence is cut into about 256 / units segments
 // of at least 256 tokens (a multiple of the 16-token chunk), and the three passes then run
@@ -166,6 +190,7 @@ kda_status kda_decode_multi(const kda_layer* layer, kda_dtype io, int32_t batch,
   a.batch = batch;
   a.tokens = tokens;
   a.ntok = ntok_dev;
+  a.cu = nullptr;
   a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.gate = gate;
   a.state_in = state_in;
   a.ring_in = ring_in;
@@ -200,22 +225,9 @@ kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
     if (total_tokens != 0) return fail(KDA_ERR_INVALID_ARG, "no sequences but total_tokens != 0");
     return ok();
   }
-  if (!cu_seqlens_dev || !cu_seqlens_host)
-    return fail(KDA_ERR_INVALID_ARG, "cu_seqlens (device and host copies) are required");
-  if (cu_seqlens_host[0] != 0) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
-  for (int32_t n = 0; n < num_seqs; ++n)
-    if (cu_seqlens_host[n + 1] < cu_seqlens_host[n])
-      return fail(KDA_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing (at %d)", n);
-  if (static_cast<int64_t>(cu_seqlens_host[num_seqs]) != total_tokens)
-    return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[num_seqs] = %d != total_tokens = %lld",
-                cu_seqlens_host[num_seqs], static_cast<long long>(total_tokens));
-  if (total_tokens > 0 && (!q || !k || !v || !z || !beta || !gate || !out))
-    return fail(KDA_ERR_INVALID_ARG, "a tensor pointer is NULL");
-  if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out)))
-    return fail(KDA_ERR_INVALID_ARG, "state buffers must be 16-byte aligned");
-  if (total_tokens > 0 &&
-      (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(gate)))
-    return fail(KDA_ERR_INVALID_ARG, "q, k, v, z and gate must be 16-byte aligned");
+  st = check_packed(num_seqs, cu_seqlens_dev, cu_seqlens_host, total_tokens, q, k, v, z, beta,
+                    gate, out, state_in, state_out);
+  if (st != KDA_OK) return st;
   if (workspace_bytes > 0 && !workspace)
     return fail(KDA_ERR_WORKSPACE, "workspace is NULL but workspace_bytes = %zu", workspace_bytes);
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
@@ -259,6 +271,42 @@ kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
     e = kda::launch_prefill(a, io, order.data(), stream);
   }
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kda_status kda_prefill_scan(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
+                            const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                            int64_t total_tokens, const void* q, const void* k, const void* v,
+                            const void* z, const void* beta, const void* gate,
+                            const float* state_in, const float* ring_in, void* out,
+                            float* state_out, float* ring_out, hipStream_t stream) {
+  kda_status st = check_layer(layer, false);
+  if (st != KDA_OK) return st;
+  if (!io_ok(io)) return fail(KDA_ERR_INVALID_ARG, "unknown io dtype %d", static_cast<int>(io));
+  if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (num_seqs == 0) {
+    if (total_tokens != 0) return fail(KDA_ERR_INVALID_ARG, "no sequences but total_tokens != 0");
+    return ok();
+  }
+  st = check_packed(num_seqs, cu_seqlens_dev, cu_seqlens_host, total_tokens, q, k, v, z, beta,
+                    gate, out, state_in, state_out);
+  if (st != KDA_OK) return st;
+  if (static_cast<int64_t>(num_seqs) * layer->num_heads > 0x7fffffffLL)
+    return fail(KDA_ERR_INVALID_ARG, "num_seqs * num_heads exceeds the grid limit");
+  kda::DecodeArgs a;
+  a.L = layer_params(layer);
+  a.batch = num_seqs;
+  a.tokens = 0;
+  a.ntok = nullptr;
+  a.cu = cu_seqlens_dev;
+  a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.gate = gate;
+  a.state_in = state_in;
+  a.ring_in = ring_in;
+  a.state_out = state_out;
+  a.ring_out = ring_out;
+  a.out = out;
+  hipError_t e = kda::launch_decode(a, io, stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill scan launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -38,7 +38,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int cg = t & 31;
   const int rg = t >> 5;
   const int64_t Hd = static_cast<int64_t>(H) * kHeadDim;
-  const int n = a.ntok ? min(max(a.ntok[b], 0), a.tokens) : a.tokens;
+  // rows of this sequence: [row0, row0 + n)
+  int64_t row0;
+  int n;
+  if (a.cu) {
+    row0 = a.cu[b];
+    n = a.cu[b + 1] - a.cu[b];
+  } else {
+    row0 = static_cast<int64_t>(b) * a.tokens;
+    n = a.ntok ? min(max(a.ntok[b], 0), a.tokens) : a.tokens;
+  }
 
   __shared__ float a_q[kHeadDim], a_k[kHeadDim], a_v[kHeadDim], eg[kHeadDim], sg[kHeadDim];
   __shared__ float dlt[kHeadDim];
@@ -66,7 +75,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const IO* pb = t < kHeadDim ? x_k : x_z;
   IO xa{}, xb{}, xc{}, xbeta{};
   auto fetch = [&](int tok) __attribute__((always_inline)) {
-    const int64_t row = static_cast<int64_t>(b) * a.tokens + tok;
+    const int64_t row = row0 + tok;
     xa = pa[row * Hd + c];
     xb = pb[row * Hd + c];
     xc = x_g[row * Hd + c];
@@ -75,22 +84,27 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // state rows rg + 8 m of this (sequence, head): byte offset 16 (32 rg + cg) + 4096 m
   const int64_t soff = static_cast<int64_t>(unit) * kHeadDim * kHeadDim;
   constexpr int kStateBytes = kHeadDim * kHeadDim * 4;
-  const __amdgpu_buffer_rsrc_t Sin = buffer_rsrc(a.state_in + soff, kStateBytes);
-  const __amdgpu_buffer_rsrc_t Sout = buffer_rsrc(a.state_out + soff, kStateBytes);
+  const __amdgpu_buffer_rsrc_t Sin = buffer_rsrc(a.state_in ? a.state_in + soff : nullptr, kStateBytes);
+  const __amdgpu_buffer_rsrc_t Sout = buffer_rsrc(a.state_out ? a.state_out + soff : nullptr, kStateBytes);
   const int svoff = 16 * (32 * rg + cg);
   float4 s[16];
+  if (a.state_in) {
 #pragma unroll
-  for (int m = 0; m < 16; ++m) s[m] = buffer_load16(Sin, svoff, 4096 * m);
+    for (int m = 0; m < 16; ++m) s[m] = buffer_load16(Sin, svoff, 4096 * m);
+  } else {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) s[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 
   if (n > 0) fetch(0);
 
   const int64_t roff = static_cast<int64_t>(b) * 3 * Hd * kRingTaps;
   const int p0 = t < kHeadDim ? 0 : 2;  // first plane this thread holds
-  float hist[2][3];
+  float hist[2][3] = {{0.f, 0.f, 0.f}, {0.f, 0.f, 0.f}};
 #pragma unroll
   for (int pp = 0; pp < 2; ++pp) {
     const int p = p0 + pp;
-    if (p < 3) {
+    if (p < 3 && a.ring_in) {
 #pragma unroll
       for (int j = 0; j < 3; ++j) hist[pp][j] = a.ring_in[roff + (p * Hd + c) * kRingTaps + j];
     }
@@ -101,7 +115,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
 #pragma clang loop unroll(disable)
   for (int tok = 0; tok < n; ++tok) {
-    const int64_t xrow = (static_cast<int64_t>(b) * a.tokens + tok) * Hd;
+    const int64_t xrow = (row0 + tok) * Hd;
     const float beta = sigmoidf_(io_to_f32(xbeta));
 
     // 2. prologue: conv + SiLU with the history, history roll, gate, beta
@@ -207,7 +221,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       s[m].z += kh[m] * d4.z;
       s[m].w += kh[m] * d4.w;
     }
-    if (tok + 1 == n) {
+    if (tok + 1 == n && a.state_out) {
 #pragma unroll
       for (int m = 0; m < 16; ++m) buffer_store16_nt(Sout, svoff, 4096 * m, s[m]);
     }
@@ -221,14 +235,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 
   // 6. no token: the state passes through; then the conv history
-  if (n == 0) {
+  if (n == 0 && a.state_out) {
 #pragma unroll
     for (int m = 0; m < 16; ++m) buffer_store16_nt(Sout, svoff, 4096 * m, s[m]);
   }
 #pragma unroll
   for (int pp = 0; pp < 2; ++pp) {
     const int p = p0 + pp;
-    if (p < 3) {
+    if (p < 3 && a.ring_out) {
 #pragma unroll
       for (int j = 0; j < 3; ++j) a.ring_out[roff + (p * Hd + c) * kRingTaps + j] = hist[pp][j];
     }

@@ -21,12 +21,16 @@ struct LayerParams {
 
 // Decode of up to `tokens` consecutive tokens per sequence (one token: the decode step).
 // Activations are [batch][tokens][...]; ntok (device, or null for all) gives each
-// sequence's count.  state_out / ring_out may equal state_in / ring_in; out may be null.
+// sequence's count.  With cu (device, [batch + 1]) the rows are packed instead: sequence b
+// has rows cu[b] .. cu[b + 1] - 1 (the sequential-scan prefill).  state_out / ring_out may
+// equal state_in / ring_in; a null state_in / ring_in starts from zeros, a null state_out /
+// ring_out / out is not written.
 struct DecodeArgs {
   LayerParams L;
   int32_t batch;
   int32_t tokens;
   const int32_t* ntok;
+  const int32_t* cu;
   const void *q, *k, *v, *z, *beta, *gate;
   const float* state_in;
   const float* ring_in;

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
   KDA_OK = 0,
@@ -120,6 +120,23 @@ kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
                        const void* z, const void* beta, const void* gate, const float* state_in,
                        const float* ring_in, void* out, float* state_out, float* ring_out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Sequential-scan prefill: the same packed problem and buffers as kda_prefill (no
+ * workspace), run token by token by the decode kernel over register-resident state
+ * (memra_engine::kda's prefill arrangement, memra_kda_scan_s128, which serves prefill and
+ * decode alike).  An A/B comparator for the chunked path, and the faster arm for short
+ * prompts.  Each sequence's outputs, final state and ring are bit-identical to running its
+ * tokens through kda_decode_step one at a time.  Any lower_bound <= 0 is accepted (there
+ * is no tile bound).  state_in / ring_in may be NULL (zeros), state_out / ring_out NULL
+ * (not written); state_out may equal state_in and ring_out ring_in.
+ */
+kda_status kda_prefill_scan(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
+                            const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                            int64_t total_tokens, const void* q, const void* k, const void* v,
+                            const void* z, const void* beta, const void* gate,
+                            const float* state_in, const float* ring_in, void* out,
+                            float* state_out, float* ring_out, hipStream_t stream);
 
 /*
  * One decode token for each of `batch` sequences (memra_engine::kda kda_attn_decode: the

@@ -11,7 +11,10 @@ Workloads (all head_dim 128, short-conv kernel 4, lower bound -5):
 * ``prefill_t4096_h32``   -- 1 sequence x 4096 tokens, 32 heads, bf16 io;
 * ``prefill_2x8192_h96``  -- 2 sequences x 8192 tokens, 96 heads, bf16 io, final states;
 * ``varlen16_h64``        -- 16 sequences with lengths ~ U[512, 16384], 64 heads, bf16 io,
-  initial state ~ N(0, 0.02) and ring ~ N(0, 1), then 32 decode steps.
+  initial state ~ N(0, 0.02) and ring ~ N(0, 1), then 32 decode steps;
+* ``short256x64_h32``     -- 256 prompts x 64 tokens, 32 heads, bf16 io, carried state and
+  ring: the short-prompt case on which the chunked and the sequential-scan prefill are
+  compared.
 
 Distributions: raw q/k/v, decay pre-activation z and output-gate pre-activation ~ N(0, 1);
 raw beta ~ N(0, 1); conv weights ~ U(-0.5, 0.5); dt_bias ~ N(0, 0.1); A_log = log U(1, 16)
@@ -65,6 +68,10 @@ WORKLOADS = {
                                    seed=20263),
     "varlen16_h64": Workload("varlen16_h64", "prefill", "bf16", 64, _varlen_lengths(20264 + 7),
                              init_state=True, init_ring=True, decode_after=32, seed=20264),
+    # a batch of short prompts for the chunked-versus-scan comparison (not one of the
+    # reference's configurations)
+    "short256x64_h32": Workload("short256x64_h32", "prefill", "bf16", 32, [64] * 256,
+                                init_state=True, init_ring=True, seed=20265),
 }
 
 

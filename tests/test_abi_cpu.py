@@ -26,9 +26,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    assert names == sorted(["kda_prefill_workspace_bytes", "kda_prefill", "kda_decode_step",
-                            "kda_decode_multi", "kda_status_string", "kda_last_error",
-                            "kda_abi_version"])
+    assert names == sorted(["kda_prefill_workspace_bytes", "kda_prefill", "kda_prefill_scan",
+                            "kda_decode_step", "kda_decode_multi", "kda_status_string",
+                            "kda_last_error", "kda_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -125,3 +125,22 @@ def test_workspace_query_is_host_only():
     cu = np.array([0, 100, 300], dtype=np.int32)
     n = lib.kda_prefill_workspace_bytes(ctypes.byref(_layer(kda)), 1, 2, cu.ctypes.data, 300)
     assert n >= 0
+
+
+def test_prefill_scan_validation():
+    """The scan arm checks its packed inputs like kda_prefill, before any launch."""
+    kda, lib = _lib()
+    lay = _layer(kda)
+
+    def scan(cu, total, q=FAKE, lb_layer=None):
+        cu = np.ascontiguousarray(cu, dtype=np.int32)
+        return lib.kda_prefill_scan(ctypes.byref(lb_layer or lay), 1, len(cu) - 1, FAKE,
+                                    cu.ctypes.data, total, q, *([FAKE] * 5), None, None, FAKE,
+                                    None, None, None)
+
+    assert scan([0, 5, 3], 3) == 1             # decreasing
+    assert scan([1, 5], 4) == 1                # cu[0] != 0
+    assert scan([0, 5], 6) == 1                # total mismatch
+    assert scan([0, 5], 5, q=0) == 1           # null activation
+    assert scan([0, 5], 5, q=FAKE + 2) == 1    # misaligned activation
+    assert lib.kda_prefill_scan(ctypes.byref(lay), 1, 0, None, None, 0, *([None] * 11), None) == 0
