@@ -60,6 +60,8 @@ def _load():
             lib.kdao_silu.argtypes = [ctypes.c_double]
             lib.kdao_gate.restype = ctypes.c_double
             lib.kdao_gate.argtypes = [ctypes.c_double] * 4
+            lib.kdao_gate_softplus.restype = ctypes.c_double
+            lib.kdao_gate_softplus.argtypes = [ctypes.c_double] * 3
             lib.kdao_l2norm.restype = None
             lib.kdao_l2norm.argtypes = [vp, ctypes.c_int, ctypes.c_double, ctypes.c_double]
             lib.kdao_gated_rmsnorm.restype = None
@@ -70,7 +72,7 @@ def _load():
             lib.kdao_core_chunked.argtypes = [ctypes.c_int] * 5 + [vp] * 7
             lib.kdao_prefill_units.restype = ctypes.c_int
             lib.kdao_prefill_units.argtypes = (
-                [ctypes.c_int32] * 3 + [ctypes.c_double] * 3 + [vp] * 4 + [ctypes.c_int]
+                [ctypes.c_int32] * 4 + [ctypes.c_double] * 3 + [vp] * 4 + [ctypes.c_int]
                 + [vp] * 7 + [vp, vp] + [ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_int]
                 + [vp] * 7)
             del dp
@@ -137,6 +139,15 @@ def gate(z: float, dt_bias: float, A_log: float, lower_bound: float = -5.0) -> f
     return _load().kdao_gate(float(z), float(dt_bias), float(A_log), float(lower_bound))
 
 
+def gate_softplus(z: float, dt_bias: float, A_log: float) -> float:
+    """g = -exp(A_log) * softplus(z + dt_bias): Kimi-Linear's unbounded gate (the analysis
+    page's status note on the decay-gate formula)."""
+    return _load().kdao_gate_softplus(float(z), float(dt_bias), float(A_log))
+
+
+GATE_BOUNDED, GATE_SOFTPLUS = 0, 1
+
+
 def l2norm(x, eps: float = 1e-6, scale: float = 1.0) -> np.ndarray:
     y = _f64(x).copy()
     _load().kdao_l2norm(_ptr(y), y.shape[-1], eps, scale)
@@ -188,8 +199,9 @@ class Layer:
     """Per-layer parameters (fp32): conv_w [3*H*d, kconv], dt_bias [H*d], A_log [H], norm_w [d]."""
 
     def __init__(self, num_heads, head_dim, conv_w, dt_bias, A_log, norm_w, conv_kernel=4,
-                 lower_bound=-5.0, l2_eps=1e-6, rms_eps=1e-5):
+                 lower_bound=-5.0, l2_eps=1e-6, rms_eps=1e-5, gate_kind=GATE_BOUNDED):
         self.H = int(num_heads)
+        self.gate_kind = int(gate_kind)
         self.d = int(head_dim)
         self.kconv = int(conv_kernel)
         self.lower_bound = float(lower_bound)
@@ -243,7 +255,7 @@ def prefill_units(layer: Layer, io: int, cu_seqlens, q, k, v, z, beta, gate_pre,
     if nthreads is None:
         nthreads = os.cpu_count() or 1
     rc = lib.kdao_prefill_units(
-        H, d, layer.kconv, layer.lower_bound, layer.l2_eps, layer.rms_eps,
+        H, d, layer.kconv, layer.gate_kind, layer.lower_bound, layer.l2_eps, layer.rms_eps,
         _ptr(layer.conv_w), _ptr(layer.dt_bias), _ptr(layer.A_log), _ptr(layer.norm_w),
         io, _ptr(cu), *[_ptr(a) for a in arrs], _ptr(s_in), _ptr(r_in),
         len(units), _ptr(units), _ptr(offs), _ptr(out), _ptr(st), _ptr(rg), int(nthreads),

@@ -67,6 +67,18 @@ double kdao_gate(double z, double dt_bias, double A_log, double lower_bound) {
   return lower_bound * kdao_sigmoid(exp(A_log) * (z + dt_bias));
 }
 
+/* softplus(x) = log(1 + e^x), written to avoid overflow for large x */
+double kdao_softplus(double x) { return x > 30.0 ? x + log1p(exp(-x)) : log1p(exp(x)); }
+
+/*
+ * Kimi-Linear's unbounded per-channel log decay ([p2] status note: -e^{A_log} softplus(z),
+ * the gate used when a model sets no lower bound; z carries dt_bias as in the bounded
+ * gate): g = -exp(A_log[h]) * softplus(z + dt_bias[c]).
+ */
+double kdao_gate_softplus(double z, double dt_bias, double A_log) {
+  return -exp(A_log) * kdao_softplus(z + dt_bias);
+}
+
 /* x <- x * (sum_i x_i^2 + eps)^-1/2 * scale, over one head row of length d ([p1]). */
 void kdao_l2norm(double* x, int d, double eps, double scale) {
   double ss = 0.0;
@@ -237,6 +249,7 @@ void kdao_core_chunked(int T, int dk, int dv, int C, int tau, const double* qh, 
 
 typedef struct {
   int32_t num_heads, head_dim, conv_kernel;
+  int32_t gate_kind; /* 0: lower-bounded sigmoid gate, 1: softplus gate */
   double lower_bound, l2_eps, rms_eps;
   const float* conv_w;  /* [3*H*d][conv_kernel], planes q,k,v ([p3] conv fusion) */
   const float* dt_bias; /* [H*d] */
@@ -319,8 +332,10 @@ static void run_unit(kdao_job* J, int u) {
     kdao_l2norm(a[1], d, L->l2_eps, 1.0);   /* k-hat */
     for (int i = 0; i < d; ++i) {
       const int64_t c = (int64_t)h * d + i;
-      gv[i] = kdao_gate(load_io(J->z, J->io_dtype, row * Hd + c), (double)L->dt_bias[c],
-                        (double)L->A_log[h], L->lower_bound);
+      const double zz = load_io(J->z, J->io_dtype, row * Hd + c);
+      gv[i] = L->gate_kind == 1
+                  ? kdao_gate_softplus(zz, (double)L->dt_bias[c], (double)L->A_log[h])
+                  : kdao_gate(zz, (double)L->dt_bias[c], (double)L->A_log[h], L->lower_bound);
       gt[i] = load_io(J->gate, J->io_dtype, row * Hd + c);
     }
     double beta = kdao_sigmoid(load_io(J->beta, J->io_dtype, row * H + h));
@@ -363,7 +378,8 @@ static void* worker(void* arg) {
  * If trace pointers are non-null, exactly one unit must be listed.
  */
 int kdao_prefill_units(int32_t num_heads, int32_t head_dim, int32_t conv_kernel,
-                       double lower_bound, double l2_eps, double rms_eps, const float* conv_w,
+                       int32_t gate_kind, double lower_bound, double l2_eps, double rms_eps,
+                       const float* conv_w,
                        const float* dt_bias, const float* A_log, const float* norm_w,
                        int io_dtype, const int64_t* cu_seqlens, const void* q, const void* k,
                        const void* v, const void* z, const void* beta, const void* gate,
@@ -373,8 +389,9 @@ int kdao_prefill_units(int32_t num_heads, int32_t head_dim, int32_t conv_kernel,
                        double* tr_k, double* tr_v, double* tr_g, double* tr_beta,
                        double* tr_o_raw, double* tr_S) {
   if (head_dim <= 0 || num_heads <= 0 || conv_kernel < 1) return -1;
+  if (gate_kind != 0 && gate_kind != 1) return -1;
   if (n_units < 0 || (tr_q && n_units != 1)) return -1;
-  kdao_layer L = {num_heads, head_dim, conv_kernel, lower_bound, l2_eps, rms_eps,
+  kdao_layer L = {num_heads, head_dim, conv_kernel, gate_kind, lower_bound, l2_eps, rms_eps,
                   conv_w, dt_bias, A_log, norm_w};
   kdao_job J;
   memset(&J, 0, sizeof J);

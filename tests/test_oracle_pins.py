@@ -75,6 +75,20 @@ def test_gate_range_stays_inside_the_bound():
     assert 16 * 5 == 80
 
 
+def test_softplus_gate_against_library_routines():
+    """Kimi-Linear's unbounded gate, -exp(A_log) softplus(z + dt_bias): softplus is
+    numpy's logaddexp(0, x) and torch's softplus; z + dt = 0 gives -exp(A_log) ln 2; large
+    arguments grow linearly and very negative ones vanish, without overflow."""
+    for A in (0.0, math.log(3.0), math.log(16.0)):
+        assert oracle.gate_softplus(-0.25, 0.25, A) == pytest.approx(-math.exp(A) * math.log(2.0), rel=1e-15)
+        for x in (-60.0, -5.0, -0.3, 0.0, 0.7, 4.0, 29.0, 31.0, 200.0):
+            ref_np = -math.exp(A) * float(np.logaddexp(0.0, x))
+            ref_t = -math.exp(A) * float(F.softplus(torch.tensor(x, dtype=torch.float64), threshold=1e9))
+            got = oracle.gate_softplus(x - 0.5, 0.5, A)
+            assert got == pytest.approx(ref_np, rel=1e-14, abs=1e-300)
+            assert got == pytest.approx(ref_t, rel=1e-14, abs=1e-300)
+
+
 def test_l2norm_closed_form_and_library():
     x = np.zeros(128)
     x[0], x[1] = 3.0, 4.0
@@ -351,6 +365,24 @@ def test_beta_zero_full_path_decays_the_initial_state():
     out, S, _ = oracle.prefill(L, oracle.F32, [0, T], a["q"], a["k"], a["v"], a["z"], a["beta"],
                                a["gate"], state_in=S0)
     assert rel(S, S0 * math.exp(-2.5 * T)) < 1e-13
+
+
+def test_beta_zero_full_path_decays_with_the_softplus_gate():
+    """The gate kind reaches the full path: with beta = 0 the final state is the initial
+    one decayed per key channel by exp(sum_t g_t), g_t = -exp(A_log) logaddexp(0, z + dt)
+    computed here with numpy (the bounded gate would give a different decay)."""
+    H, d, T = 2, 8, 5
+    L = _layer(H, d, 22)
+    L.gate_kind = oracle.GATE_SOFTPLUS
+    a = _acts(T, H, d, 23)
+    a["beta"][:] = -1e4
+    S0 = np.random.default_rng(24).normal(0, 0.02, (1, H, d, d))
+    out, S, _ = oracle.prefill(L, oracle.F32, [0, T], a["q"], a["k"], a["v"], a["z"], a["beta"],
+                               a["gate"], state_in=S0)
+    x = a["z"].astype(np.float64) + L.dt_bias.astype(np.float64)[None, :]       # [T, H*d]
+    g = -np.exp(np.repeat(L.A_log.astype(np.float64), d))[None, :] * np.logaddexp(0.0, x)
+    decay = np.exp(g.sum(axis=0)).reshape(H, d)                                   # per (h, key)
+    assert rel(S[0], S0[0] * decay[:, :, None]) < 1e-12
 
 
 def _split(a, lo, hi):
