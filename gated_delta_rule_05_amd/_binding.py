@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 HEAD_DIM = 128
 CONV_KERNEL = 4
 
@@ -38,7 +38,10 @@ class KdaLayerC(ctypes.Structure):
                 ("conv_kernel", ctypes.c_int32), ("lower_bound", ctypes.c_float),
                 ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("conv_w", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
-                ("A_log", ctypes.c_void_p), ("norm_w", ctypes.c_void_p)]
+                ("A_log", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
+                ("gate_kind", ctypes.c_int32)]
+
+GATE_BOUNDED, GATE_SOFTPLUS = 0, 1
 
 
 _lib = None
@@ -118,10 +121,12 @@ def _need(t, name, shape, dtype, device):
 
 class Layer:
     """One layer's parameters on the GPU: conv_w [3*H*128, 4], dt_bias [H*128], A_log [H],
-    norm_w [128], all fp32; the gate's lower bound and the two epsilons."""
+    norm_w [128], all fp32; the gate's lower bound, the two epsilons, and the gate formula
+    (GATE_BOUNDED, or GATE_SOFTPLUS for the unbounded softplus gate)."""
 
     def __init__(self, num_heads, conv_w, dt_bias, A_log, norm_w, lower_bound=-5.0,
-                 l2_eps=1e-6, rms_eps=1e-5, head_dim=HEAD_DIM, conv_kernel=CONV_KERNEL, **_):
+                 l2_eps=1e-6, rms_eps=1e-5, head_dim=HEAD_DIM, conv_kernel=CONV_KERNEL,
+                 gate_kind=GATE_BOUNDED, **_):
         self.H = int(num_heads)
         dev = conv_w.device
         Hd = self.H * HEAD_DIM
@@ -133,7 +138,7 @@ class Layer:
         self.tensors = (conv_w, dt_bias, A_log, norm_w)  # keep alive
         self.c = KdaLayerC(self.H, int(head_dim), int(conv_kernel), float(lower_bound),
                            float(l2_eps), float(rms_eps), conv_w.data_ptr(), dt_bias.data_ptr(),
-                           A_log.data_ptr(), norm_w.data_ptr())
+                           A_log.data_ptr(), norm_w.data_ptr(), int(gate_kind))
 
 
 def prefill_workspace_bytes(layer: Layer, io_dtype: torch.dtype, cu_seqlens_host) -> int:

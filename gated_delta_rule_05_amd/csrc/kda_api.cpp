@@ -43,6 +43,9 @@ kda_status check_layer(const kda_layer* L, bool chunked) {
   if (!(L->l2_eps >= 0.f) || !(L->rms_eps >= 0.f) || !std::isfinite(L->l2_eps) ||
       !std::isfinite(L->rms_eps))
     return fail(KDA_ERR_INVALID_ARG, "epsilons must be finite and non-negative");
+  if (L->gate_kind != KDA_GATE_BOUNDED && L->gate_kind != KDA_GATE_SOFTPLUS)
+    return fail(KDA_ERR_INVALID_ARG, "unknown gate_kind %d", L->gate_kind);
+  if (L->gate_kind == KDA_GATE_SOFTPLUS) return KDA_OK;  // lower_bound unused
   if (!std::isfinite(L->lower_bound) || L->lower_bound > 0.f)
     return fail(KDA_ERR_INVALID_ARG, "lower_bound must be finite and <= 0");
   // The chunked kernel forms exp(+-Gcum) over 16-token tiles from a mid-tile reference:
@@ -55,6 +58,7 @@ kda_status check_layer(const kda_layer* L, bool chunked) {
 kda::LayerParams layer_params(const kda_layer* L) {
   kda::LayerParams p;
   p.H = L->num_heads;
+  p.gate_kind = L->gate_kind;
   p.lower_bound = L->lower_bound;
   p.l2_eps = L->l2_eps;
   p.rms_eps = L->rms_eps;
@@ -253,6 +257,10 @@ kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
   a.out = out;
   a.state_out = state_out;
   a.ring_out = ring_out;
+  if (layer->gate_kind == KDA_GATE_SOFTPLUS)  // unbounded gate: no tile bound, run the scan
+    return kda_prefill_scan(layer, io, num_seqs, cu_seqlens_dev, cu_seqlens_host, total_tokens,
+                            q, k, v, z, beta, gate, state_in, ring_in, out, state_out, ring_out,
+                            stream);
   a.pass = kda::kPassWhole;
   a.seg_b = a.seg_m = a.seg_start = nullptr;
 

@@ -151,7 +151,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       hist[0][1] = hist[0][2];
       hist[0][2] = x;
       a_v[i] = siluf_(y);
-      const float g = kda_gate(io_to_f32(xb), dtb, ascale, a.L.lower_bound);
+      const float g = a.L.gate_kind == KDA_GATE_SOFTPLUS
+                          ? kda_gate_softplus(io_to_f32(xb), dtb, ascale)
+                          : kda_gate(io_to_f32(xb), dtb, ascale, a.L.lower_bound);
       eg[i] = expf(g);
       sg[i] = sigmoidf_(io_to_f32(xc));
     }

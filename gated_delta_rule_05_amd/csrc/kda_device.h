@@ -88,6 +88,13 @@ __device__ __forceinline__ float kda_gate(float z, float dt_bias, float a_scale,
   return lb * sigmoidf_(a_scale * (z + dt_bias));
 }
 
+// The unbounded gate: g = -exp(A_log) * softplus(z + dt_bias), a_scale = exp(A_log);
+// softplus(x) = log(1 + e^x), linear in x above 20 (where e^-x is below fp32's epsilon).
+__device__ __forceinline__ float kda_gate_softplus(float z, float dt_bias, float a_scale) {
+  const float x = z + dt_bias;
+  return -a_scale * (x > 20.f ? x + log1pf(expf(-x)) : log1pf(expf(x)));
+}
+
 // Sum over the 64 lanes of a wave; every lane receives the total.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -12,6 +12,7 @@ constexpr int kHeadDimHost = 128;
 
 struct LayerParams {
   int32_t H;
+  int32_t gate_kind;  // KDA_GATE_BOUNDED or KDA_GATE_SOFTPLUS
   float lower_bound, l2_eps, rms_eps;
   const float* conv_w;
   const float* dt_bias;

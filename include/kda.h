@@ -50,17 +50,28 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
   KDA_OK = 0,
   KDA_ERR_INVALID_ARG = 1, /* null or misaligned pointer, bad size, inconsistent cu_seqlens */
-  KDA_ERR_UNSUPPORTED = 2, /* head_dim != 128, conv kernel != 4, lower bound outside [-5, 0] */
+  KDA_ERR_UNSUPPORTED = 2, /* head_dim != 128, conv kernel != 4, chunked lower bound below -5 */
   KDA_ERR_WORKSPACE = 3,   /* workspace NULL with a nonzero size, or not 256-byte aligned */
   KDA_ERR_HIP = 4          /* the HIP runtime refused a launch */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Decay-gate formula. */
+typedef enum {
+  /* g = lower_bound * sigmoid(exp(A_log) * (z + dt_bias)) (OpenModelAtlas "Kimi K3 -
+     Retention gate", gate.py; Kimi K3) */
+  KDA_GATE_BOUNDED = 0,
+  /* g = -exp(A_log) * softplus(z + dt_bias), unbounded (Kimi-Linear, per the analysis
+     page's status note); lower_bound is ignored.  The chunked prefill's tile factors need
+     the bound, so kda_prefill runs the sequential scan for this gate. */
+  KDA_GATE_SOFTPLUS = 1
+} kda_gate_kind;
 
 /*
  * One layer's shape and parameters (device pointers, fp32):
@@ -69,7 +80,8 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *   A_log   [H]                        per-head log scale of the gate
  *   norm_w  [d]                        gated-RMSNorm weight, shared by all heads
  * lower_bound is the gate's lower bound (-5 in the pages' models); l2_eps the q/k L2
- * epsilon (1e-6); rms_eps the output RMSNorm epsilon.
+ * epsilon (1e-6); rms_eps the output RMSNorm epsilon; gate_kind selects the decay-gate
+ * formula (kda_gate_kind).
  */
 typedef struct kda_layer {
   int32_t num_heads;
@@ -82,6 +94,7 @@ typedef struct kda_layer {
   const float* dt_bias;
   const float* A_log;
   const float* norm_w;
+  int32_t gate_kind;   /* kda_gate_kind */
 } kda_layer;
 
 /*

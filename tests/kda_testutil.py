@@ -28,7 +28,7 @@ def head_layer(params: dict, h: int) -> oracle.Layer:
                         A_log=_cpu(params["A_log"]).numpy()[h:h + 1],
                         norm_w=_cpu(params["norm_w"]).numpy(),
                         lower_bound=params["lower_bound"], l2_eps=params["l2_eps"],
-                        rms_eps=params["rms_eps"])
+                        rms_eps=params["rms_eps"], gate_kind=params.get("gate_kind", 0))
 
 
 def io_code(dtype) -> int:
@@ -89,7 +89,7 @@ def decode_as_prefill(dec: dict, steps: int, b: int, h: int) -> dict:
     prob["layer"] = dict(num_heads=1, conv_w=torch.from_numpy(lay.conv_w),
                          dt_bias=torch.from_numpy(lay.dt_bias), A_log=torch.from_numpy(lay.A_log),
                          norm_w=torch.from_numpy(lay.norm_w), lower_bound=lay.lower_bound,
-                         l2_eps=lay.l2_eps, rms_eps=lay.rms_eps)
+                         l2_eps=lay.l2_eps, rms_eps=lay.rms_eps, gate_kind=lay.gate_kind)
     return prob
 
 

@@ -79,6 +79,19 @@ def _multi(lib, layer, batch=2, tokens=3, q=FAKE, s_in=FAKE, r_in=FAKE, s_out=FA
                                 FAKE, FAKE, s_in, r_in, s_out, r_out, FAKE, None)
 
 
+def test_gate_kind_validation():
+    kda, lib = _lib()
+    lay = _layer(kda)
+    lay.gate_kind = 7
+    assert _decode(lib, lay) == 1
+    assert b"gate_kind" in lib.kda_last_error()
+    # the softplus gate ignores lower_bound, which the bounded gate rejects above 0
+    lay = _layer(kda, lb=3.0)
+    assert _decode(lib, lay) == 1
+    lay.gate_kind = kda.GATE_SOFTPLUS
+    assert _decode(lib, lay, batch=0) == 0
+
+
 def test_decode_multi_validation():
     """Rejections happen before any launch (nothing reaches the GPU on these paths)."""
     kda, lib = _lib()

@@ -80,3 +80,41 @@ def test_scan_takes_any_lower_bound():
     with pytest.raises(kda.KdaError):
         kda.prefill(layer, prob["q"], prob["k"], prob["v"], prob["z"], prob["beta"], prob["gate"],
                     prob["cu_seqlens"].to(DEV), prob["cu_seqlens"], state_in=prob["state_in"])
+
+
+def test_softplus_gate_prefill_and_decode():
+    """Kimi-Linear's unbounded gate g = -exp(A_log) softplus(z + dt_bias): kda_prefill runs
+    the scan for it (the chunked tile factors need the lower bound), equal bit for bit to
+    the explicit scan arm and to the oracle; decode steps continue from its states."""
+    import gated_delta_rule_05_amd as kda
+    from kda_testutil import assert_close, decode_as_prefill, oracle_units
+    lens = [45, 3, 0, 60]
+    prob = synthetic.make_prefill(lens, H=2, io="bf16", seed=405, device=DEV, init_state=True,
+                                  init_ring=True)
+    prob["layer"]["gate_kind"] = kda.GATE_SOFTPLUS
+    prob["z"].mul_(0.25).sub_(3.0)  # softplus(z - 3) ~ 0.05: slow decay, state carried
+    res = _kda().prefill(kda.Layer(**prob["layer"]), prob["q"], prob["k"], prob["v"], prob["z"],
+                         prob["beta"], prob["gate"], prob["cu_seqlens"].to(DEV), prob["cu_seqlens"],
+                         state_in=prob["state_in"], ring_in=prob["ring_in"])
+    torch.cuda.synchronize()
+    scan = _scan(prob)
+    for x, y in zip(res, scan):
+        assert torch.equal(x, y)
+    _check(prob, res, _all_units(prob), "softplus_prefill")
+    # decode from the returned states: 5 steps on 4 sequences, against the oracle run over
+    # the decode tokens from those states (which the prefill check pinned)
+    layer = kda.Layer(**prob["layer"])
+    dec = synthetic.make_decode(B=4, H=2, io="bf16", steps=5, seed=406, device=DEV)
+    dec["layer"] = prob["layer"]
+    dec["z"].mul_(0.25).sub_(3.0)
+    dec["state"], dec["ring"] = res[1].clone(), res[2].clone()
+    st, rg = dec["state"].clone(), dec["ring"].clone()
+    outs = torch.stack([kda.decode_step(layer, dec["q"][s], dec["k"][s], dec["v"][s], dec["z"][s],
+                                        dec["beta"][s], dec["gate"][s], st, rg) for s in range(5)])
+    torch.cuda.synchronize()
+    for b in range(4):
+        for h in range(2):
+            (o_ref, s_ref, _), = oracle_units(decode_as_prefill(dec, 5, b, h), [(0, 0)], workers=1)
+            assert_close(outs[:, b, h * 128:(h + 1) * 128].float().cpu().numpy(), o_ref, True,
+                         f"softplus decode out (b={b}, h={h})", stored_bf16=True)
+            assert_close(st[b, h].cpu().numpy(), s_ref, True, f"softplus decode state (b={b}, h={h})")
