@@ -205,5 +205,17 @@ __device__ __forceinline__ void eliminate_strided(float* tt, const float* arow) 
   }
 }
 
+// The same for two of the four strided slots (SA, SB) only: columns never mix in the
+// elimination, so two waves can share it, one taking slots {0, 3} and the other {1, 2}
+// (18 updates each).
+template <int J, int SA, int SB>
+__device__ __forceinline__ void eliminate_strided2(float* tt, const float* arow) {
+  if constexpr (J < C - 1) {
+    if constexpr (SA <= J / 4) tt[0] -= arow[J] * row_bcast<J>(tt[0]);
+    if constexpr (SB <= J / 4) tt[1] -= arow[J] * row_bcast<J>(tt[1]);
+    eliminate_strided2<J + 1, SA, SB>(tt, arow);
+  }
+}
+
 }  // namespace mf
 }  // namespace kda

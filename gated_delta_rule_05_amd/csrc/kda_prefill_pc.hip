@@ -11,7 +11,7 @@
 //     into LDS;
 //   * 8 consumer waves run chunk c's state pass, one 16-column value tile of the fp32
 //     128x128 state each, held in MFMA accumulators for the whole sequence: O = Qa S,
-//     beside which one of them forms T = (I + A)^-1 Diag(beta) (DPP elimination, once
+//     beside which two of them form T = (I + A)^-1 Diag(beta) (DPP elimination, once
 //     per chunk);
 //     then U~ = T V, W^T = Ka^T T^T (landing in the A-operand layout of W.S),
 //     U = U~ - W S, O += P U; then the gated RMSNorm epilogue; then
@@ -35,9 +35,10 @@ constexpr int PW = 8;                  // producer waves
 constexpr int CWN = 8;                 // consumer waves
 constexpr int PT = 64 * PW;            // producer threads
 // Waves that also run the once-per-chunk jobs (wave w runs on SIMD w % 4): the T
-// elimination goes to a consumer wave, whose interval 1 is light; the two Gram tiles to
-// the v producer waves (SIMDs 0 and 1), which are otherwise idle in interval 4.
-constexpr int kElimCw = 2;  // consumer wave PW + 2, on SIMD 2
+// elimination goes to two consumer waves, whose interval 1 is light; the two Gram tiles
+// to the v producer waves (SIMDs 0 and 1), which are otherwise idle in interval 4.
+constexpr int kElimCwA = 2;  // consumer waves PW + 2 and PW + 3, on SIMDs 2 and 3
+constexpr int kElimCwB = 3;
 constexpr int kGramAWave = 4;
 constexpr int kGramPWave = 5;
 constexpr int NT = 64 * (PW + CWN);
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       if (has_next && (uwave == kGramAWave || uwave == kGramPWave)) {
         const bool gram_a = uwave == kGramAWave;
         // Gram tiles of chunk i + 1: A = Kp Km^T (strict lower, times beta_r), eliminated
-        // by consumer wave kElimCw in the next interval 1; P = Qp Km^T (lower incl.)
+        // by consumer waves kElimCwA/B in the next interval 1; P = Qp Km^T (lower incl.)
         const __bf16(*Xh)[OPP] = gram_a ? sm.kp[0] : sm.qp[0];
         const __bf16(*Xl)[OPP] = gram_a ? sm.kp[1] : sm.qp[1];
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
@@ -471,12 +472,13 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 
       // ---------------------------------------------------------- interval 1
       if (i >= 0) {
-        if (cw == kElimCw) {
+        if (cw == kElimCwA || cw == kElimCwB) {
           // T = (I + A)^-1 Diag(beta) by elimination with rows spread over lanes (DPP
           // broadcasts inside each 16-lane row); A[r][j] = 0 for j >= r, so the update
-          // is unconditional.  Lane (lm, lq) ends up with T[lm][lq + 4 s].
-          float arow[C], tt[4];
-  #pragma unroll
+          // is unconditional.  Lane (lm, lq) holds T[lm][lq + 4 s]; wave kElimCwA takes
+          // slots s = 0, 3 and wave kElimCwB slots 1, 2.
+          float arow[C], tt[2];
+#pragma unroll
           for (int j = 0; j < C; j += 4) {
             const float4 v4 = *reinterpret_cast<const float4*>(&sm.A[lm][j]);
             arow[j] = v4.x;
@@ -485,11 +487,16 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
             arow[j + 3] = v4.w;
           }
           const float bl = K.beta[lm];
-  #pragma unroll
-          for (int s = 0; s < 4; ++s) tt[s] = (lq + 4 * s == lm) ? bl : 0.f;
-          eliminate_strided<0>(tt, arow);
-  #pragma unroll
-          for (int s = 0; s < 4; ++s) split_store(&K.tm[0][lm][lq + 4 * s], &K.tm[1][lm][lq + 4 * s], tt[s]);
+          const bool wa = cw == kElimCwA;
+          const int s0 = wa ? 0 : 1, s1 = wa ? 3 : 2;
+          tt[0] = (lq + 4 * s0 == lm) ? bl : 0.f;
+          tt[1] = (lq + 4 * s1 == lm) ? bl : 0.f;
+          if (wa)
+            eliminate_strided2<0, 0, 3>(tt, arow);
+          else
+            eliminate_strided2<0, 1, 2>(tt, arow);
+          split_store(&K.tm[0][lm][lq + 4 * s0], &K.tm[1][lm][lq + 4 * s0], tt[0]);
+          split_store(&K.tm[0][lm][lq + 4 * s1], &K.tm[1][lm][lq + 4 * s1], tt[1]);
         }
         // S as fp16 B operands (per 32 keys: 4 lq + s, then 16 + 4 lq + s)
 #pragma unroll
