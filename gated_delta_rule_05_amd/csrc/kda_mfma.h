@@ -128,6 +128,27 @@ __device__ __forceinline__ f32x4_t mma16s(bf16x4_t ah, bf16x4_t al, bf16x4_t bh,
   return mma16(ah, bh, c);
 }
 
+// The same for a 16-long inner dimension on the 16x16x32 instruction, which issues in the
+// same time as the 16x16x16 one.  The A operand carries both halves, a = [ah | al] (slots
+// j < 4 of a lane hold ah, slots j >= 4 al, for the same four positions of the inner
+// dimension), and the two B operands are built once per tile: b_l0 = [bl | 0] and
+// b_hh = [bh | bh].  Then a b_l0 = ah bl and a b_hh = ah bh + al bh.  Both steps use the
+// same opcode: a 16x16x16 result taken as the accumulator of a 16x16x32 a few instructions
+// later gave wrong rows on gfx950, whereas chains of one opcode accumulate correctly.
+__device__ __forceinline__ f32x4_t mma16p(bf16x8_t a, bf16x8_t b_l0, bf16x8_t b_hh, f32x4_t c) {
+  c = mma32(a, b_l0, c);
+  return mma32(a, b_hh, c);
+}
+// (b_l0, b_hh) from the bf16 halves of a B operand
+__device__ __forceinline__ void b_pair(bf16x4_t bh, bf16x4_t bl, bf16x8_t& b_l0, bf16x8_t& b_hh) {
+  const bf16x4_t z = {};
+  b_l0 = __builtin_shufflevector(bl, z, 0, 1, 2, 3, 4, 5, 6, 7);
+  b_hh = __builtin_shufflevector(bh, bh, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// Position of element x (0..15) of a row in the interleaved (hi, lo) layout read by
+// mma16p: lane group x / 4 takes 8 values, ah then al.  The lo part sits 4 further on.
+__device__ __forceinline__ int il16(int x) { return 8 * (x >> 2) + (x & 3); }
+
 template <typename V, typename E>
 __device__ __forceinline__ V ld(const E* p) {
   return *reinterpret_cast<const V*>(p);

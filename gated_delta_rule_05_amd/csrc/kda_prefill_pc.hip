@@ -45,6 +45,7 @@ constexpr int NT = 64 * (PW + CWN);
 constexpr int LDP = 132;               // fp32 row stride of [16][128] arrays
 constexpr int OPP = 136;               // bf16 row stride of [16][128] operands
 constexpr int KTP = 24;                // bf16 row stride of [128][16] operands
+constexpr int ILP = 40;                // bf16 row stride of interleaved hi/lo [.][16] operands
 
 struct PcOrder {
   int32_t idx[kMaxOrdered];
@@ -54,9 +55,9 @@ struct PcOrder {
 struct alignas(16) KBuf {
   _Float16 qa[C][OPP];          // Qa = q-hat exp(Gcum), fp16, key order of the .S products
   __bf16 kat[kHeadDim][KTP];    // Ka^T, hi
-  __bf16 klt[2][kHeadDim][KTP]; // Kl^T, hi/lo
-  __bf16 p[2][C][20];           // P (lower incl.), hi/lo
-  __bf16 tm[2][C][20];          // T = (I + A)^-1 Diag(beta), hi/lo
+  __bf16 klt[kHeadDim][ILP];    // Kl^T, hi/lo interleaved (il16)
+  __bf16 p[C][ILP];             // P (lower incl.), hi/lo interleaved
+  __bf16 tm[C][ILP];            // T = (I + A)^-1 Diag(beta), hi/lo interleaved
   float V[C][LDP];              // V = silu(conv v)
   float eg15[kHeadDim];         // exp(Gcum at the chunk end)
   float beta[C];
@@ -89,6 +90,8 @@ static_assert(sizeof(PcSmem) + kDmaBytes <= 160 * 1024, "LDS budget of one workg
 static_assert(offsetof(PcSmem, kb) % 16 == 0 && sizeof(KBuf) % 16 == 0 &&
                   offsetof(KBuf, qa) % 16 == 0 && offsetof(KBuf, eg15) % 16 == 0 &&
                   offsetof(KBuf, V) % 16 == 0 && offsetof(PcSmem, ss) % 16 == 0 &&
+                  offsetof(KBuf, klt) % 16 == 0 && offsetof(KBuf, p) % 16 == 0 &&
+                  offsetof(KBuf, tm) % 16 == 0 && (ILP * 2) % 16 == 0 &&
                   offsetof(PcSmem, A) % 16 == 0 && offsetof(PcSmem, aq) % 16 == 0 &&
                   offsetof(PcSmem, ak) % 16 == 0 && offsetof(PcSmem, gam) % 16 == 0 &&
                   offsetof(PcSmem, g7) % 16 == 0 && offsetof(PcSmem, qp) % 16 == 0 &&
@@ -373,7 +376,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           KN.kat[c4 + v][r] = static_cast<__bf16>(ka[v]);
-          split_store(&KN.klt[0][c4 + v][r], &KN.klt[1][c4 + v][r], kl[v]);
+          split_store(&KN.klt[c4 + v][il16(r)], &KN.klt[c4 + v][il16(r) + 4], kl[v]);
         }
       }
       lds_barrier();
@@ -402,7 +405,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           if (gram_a) {
             sm.A[r][j] = (j < r) ? KN.beta[r] * acc[s] : 0.f;
           } else {
-            split_store(&KN.p[0][r][j], &KN.p[1][r][j], (j <= r) ? acc[s] : 0.f);
+            split_store(&KN.p[r][il16(j)], &KN.p[r][il16(j) + 4], (j <= r) ? acc[s] : 0.f);
           }
         }
       }
@@ -447,7 +450,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     const float nw = a.L.norm_w[col];
     lds_barrier();
 
-    bf16x4_t uh = {}, ul = {};
+    bf16x8_t u_l0 = {}, u_hh = {};  // U as the B operands of mma16p
     // S = Diag(exp(Gcum_C)) S + Kl^T U, once chunk i's U is known
     auto update_state = [&](const KBuf& K) __attribute__((always_inline)) {
 #pragma unroll
@@ -457,8 +460,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         S[it][1] *= e4.y;
         S[it][2] *= e4.z;
         S[it][3] *= e4.w;
-        S[it] = mma16s(ld<bf16x4_t>(&K.klt[0][16 * it + lm][4 * lq]),
-                       ld<bf16x4_t>(&K.klt[1][16 * it + lm][4 * lq]), uh, ul, S[it]);
+        S[it] = mma16p(ld<bf16x8_t>(&K.klt[16 * it + lm][8 * lq]), u_l0, u_hh, S[it]);
       }
     };
 
@@ -495,8 +497,8 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
             eliminate_strided2<0, 0, 3>(tt, arow);
           else
             eliminate_strided2<0, 1, 2>(tt, arow);
-          split_store(&K.tm[0][lm][lq + 4 * s0], &K.tm[1][lm][lq + 4 * s0], tt[0]);
-          split_store(&K.tm[0][lm][lq + 4 * s1], &K.tm[1][lm][lq + 4 * s1], tt[1]);
+          split_store(&K.tm[lm][il16(lq + 4 * s0)], &K.tm[lm][il16(lq + 4 * s0) + 4], tt[0]);
+          split_store(&K.tm[lm][il16(lq + 4 * s1)], &K.tm[lm][il16(lq + 4 * s1) + 4], tt[1]);
         }
         // S as fp16 B operands (per 32 keys: 4 lq + s, then 16 + 4 lq + s)
 #pragma unroll
@@ -517,8 +519,8 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       // ---------------------------------------------------------- interval 2
       if (i >= 0) {
         // T, split into bf16 hi/lo: lane (lm, lq) holds T[lm][4 lq + s]
-        const bf16x4_t th = ld<bf16x4_t>(&K.tm[0][lm][4 * lq]);
-        const bf16x4_t tl = ld<bf16x4_t>(&K.tm[1][lm][4 * lq]);
+        const bf16x8_t tq = ld<bf16x8_t>(&K.tm[lm][8 * lq]);
+        const bf16x4_t th = __builtin_shufflevector(tq, tq, 0, 1, 2, 3);
         // U~ = T V for this wave's value tile
         f32x4_t Ut = {0.f, 0.f, 0.f, 0.f};
         {
@@ -527,7 +529,9 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           for (int s = 0; s < 4; ++s) v4[s] = K.V[4 * lq + s][col];
           bf16x4_t vh, vl;
           split_vec<4>(v4, vh, vl);
-          Ut = mma16s(th, tl, vh, vl, Ut);
+          bf16x8_t v_l0, v_hh;
+          b_pair(vh, vl, v_l0, v_hh);
+          Ut = mma16p(tq, v_l0, v_hh, Ut);
         }
         // W S, with W^T = Ka^T T^T computed two 16-key tiles at a time
         f32x4_t ws = {0.f, 0.f, 0.f, 0.f};
@@ -548,10 +552,12 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         const f32x4_t U = Ut - ws;
         {
           float u4[4] = {U[0], U[1], U[2], U[3]};
+          bf16x4_t uh, ul;
           split_vec<4>(u4, uh, ul);
+          b_pair(uh, ul, u_l0, u_hh);
         }
         // O += P U
-        O = mma16s(ld<bf16x4_t>(&K.p[0][lm][4 * lq]), ld<bf16x4_t>(&K.p[1][lm][4 * lq]), uh, ul, O);
+        O = mma16p(ld<bf16x8_t>(&K.p[lm][8 * lq]), u_l0, u_hh, O);
         float ss[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) ss[s] = row_sum16(O[s] * O[s]);
