@@ -76,6 +76,8 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_wave_base)
                : "memory", "m0");
 }
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits for this wave's outstanding LDS operations (e.g. reads of a buffer it refills next).
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Hides a value from the optimiser so that address arithmetic is recomputed where it is
 // used instead of being kept live (in 64-bit registers) across the whole kernel.

@@ -3,22 +3,29 @@
 // Same algebra as the fp32 prefill kernel (kda_prefill.hip; docs.rs "memra_engine::kda"
 // header prose for the per-channel Gcum chunk form, "Kimi Delta Attention (KDA) --
 // analysis & C kernel plan" section "Recurrence", OpenModelAtlas "Kimi K3 - Retention
-// gate" "Why" for the 16-token tile bound), mapped so that the two kinds of work overlap:
+// gate" "Why" for the 16-token tile bound), mapped so that the two kinds of work overlap.
+//
+// The keys enter unnormalised.  With k-hat = a / |a|' (|a|' = sqrt(|a|^2 + eps)), the update
+// beta k-hat (v - S^T k-hat)^T equals beta' a (v' - S^T a)^T with beta' = beta / |a|'^2 and
+// v' = |a|' v, so the recurrence is the same one over the raw SiLU outputs a with beta'
+// and v'; likewise o = S^T q-hat is S^T a_q scaled per row.  The operands of a chunk are
+// therefore built before its row norms are known; the norms only touch beta', V' and the
+// output rows.
 //
 //   * 8 producer waves build everything chunk c+1 needs from its raw rows alone: short
-//     conv + SiLU, gate and Gcum, q/k norms, MFMA-ready operands (bf16 hi/lo) and the
-//     Gram tiles A and P, while the next-but-one chunk's raw rows stream from HBM straight
-//     into LDS;
+//     conv + SiLU, gate and Gcum (interval 1); the MFMA-ready operands (bf16 hi/lo, fp16)
+//     and partial sums of squares of the q and k rows (interval 2); the Gram tiles
+//     A = Kp Km^T and P = Qp Km^T and the row norms (interval 3).  Each wave streams the
+//     next-but-one chunk's raw rows of its own slice from HBM straight into LDS.
 //   * 8 consumer waves run chunk c's state pass, one 16-column value tile of the fp32
-//     128x128 state each, held in MFMA accumulators for the whole sequence: O = Qa S,
-//     beside which two of them form T = (I + A)^-1 Diag(beta) (DPP elimination, once
-//     per chunk);
-//     then U~ = T V, W^T = Ka^T T^T (landing in the A-operand layout of W.S),
-//     U = U~ - W S, O += P U; then the gated RMSNorm epilogue; then
+//     128x128 state each, held in MFMA accumulators for the whole sequence: O = Qa S and
+//     X = Ka S, beside which two of them form T = (I + A)^-1 Diag(beta') (DPP
+//     elimination, once per chunk); then U = U~ - W S = T (V' - X) (with U~ = T V' and
+//     W = T Ka) and O += P U; then the gated RMSNorm epilogue and
 //     S <- Diag(e^Gcum_C) S + Kl^T U.
 //
 // Operands that cross from producers to consumers are double-buffered by chunk parity.
-// Four LDS barriers per chunk.  With 16 waves per workgroup each SIMD holds two producer
+// Three LDS barriers per chunk.  With 16 waves per workgroup each SIMD holds two producer
 // and two consumer waves, so the VALU-heavy and MFMA-heavy halves hide each other's
 // latencies.
 #include "kda_device.h"
@@ -36,7 +43,7 @@ constexpr int CWN = 8;                 // consumer waves
 constexpr int PT = 64 * PW;            // producer threads
 // Waves that also run the once-per-chunk jobs (wave w runs on SIMD w % 4): the T
 // elimination goes to two consumer waves, whose interval 1 is light; the two Gram tiles
-// to the v producer waves (SIMDs 0 and 1), which are otherwise idle in interval 4.
+// to the v producer waves (SIMDs 0 and 1), which are otherwise idle in interval 3.
 constexpr int kElimCwA = 2;  // consumer waves PW + 2 and PW + 3, on SIMDs 2 and 3
 constexpr int kElimCwB = 3;
 constexpr int kGramAWave = 4;
@@ -44,8 +51,9 @@ constexpr int kGramPWave = 5;
 constexpr int NT = 64 * (PW + CWN);
 constexpr int LDP = 132;               // fp32 row stride of [16][128] arrays
 constexpr int OPP = 136;               // bf16 row stride of [16][128] operands
-constexpr int KTP = 24;                // bf16 row stride of [128][16] operands
 constexpr int ILP = 40;                // bf16 row stride of interleaved hi/lo [.][16] operands
+constexpr int NSP = 36;                // fp32 row stride of the [16][32] partial sums of squares
+constexpr float kQScale = 0.08838834764831845f;  // d^-1/2
 
 struct PcOrder {
   int32_t idx[kMaxOrdered];
@@ -53,31 +61,31 @@ struct PcOrder {
 
 // What consumers read for one chunk (double-buffered by chunk parity).
 struct alignas(16) KBuf {
-  _Float16 qa[C][OPP];          // Qa = q-hat exp(Gcum), fp16, key order of the .S products
-  __bf16 kat[kHeadDim][KTP];    // Ka^T, hi
+  _Float16 qa[C][OPP];          // Qa = a_q exp(Gcum), fp16, key order of the .S products
+  _Float16 ka[C][OPP];          // Ka = a_k exp(Gcum), fp16, key order of the .S products
   __bf16 klt[kHeadDim][ILP];    // Kl^T, hi/lo interleaved (il16)
   __bf16 p[C][ILP];             // P (lower incl.), hi/lo interleaved
-  __bf16 tm[C][ILP];            // T = (I + A)^-1 Diag(beta), hi/lo interleaved
-  float V[C][LDP];              // V = silu(conv v)
+  __bf16 tm[C][ILP];            // T = (I + A)^-1 Diag(beta'), hi/lo interleaved
+  float V[C][LDP];              // v = silu(conv v)
   float eg15[kHeadDim];         // exp(Gcum at the chunk end)
-  float beta[C];
+  float beta[C];                // sigmoid(raw beta), then beta' = beta / |a_k|'^2
+  float vk[C];                  // |a_k|' = sqrt(|a_k|^2 + eps): V' = vk V
+  float rq[C];                  // d^-1/2 / |a_q|'
 };
 
 struct alignas(16) PcSmem {
   KBuf kb[2];
-  uint16_t braw[C];             // staged raw beta
-  float aq[C][LDP];             // silu(conv q)
-  float ak[C][LDP];             // silu(conv k)
+  float aq[C][LDP];             // a_q = silu(conv q)
+  float ak[C][LDP];             // a_k = silu(conv k)
   float gam[C][LDP];            // Gcum (log2 units)
-  __bf16 qp[2][C][OPP];         // Qp = q-hat exp(Gcum - Gref), hi/lo
-  __bf16 kp[2][C][OPP];         // Kp = k-hat exp(Gcum - Gref), hi/lo
-  __bf16 km[2][C][OPP];         // Km = k-hat exp(Gref - Gcum), hi/lo
+  __bf16 qp[2][C][OPP];         // Qp = a_q exp(Gcum - Gref), hi/lo
+  __bf16 kp[2][C][OPP];         // Kp = a_k exp(Gcum - Gref), hi/lo
+  __bf16 km[2][C][OPP];         // Km = a_k exp(Gref - Gcum), hi/lo
   float g7[kHeadDim];           // Gcum at the chunk midpoint (Gram reference), log2 units
-  float g15[kHeadDim];          // Gcum at the chunk end, log2 units
   float eg7[kHeadDim];          // exp(Gcum at the midpoint)
   float e157[kHeadDim];         // exp(Gcum at the end - Gcum at the midpoint)
-  float rn[2 * C];              // 1/|q| * d^-1/2, then 1/|k|
-  float A[C][20];               // A times beta (strict lower), for the elimination
+  float nsq[2][C][NSP];         // per row: sums of squares of a_q (0) and a_k (1), per 4 channels
+  float A[C][20];               // A times beta' (strict lower), for the elimination
   float ss[CWN][C];             // per consumer wave, per row: sum of O^2 over its columns
 };
 
@@ -95,13 +103,16 @@ static_assert(offsetof(PcSmem, kb) % 16 == 0 && sizeof(KBuf) % 16 == 0 &&
                   offsetof(PcSmem, A) % 16 == 0 && offsetof(PcSmem, aq) % 16 == 0 &&
                   offsetof(PcSmem, ak) % 16 == 0 && offsetof(PcSmem, gam) % 16 == 0 &&
                   offsetof(PcSmem, g7) % 16 == 0 && offsetof(PcSmem, qp) % 16 == 0 &&
+                  offsetof(PcSmem, nsq) % 16 == 0 && offsetof(KBuf, beta) % 16 == 0 &&
+                  offsetof(KBuf, vk) % 16 == 0 && offsetof(KBuf, rq) % 16 == 0 &&
                   offsetof(PcSmem, kp) % 16 == 0 && offsetof(PcSmem, km) % 16 == 0,
               "16-byte aligned LDS members");
 
 __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder order, SplitPlan plan) {
   __shared__ PcSmem sm;
-  // raw rows of q, k, v, z of the next-but-one chunk, unpadded
-  __shared__ __attribute__((aligned(16))) uint16_t raw_lds[4][C][kHeadDim];
+  // raw rows of q, k, v, z of the next chunk, as [plane][channel half][row][64]: producer
+  // wave w reads and refills slice [w / 2][w % 2] only
+  __shared__ __attribute__((aligned(16))) uint16_t raw_lds[4][2][C][kHeadDim / 2];
   // raw output-gate rows, double-buffered by chunk parity (read by the epilogue)
   __shared__ __attribute__((aligned(16))) uint16_t graw_lds[2][C][kHeadDim];
 
@@ -159,6 +170,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     // ============================================================== producer waves
     const int urole = __builtin_amdgcn_readfirstlane(role);
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    const int hf = uwave & 1;  // channel half of this wave's raw slice
     float w[4] = {0.f, 0.f, 0.f, 0.f}, hist[3] = {0.f, 0.f, 0.f};
     if (urole < 3) {
 #pragma unroll
@@ -181,17 +193,14 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     const float ga = -kLog2e * ascale, gb = -kLog2e * ascale * a.L.dt_bias[c];
     const float lb2 = kLog2e * a.L.lower_bound;
 
-    // Raw rows of a chunk, straight into LDS, as 16 pieces of 16 bytes per row.  Planes q,
-    // k, v, z go to sm.raw: piece s (plane s / 256, row (s / 16) % 16, bytes 16 (s % 16) of
-    // the row) lands at byte 16 s, so the 64 pieces of one wave instruction are 1 KiB
-    // contiguous, as the instruction writes them.  The output-gate plane goes to the
-    // consumers' double-buffered copy in the same way.  Rows past the end of a sequence
-    // re-read its last row.
-    constexpr int SPR = kHeadDim * 2 / 16;
-    constexpr int NSEG = 4 * C * SPR;
-    static_assert(NSEG == 2 * PT && (C * SPR) % 64 == 0, "two pieces per producer thread");
-    static_assert(C * SPR == 4 * 64, "the gate plane is four waves' pieces");
-    uint16_t braw = 0;
+    // Raw rows of a chunk, straight into LDS.  Each wave fetches exactly the slice it reads
+    // itself in interval 1 (plane urole, channels 64 hf .. + 63, all 16 rows) as two
+    // instructions of 64 pieces of 16 bytes: piece (k, lane) is row 8 k + lane / 8, bytes
+    // 16 (lane % 8) of the slice's row, and one instruction's pieces land contiguously at
+    // raw_lds[urole][hf][8 k].  No other wave touches the slice, so the wave orders its
+    // reads and refills by itself.  The output-gate plane goes to the consumers'
+    // double-buffered copy: four waves, piece s = 64 wave + lane is row s / 16, bytes
+    // 16 (s % 16).  Rows past the end of a sequence re-read its last row.
     const char* const pq = static_cast<const char*>(a.q);
     const char* const pk = static_cast<const char*>(a.k);
     const char* const pv = static_cast<const char*>(a.v);
@@ -200,44 +209,30 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     const bf16_t* const x_b = static_cast<const bf16_t*>(a.beta);
     const int row_bytes = static_cast<int>(Hd) * 2;
     const int64_t head_bytes = static_cast<int64_t>(h) * kHeadDim * 2;
-    // byte offset of this lane's piece k inside a chunk (plane base and first row aside),
-    // for a full chunk and for a last chunk of Ln rows
-    auto piece_off = [&](int k, int Ln) __attribute__((always_inline)) {
-      const int s0 = 64 * wave + k * PT;
-      const int rem = (s0 + lane) % (C * SPR);
-      return min(rem / SPR, Ln - 1) * row_bytes + 16 * (rem % SPR);
-    };
-    const int off_full0 = piece_off(0, C), off_full1 = piece_off(1, C);
+    const char* const plane_base = (urole == 0 ? pq : urole == 1 ? pk : urole == 2 ? pv : pz) +
+                                   head_bytes + (kHeadDim / 2) * 2 * hf + 16 * (lane & 7);
+    uint16_t braw = 0;  // raw beta of row t (threads t < C), one chunk ahead
     auto prefetch = [&](int c0n) __attribute__((always_inline)) {
       const int Ln = min(C, T - c0n);
-      const bool full = Ln == C;
+      const char* base = plane_base + (t0 + c0n) * Hd * 2;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int s0 = __builtin_amdgcn_readfirstlane(64 * wave + k * PT);
-        const int pl = s0 / (C * SPR);
-        const char* base = pl == 0 ? pq : pl == 1 ? pk : pl == 2 ? pv : pz;
-        base += (t0 + c0n) * Hd * 2 + head_bytes;
-        const int off = full ? (k == 0 ? off_full0 : off_full1) : piece_off(k, Ln);
-        lds_dma16(base + off, &raw_lds[0][0][0] + 8 * s0);
-      }
+      for (int k = 0; k < 2; ++k)
+        lds_dma16(base + min(8 * k + (lane >> 3), Ln - 1) * row_bytes, &raw_lds[urole][hf][8 * k][0]);
       if (t < C) braw = x_b[(t0 + c0n + min(t, Ln - 1)) * H + h].bits;
     };
     auto prefetch_gate = [&](int c0n, int buf) __attribute__((always_inline)) {
-      if (__builtin_amdgcn_readfirstlane(wave) < 4) {
+      if (uwave < 4) {
         const int Ln = min(C, T - c0n);
-        const int s0 = __builtin_amdgcn_readfirstlane(64 * wave);
-        const int rem = s0 + lane;
+        const int sg = 64 * uwave + lane;
         const char* base = pgt + (t0 + c0n) * Hd * 2 + head_bytes;
-        const int off = Ln == C ? off_full0 : min(rem / SPR, Ln - 1) * row_bytes + 16 * (rem % SPR);
-        lds_dma16(base + off, &graw_lds[buf][0][0] + 8 * s0);
+        lds_dma16(base + min(sg >> 4, Ln - 1) * row_bytes + 16 * (sg & 15),
+                  &graw_lds[buf][0][0] + 8 * 64 * uwave);
       }
     };
 
     if (T > 0) {
       prefetch(0);
-      prefetch_gate(0, 0);
       wait_vm();
-      if (t < C) sm.braw[t] = braw;
     }
     lds_barrier();
 
@@ -255,7 +250,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         // that the rows' exp/rcp chains interleave.
         uint16_t xr[C];
 #pragma unroll
-        for (int r = 0; r < C; ++r) xr[r] = raw_lds[urole][r][ch];
+        for (int r = 0; r < C; ++r) xr[r] = raw_lds[urole][hf][r][lane];
         const bool full = Ln == C;
         if (urole == 2 && transfer_m) {
           // the transfer matrix is the end state from the identity with v = 0
@@ -306,42 +301,29 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
             }
           }
           sm.g7[ch] = G7;
-          sm.g15[ch] = G;
           KN.eg15[ch] = fexp2(G);
           sm.eg7[ch] = fexp2(G7);
           sm.e157[ch] = fexp2(G - G7);
         }
-        if (t < C) KN.beta[t] = (t < Ln) ? fsigmoid(bf16_to_f32(sm.braw[t])) : 0.f;
+        if (t < C) KN.beta[t] = (t < Ln) ? fsigmoid(bf16_to_f32(braw)) : 0.f;
+        // this wave's raw slice is consumed: refill it with chunk i + 2 (the reads are
+        // complete before the transfer is issued), and fetch chunk i + 1's output gate
+        // into the buffer the consumers finished with in the previous iteration
+        if (i + 2 < nch) {
+          lds_wait();
+          prefetch((i + 2) * C);
+        }
+        prefetch_gate((i + 1) * C, (i + 1) & 1);
       }
       lds_barrier();
 
       // ---------------------------------------------------------- interval 2
-      // raw rows of chunk i + 2 (chunk i + 1's were consumed in interval 1)
-      if (i + 2 < nch) prefetch((i + 2) * C);
-      if (has_next) {
-        // q/k row norms: 16 threads per (plane, row)
-        const int task = t >> 4, part = t & 15;
-        const float(*X)[LDP] = task < C ? sm.aq : sm.ak;
-        const int r = task & (C - 1);
-        float ss = 0.f;
-#pragma unroll
-        for (int m = 0; m < kHeadDim / 16; ++m) {
-          const float x = X[r][part + 16 * m];
-          ss += x * x;
-        }
-        ss = row_sum16(ss);
-        if (part == 0)
-          sm.rn[task] = (1.0f / sqrtf(ss + a.L.l2_eps)) * (task < C ? 0.08838834764831845f : 1.0f);
-      }
-      lds_barrier();
-
-      // ---------------------------------------------------------- interval 3
       if (has_next) {
         // Every operand of chunk i + 1 for row r, channels c4 .. c4 + 3 (rows run fastest
         // across lanes, so the transposed Ka / Kl writes are 32 contiguous bytes per
-        // channel).  With d = Gcum - Gcum_mid: Qp = q-hat e^d, Kp = k-hat e^d,
-        // Km = k-hat e^-d; Qa = Qp e^Gcum_mid, Ka = Kp e^Gcum_mid, Kl = Km e^(Gcum_end -
-        // Gcum_mid).
+        // channel).  With d = Gcum - Gcum_mid: Qp = a_q e^d, Kp = a_k e^d, Km = a_k e^-d;
+        // Qa = Qp e^Gcum_mid, Ka = Kp e^Gcum_mid, Kl = Km e^(Gcum_end - Gcum_mid).  Also the
+        // rows' sums of squares over these 4 channels.
         const int r = t & (C - 1), c4 = 4 * (t >> 4);
         const float4 qv = ld<float4>(&sm.aq[r][c4]);
         const float4 kv = ld<float4>(&sm.ak[r][c4]);
@@ -349,13 +331,12 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         const float4 g7 = ld<float4>(&sm.g7[c4]);
         const float4 e7 = ld<float4>(&sm.eg7[c4]);
         const float4 e157 = ld<float4>(&sm.e157[c4]);
-        const float rq = sm.rn[r], rk = sm.rn[C + r];
-        const float q4[4] = {qv.x * rq, qv.y * rq, qv.z * rq, qv.w * rq};
-        const float k4[4] = {kv.x * rk, kv.y * rk, kv.z * rk, kv.w * rk};
+        const float q4[4] = {qv.x, qv.y, qv.z, qv.w};
+        const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
         const float d4[4] = {gv.x - g7.x, gv.y - g7.y, gv.z - g7.z, gv.w - g7.w};
         const float m7[4] = {e7.x, e7.y, e7.z, e7.w};
         const float m157[4] = {e157.x, e157.y, e157.z, e157.w};
-        float qp[4], kp[4], km[4], qa[4], ka[4], kl[4];
+        float qp[4], kp[4], km[4], qa[4], ka[4], kl[4], sq = 0.f, sk = 0.f;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float el = fexp2(d4[v]), er = fexp2(-d4[v]);
@@ -365,26 +346,48 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           qa[v] = qp[v] * m7[v];
           ka[v] = kp[v] * m7[v];
           kl[v] = km[v] * m157[v];
+          sq = fmaf(q4[v], q4[v], sq);
+          sk = fmaf(k4[v], k4[v], sk);
         }
+        sm.nsq[0][r][t >> 4] = sq;
+        sm.nsq[1][r][t >> 4] = sk;
         store4(&sm.qp[0][r][c4], &sm.qp[1][r][c4], qp);
         store4(&sm.kp[0][r][c4], &sm.kp[1][r][c4], kp);
         store4(&sm.km[0][r][c4], &sm.km[1][r][c4], km);
-        // Qa in the key order of the .S products: channels 32 kb + 4 m .. + 3 sit at
-        // 32 kb + 8 (m % 4) + 4 (m / 4)
+        // Qa and Ka in the key order of the .S products: channels 32 kb + 4 m .. + 3 sit
+        // at 32 kb + 8 (m % 4) + 4 (m / 4)
         const int pa = 32 * (c4 >> 5) + 8 * ((c4 >> 2) & 3) + 4 * ((c4 >> 4) & 1);
         store4_f16(&KN.qa[r][pa], qa);
+        store4_f16(&KN.ka[r][pa], ka);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          KN.kat[c4 + v][r] = static_cast<__bf16>(ka[v]);
+        for (int v = 0; v < 4; ++v)
           split_store(&KN.klt[c4 + v][il16(r)], &KN.klt[c4 + v][il16(r) + 4], kl[v]);
-        }
       }
       lds_barrier();
 
-      // ---------------------------------------------------------- interval 4
+      // ---------------------------------------------------------- interval 3
       if (has_next && (uwave == kGramAWave || uwave == kGramPWave)) {
         const bool gram_a = uwave == kGramAWave;
-        // Gram tiles of chunk i + 1: A = Kp Km^T (strict lower, times beta_r), eliminated
+        // Row norms: lane (lm, lq) sums the 32 partial sums of row lm.  Wave kGramAWave
+        // turns |a_k|^2 into |a_k|' and beta' = beta / |a_k|'^2, wave kGramPWave |a_q|^2
+        // into d^-1/2 / |a_q|'.
+        const float(*ns)[NSP] = sm.nsq[gram_a ? 1 : 0];
+        float tot = 0.f;
+#pragma unroll
+        for (int g = 0; g < kHeadDim / 4; g += 4) {
+          const float4 v4 = ld<float4>(&ns[lm][g]);
+          tot += (v4.x + v4.y) + (v4.z + v4.w);
+        }
+        const float den = tot + a.L.l2_eps;
+        if (lq == 0) {
+          if (gram_a) {
+            KN.vk[lm] = sqrtf(den);
+            KN.beta[lm] = KN.beta[lm] / den;
+          } else {
+            KN.rq[lm] = (1.0f / sqrtf(den)) * kQScale;
+          }
+        }
+        // Gram tiles of chunk i + 1: A = Kp Km^T (strict lower, times beta'_r), eliminated
         // by consumer waves kElimCwA/B in the next interval 1; P = Qp Km^T (lower incl.)
         const __bf16(*Xh)[OPP] = gram_a ? sm.kp[0] : sm.qp[0];
         const __bf16(*Xl)[OPP] = gram_a ? sm.kp[1] : sm.qp[1];
@@ -399,22 +402,23 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           a1 = mma32(xl, mh, a1);
         }
         acc += a1;
+        if (gram_a) {
+          // beta' of rows 4 lq .. 4 lq + 3, written just above by this wave
+          const float4 b4 = ld<float4>(&KN.beta[4 * lq]);
+          const float bp[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int r = 4 * lq + s, j = lm;
-          if (gram_a) {
-            sm.A[r][j] = (j < r) ? KN.beta[r] * acc[s] : 0.f;
-          } else {
+          for (int s = 0; s < 4; ++s) sm.A[4 * lq + s][lm] = (lm < 4 * lq + s) ? bp[s] * acc[s] : 0.f;
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int r = 4 * lq + s, j = lm;
             split_store(&KN.p[r][il16(j)], &KN.p[r][il16(j) + 4], (j <= r) ? acc[s] : 0.f);
           }
         }
       }
-      if (i + 2 < nch) {
-        wait_vm();  // this wave's pieces of chunk i + 2 are in LDS
-        if (t < C) sm.braw[t] = braw;
-        // chunk i's output gate has been read by now; its buffer takes chunk i + 2's
-        prefetch_gate((i + 2) * C, (i + 2) & 1);
-      }
+      // this wave's transfers (raw rows of chunk i + 2, output gate of chunk i + 1) are
+      // in LDS before the barrier that publishes them
+      wait_vm();
       lds_barrier();
     }
 
@@ -447,9 +451,9 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 #pragma unroll
         for (int s = 0; s < 4; ++s) S[it][s] = (transfer_m && 16 * it + 4 * lq + s == col) ? 1.f : 0.f;
     }
-    const float nw = a.L.norm_w[col];
     lds_barrier();
 
+    const float nw = a.L.norm_w[col];
     bf16x8_t u_l0 = {}, u_hh = {};  // U as the B operands of mma16p
     // S = Diag(exp(Gcum_C)) S + Kl^T U, once chunk i's U is known
     auto update_state = [&](const KBuf& K) __attribute__((always_inline)) {
@@ -466,16 +470,14 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 
     // iteration i: consumers run chunk i
     for (int i = -1; i < nch; ++i) {
-      const bool has_next = i + 1 < nch;
       KBuf& K = sm.kb[i & 1];
-      KBuf& KN = sm.kb[(i + 1) & 1];
-      f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-      f16x8_t sf[4];
+      f32x4_t O = {0.f, 0.f, 0.f, 0.f};  // Qa S + P U
+      f32x4_t X = {0.f, 0.f, 0.f, 0.f};  // Ka S
 
       // ---------------------------------------------------------- interval 1
       if (i >= 0) {
         if (cw == kElimCwA || cw == kElimCwB) {
-          // T = (I + A)^-1 Diag(beta) by elimination with rows spread over lanes (DPP
+          // T = (I + A)^-1 Diag(beta') by elimination with rows spread over lanes (DPP
           // broadcasts inside each 16-lane row); A[r][j] = 0 for j >= r, so the update
           // is unconditional.  Lane (lm, lq) holds T[lm][lq + 4 s]; wave kElimCwA takes
           // slots s = 0, 3 and wave kElimCwB slots 1, 2.
@@ -500,56 +502,39 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           split_store(&K.tm[lm][il16(lq + 4 * s0)], &K.tm[lm][il16(lq + 4 * s0) + 4], tt[0]);
           split_store(&K.tm[lm][il16(lq + 4 * s1)], &K.tm[lm][il16(lq + 4 * s1) + 4], tt[1]);
         }
-        // S as fp16 B operands (per 32 keys: 4 lq + s, then 16 + 4 lq + s)
+        // O = Qa S (rows still to be scaled by d^-1/2 / |a_q|') and X = Ka S, with S as
+        // fp16 B operands (per 32 keys: 4 lq + s, then 16 + 4 lq + s)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
+          f16x8_t sf;
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            sf[kb][s] = static_cast<_Float16>(S[2 * kb][s]);
-            sf[kb][4 + s] = static_cast<_Float16>(S[2 * kb + 1][s]);
+            sf[s] = static_cast<_Float16>(S[2 * kb][s]);
+            sf[4 + s] = static_cast<_Float16>(S[2 * kb + 1][s]);
           }
+          O = mma32h(ld<f16x8_t>(&K.qa[lm][32 * kb + 8 * lq]), sf, O);
+          X = mma32h(ld<f16x8_t>(&K.ka[lm][32 * kb + 8 * lq]), sf, X);
         }
-        // O = Qa S
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          O = mma32h(ld<f16x8_t>(&K.qa[lm][32 * kb + 8 * lq]), sf[kb], O);
       }
       lds_barrier();
 
       // ---------------------------------------------------------- interval 2
       if (i >= 0) {
-        // T, split into bf16 hi/lo: lane (lm, lq) holds T[lm][4 lq + s]
+        // U = U~ - W S = T (V' - Ka S) for this wave's value tile, V' = |a_k|' V by rows
         const bf16x8_t tq = ld<bf16x8_t>(&K.tm[lm][8 * lq]);
-        const bf16x4_t th = __builtin_shufflevector(tq, tq, 0, 1, 2, 3);
-        // U~ = T V for this wave's value tile
-        f32x4_t Ut = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t U = {0.f, 0.f, 0.f, 0.f};
         {
-          float v4[4];
+          const float4 k4 = ld<float4>(&K.vk[4 * lq]);
+          const float vk[4] = {k4.x, k4.y, k4.z, k4.w};
+          float y4[4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) v4[s] = K.V[4 * lq + s][col];
-          bf16x4_t vh, vl;
-          split_vec<4>(v4, vh, vl);
-          bf16x8_t v_l0, v_hh;
-          b_pair(vh, vl, v_l0, v_hh);
-          Ut = mma16p(tq, v_l0, v_hh, Ut);
+          for (int s = 0; s < 4; ++s) y4[s] = fmaf(K.V[4 * lq + s][col], vk[s], -X[s]);
+          bf16x4_t yh, yl;
+          split_vec<4>(y4, yh, yl);
+          bf16x8_t y_l0, y_hh;
+          b_pair(yh, yl, y_l0, y_hh);
+          U = mma16p(tq, y_l0, y_hh, U);
         }
-        // W S, with W^T = Ka^T T^T computed two 16-key tiles at a time
-        f32x4_t ws = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const f32x4_t w0 = mma16(ld<bf16x4_t>(&K.kat[32 * kb + lm][4 * lq]), th,
-                                   f32x4_t{0.f, 0.f, 0.f, 0.f});
-          const f32x4_t w1 = mma16(ld<bf16x4_t>(&K.kat[32 * kb + 16 + lm][4 * lq]), th,
-                                   f32x4_t{0.f, 0.f, 0.f, 0.f});
-          f16x8_t wb;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            wb[s] = static_cast<_Float16>(w0[s]);
-            wb[4 + s] = static_cast<_Float16>(w1[s]);
-          }
-          ws = mma32h(wb, sf[kb], ws);
-        }
-        const f32x4_t U = Ut - ws;
         {
           float u4[4] = {U[0], U[1], U[2], U[3]};
           bf16x4_t uh, ul;
@@ -563,51 +548,55 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         for (int s = 0; s < 4; ++s) ss[s] = row_sum16(O[s] * O[s]);
         if (lm == 0)
           *reinterpret_cast<float4*>(&sm.ss[cw][4 * lq]) = make_float4(ss[0], ss[1], ss[2], ss[3]);
+
       }
       lds_barrier();
 
       // ---------------------------------------------------------- interval 3
-      if (i >= 0 && write_out) {
-        // gated RMSNorm of the chunk's output rows and the store
-        const int L = min(C, T - i * C);
-        float tot[4];
-        {
-          const float4 s4 = ld<float4>(&sm.ss[0][4 * lq]);
-          tot[0] = s4.x;
-          tot[1] = s4.y;
-          tot[2] = s4.z;
-          tot[3] = s4.w;
-        }
+      if (i >= 0) {
+        if (write_out) {
+          // gated RMSNorm of the chunk's output rows and the store.  The true rows are
+          // rq O: rq O / sqrt(mean (rq O)^2 + eps) = O rq / sqrt(rq^2 mean O^2 + eps).
+          const int L = min(C, T - i * C);
+          float tot[4];
+          {
+            const float4 s4 = ld<float4>(&sm.ss[0][4 * lq]);
+            tot[0] = s4.x;
+            tot[1] = s4.y;
+            tot[2] = s4.z;
+            tot[3] = s4.w;
+          }
 #pragma unroll
-        for (int wv = 1; wv < CWN; ++wv) {
-          const float4 s4 = ld<float4>(&sm.ss[wv][4 * lq]);
-          tot[0] += s4.x;
-          tot[1] += s4.y;
-          tot[2] += s4.z;
-          tot[3] += s4.w;
-        }
-        float y[4];
+          for (int wv = 1; wv < CWN; ++wv) {
+            const float4 s4 = ld<float4>(&sm.ss[wv][4 * lq]);
+            tot[0] += s4.x;
+            tot[1] += s4.y;
+            tot[2] += s4.z;
+            tot[3] += s4.w;
+          }
+          const float4 r4 = ld<float4>(&K.rq[4 * lq]);
+          const float rq[4] = {r4.x, r4.y, r4.z, r4.w};
+          float y[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const float rr = __builtin_amdgcn_rsqf(tot[s] * (1.0f / kHeadDim) + a.L.rms_eps);
-          const float g = fsigmoid(bf16_to_f32(graw_lds[i & 1][4 * lq + s][col]));
-          y[s] = nw * O[s] * rr * g;
-        }
-        bf16_t* po = static_cast<bf16_t*>(a.out) + (t0 + i * C + 4 * lq) * Hd +
-                     static_cast<int64_t>(h) * kHeadDim + col;
-        if (L == C) {
+          for (int s = 0; s < 4; ++s) {
+            const float rr =
+                rq[s] * __builtin_amdgcn_rsqf(rq[s] * rq[s] * tot[s] * (1.0f / kHeadDim) + a.L.rms_eps);
+            const float g = fsigmoid(bf16_to_f32(graw_lds[i & 1][4 * lq + s][col]));
+            y[s] = nw * O[s] * rr * g;
+          }
+          bf16_t* po = static_cast<bf16_t*>(a.out) + (t0 + i * C + 4 * lq) * Hd +
+                       static_cast<int64_t>(h) * kHeadDim + col;
+          if (L == C) {
 #pragma unroll
-          for (int s = 0; s < 4; ++s) po[s * Hd].bits = f32_to_bf16(y[s]);
-        } else {
+            for (int s = 0; s < 4; ++s) po[s * Hd].bits = f32_to_bf16(y[s]);
+          } else {
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            if (4 * lq + s < L) po[s * Hd].bits = f32_to_bf16(y[s]);
+            for (int s = 0; s < 4; ++s)
+              if (4 * lq + s < L) po[s * Hd].bits = f32_to_bf16(y[s]);
+          }
         }
+        update_state(K);
       }
-      lds_barrier();
-
-      // ---------------------------------------------------------- interval 4
-      if (i >= 0) update_state(K);
       lds_barrier();
     }
 
