@@ -29,10 +29,13 @@ __device__ __forceinline__ float fsigmoid(float x) { return frcp(1.0f + fexp(-x)
 
 // Cross-lane moves inside a row of 16 lanes (DPP): row_newbcast:n hands every lane of the
 // row the value of its lane n; row_ror:k rotates the row by k lanes.
+// Every control used here (row_ror, row_newbcast) reads a valid lane of the same row for
+// every lane, so the instruction's old value is never kept; mov_dpp leaves it undefined,
+// which lets the compiler fold the move into the consuming add (v_add_f32_dpp) instead of
+// first zeroing a temporary.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                               0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 template <int N>
 __device__ __forceinline__ float row_bcast(float x) {
