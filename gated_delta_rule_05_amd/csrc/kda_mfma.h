@@ -95,13 +95,50 @@ __device__ __forceinline__ void split_store(__bf16* hi, __bf16* lo, float x) {
   *lo = static_cast<__bf16>(x - static_cast<float>(h));
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// The bf16 (hi, lo) split of two values, each half packed two to a register: hi rounds x
+// to nearest even, lo rounds the exact remainder x - hi.  One packed conversion per half
+// and pair; the hi values come back to fp32 by a shift and a mask.  The same values as
+// split_store, at three instructions per value instead of four.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x0, x1}, bf16x2_t));
+  const float l0 = x0 - __uint_as_float(h << 16);
+  const float l1 = x1 - __uint_as_float(h & 0xffff0000u);
+  hi = h;
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){l0, l1}, bf16x2_t));
+}
+__device__ __forceinline__ __bf16 bf16_lo(uint32_t w) { return __builtin_bit_cast(__bf16, static_cast<uint16_t>(w)); }
+__device__ __forceinline__ __bf16 bf16_hi(uint32_t w) {
+  return __builtin_bit_cast(__bf16, static_cast<uint16_t>(w >> 16));
+}
+// split_store of two values at once
+__device__ __forceinline__ void split_store2(__bf16* hi0, __bf16* lo0, __bf16* hi1, __bf16* lo1, float x0,
+                                             float x1) {
+  uint32_t h, l;
+  split2(x0, x1, h, l);
+  *hi0 = bf16_lo(h);
+  *lo0 = bf16_lo(l);
+  *hi1 = bf16_hi(h);
+  *lo1 = bf16_hi(l);
+}
+
+// Splits of N = 4 or 8 consecutive values into bf16 vectors (hi, lo).
 template <int N, typename V>
 __device__ __forceinline__ void split_vec(const float* x, V& hi, V& lo) {
+  static_assert(N == 4 || N == 8, "split_vec: 4 or 8 values");
+  uint32_t h[N / 2], l[N / 2];
 #pragma unroll
-  for (int s = 0; s < N; ++s) {
-    const __bf16 h = static_cast<__bf16>(x[s]);
-    hi[s] = h;
-    lo[s] = static_cast<__bf16>(x[s] - static_cast<float>(h));
+  for (int s = 0; s < N / 2; ++s) split2(x[2 * s], x[2 * s + 1], h[s], l[s]);
+  if constexpr (N == 4) {
+    hi = __builtin_bit_cast(V, (u32x2_t){h[0], h[1]});
+    lo = __builtin_bit_cast(V, (u32x2_t){l[0], l[1]});
+  } else {
+    hi = __builtin_bit_cast(V, (u32x4_t){h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(V, (u32x4_t){l[0], l[1], l[2], l[3]});
   }
 }
 

@@ -16,13 +16,16 @@
 //     conv + SiLU, gate and Gcum (interval 1); the MFMA-ready operands (bf16 hi/lo, fp16)
 //     and partial sums of squares of the q and k rows (interval 2); the Gram tiles
 //     A = Kp Km^T and P = Qp Km^T and the row norms (interval 3).  Each wave streams the
-//     next-but-one chunk's raw rows of its own slice from HBM straight into LDS.
+//     next-but-one chunk's raw rows of its own slice from HBM straight into LDS.  In
+//     interval 3 one of them also turns the consumers' partial sums of squares of chunk
+//     c's output rows into the RMSNorm row factors.
 //   * 8 consumer waves run chunk c's state pass, one 16-column value tile of the fp32
 //     128x128 state each, held in MFMA accumulators for the whole sequence: O = Qa S and
 //     X = Ka S, beside which two of them form T = (I + A)^-1 Diag(beta') (DPP
-//     elimination, once per chunk); then U = U~ - W S = T (V' - X) (with U~ = T V' and
-//     W = T Ka) and O += P U; then the gated RMSNorm epilogue and
-//     S <- Diag(e^Gcum_C) S + Kl^T U.
+//     elimination, once per chunk), and the gated RMSNorm epilogue of chunk c-1's rows
+//     (interval 1); then U = U~ - W S = T (V' - X) (with U~ = T V' and W = T Ka),
+//     O += P U and the rows' partial sums of squares (interval 2); then
+//     S <- Diag(e^Gcum_C) S + Kl^T U (interval 3).
 //
 // Operands that cross from producers to consumers are double-buffered by chunk parity.
 // Three LDS barriers per chunk.  With 16 waves per workgroup each SIMD holds two producer
@@ -48,12 +51,21 @@ constexpr int kElimCwA = 2;  // consumer waves PW + 2 and PW + 3, on SIMDs 2 and
 constexpr int kElimCwB = 3;
 constexpr int kGramAWave = 4;
 constexpr int kGramPWave = 5;
+// Producer wave (SIMD 2, idle in interval 3) that forms the RMSNorm row factors.
+constexpr int kNormWave = 6;
 constexpr int NT = 64 * (PW + CWN);
 constexpr int LDP = 132;               // fp32 row stride of [16][128] arrays
 constexpr int OPP = 136;               // bf16 row stride of [16][128] operands
 constexpr int ILP = 40;                // bf16 row stride of interleaved hi/lo [.][16] operands
 constexpr int NSP = 36;                // fp32 row stride of the [16][32] partial sums of squares
 constexpr float kQScale = 0.08838834764831845f;  // d^-1/2
+// The producers keep the SiLU conv outputs of q, k and v scaled by kCs = -log2 e: with
+// conv weights scaled by kCs, the conv sum is the exponent of SiLU's sigmoid in base 2,
+// and kCs a = ys / (1 + 2^ys).  The constant cancels in the per-row factors: with
+// a~ = kCs a, |a|'^2 = (|a~|^2 + kCs^2 eps) / kCs^2, so beta' = beta / (|a~|^2 + kCs^2 eps),
+// V' = |a_k|' (kCs v) and the q scale d^-1/2 / (kCs |a_q|') = -d^-1/2 / sqrt(|a~_q|^2 + kCs^2 eps).
+constexpr float kCs = -1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;  // 1 / |kCs|
 
 struct PcOrder {
   int32_t idx[kMaxOrdered];
@@ -66,17 +78,17 @@ struct alignas(16) KBuf {
   __bf16 klt[kHeadDim][ILP];    // Kl^T, hi/lo interleaved (il16)
   __bf16 p[C][ILP];             // P (lower incl.), hi/lo interleaved
   __bf16 tm[C][ILP];            // T = (I + A)^-1 Diag(beta'), hi/lo interleaved
-  float V[C][LDP];              // v = silu(conv v)
+  float V[C][LDP];              // kCs v, v = silu(conv v)
   float eg15[kHeadDim];         // exp(Gcum at the chunk end)
-  float beta[C];                // sigmoid(raw beta), then beta' = beta / |a_k|'^2
+  float beta[C];                // sigmoid(raw beta), then beta' (for the scaled keys kCs a_k)
   float vk[C];                  // |a_k|' = sqrt(|a_k|^2 + eps): V' = vk V
-  float rq[C];                  // d^-1/2 / |a_q|'
+  float rq[C];                  // q scale of the scaled rows kCs a_q: d^-1/2 / (kCs |a_q|')
 };
 
 struct alignas(16) PcSmem {
   KBuf kb[2];
-  float aq[C][LDP];             // a_q = silu(conv q)
-  float ak[C][LDP];             // a_k = silu(conv k)
+  float aq[C][LDP];             // kCs a_q, a_q = silu(conv q)
+  float ak[C][LDP];             // kCs a_k, a_k = silu(conv k)
   float gam[C][LDP];            // Gcum (log2 units)
   __bf16 qp[2][C][OPP];         // Qp = a_q exp(Gcum - Gref), hi/lo
   __bf16 kp[2][C][OPP];         // Kp = a_k exp(Gcum - Gref), hi/lo
@@ -87,6 +99,7 @@ struct alignas(16) PcSmem {
   float nsq[2][C][NSP];         // per row: sums of squares of a_q (0) and a_k (1), per 4 channels
   float A[C][20];               // A times beta' (strict lower), for the elimination
   float ss[CWN][C];             // per consumer wave, per row: sum of O^2 over its columns
+  float rr[2][C];               // per row: the RMSNorm factor, by chunk parity
 };
 
 // The LDS DMA targets are variables of their own: the compiler then knows that the
@@ -174,7 +187,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     float w[4] = {0.f, 0.f, 0.f, 0.f}, hist[3] = {0.f, 0.f, 0.f};
     if (urole < 3) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = a.L.conv_w[(role * Hd + c) * kConvTaps + j];
+      for (int j = 0; j < 4; ++j) w[j] = kCs * a.L.conv_w[(role * Hd + c) * kConvTaps + j];
       if (kseg > 0) {
         // a later segment: the conv history is the previous segment's last raw rows
         // (segments before the last are at least one chunk long)
@@ -262,24 +275,24 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 #pragma unroll
             for (int r = 0; r < C; ++r) {
               const float x = bf16_to_f32(xr[r]);
-              const float y = w[3] * x + w[0] * hist[0] + w[1] * hist[1] + w[2] * hist[2];
+              const float ys = w[3] * x + w[0] * hist[0] + w[1] * hist[1] + w[2] * hist[2];
               hist[0] = hist[1];
               hist[1] = hist[2];
               hist[2] = x;
-              dst[r][ch] = y * fsigmoid(y);
+              dst[r][ch] = ys * frcp(1.0f + fexp2(ys));
             }
           } else {
 #pragma unroll
             for (int r = 0; r < C; ++r) {
               const float x = bf16_to_f32(xr[r]);
-              const float y = w[3] * x + w[0] * hist[0] + w[1] * hist[1] + w[2] * hist[2];
+              const float ys = w[3] * x + w[0] * hist[0] + w[1] * hist[1] + w[2] * hist[2];
               const bool live = r < Ln;
               if (live) {
                 hist[0] = hist[1];
                 hist[1] = hist[2];
                 hist[2] = x;
               }
-              dst[r][ch] = live ? y * fsigmoid(y) : 0.f;
+              dst[r][ch] = live ? ys * frcp(1.0f + fexp2(ys)) : 0.f;
             }
           }
         } else {
@@ -307,18 +320,19 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         }
         if (t < C) KN.beta[t] = (t < Ln) ? fsigmoid(bf16_to_f32(braw)) : 0.f;
         // this wave's raw slice is consumed: refill it with chunk i + 2 (the reads are
-        // complete before the transfer is issued), and fetch chunk i + 1's output gate
-        // into the buffer the consumers finished with in the previous iteration
+        // complete before the transfer is issued)
         if (i + 2 < nch) {
           lds_wait();
           prefetch((i + 2) * C);
         }
-        prefetch_gate((i + 1) * C, (i + 1) & 1);
       }
       lds_barrier();
 
       // ---------------------------------------------------------- interval 2
       if (has_next) {
+        // chunk i + 1's output gate, into the buffer whose previous chunk (i - 1) the
+        // consumers' epilogue read in interval 1
+        prefetch_gate((i + 1) * C, (i + 1) & 1);
         // Every operand of chunk i + 1 for row r, channels c4 .. c4 + 3 (rows run fastest
         // across lanes, so the transposed Ka / Kl writes are 32 contiguous bytes per
         // channel).  With d = Gcum - Gcum_mid: Qp = a_q e^d, Kp = a_k e^d, Km = a_k e^-d;
@@ -360,17 +374,18 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         store4_f16(&KN.qa[r][pa], qa);
         store4_f16(&KN.ka[r][pa], ka);
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          split_store(&KN.klt[c4 + v][il16(r)], &KN.klt[c4 + v][il16(r) + 4], kl[v]);
+        for (int v = 0; v < 4; v += 2)
+          split_store2(&KN.klt[c4 + v][il16(r)], &KN.klt[c4 + v][il16(r) + 4], &KN.klt[c4 + v + 1][il16(r)],
+                       &KN.klt[c4 + v + 1][il16(r) + 4], kl[v], kl[v + 1]);
       }
       lds_barrier();
 
       // ---------------------------------------------------------- interval 3
       if (has_next && (uwave == kGramAWave || uwave == kGramPWave)) {
         const bool gram_a = uwave == kGramAWave;
-        // Row norms: lane (lm, lq) sums the 32 partial sums of row lm.  Wave kGramAWave
-        // turns |a_k|^2 into |a_k|' and beta' = beta / |a_k|'^2, wave kGramPWave |a_q|^2
-        // into d^-1/2 / |a_q|'.
+        // Row norms: lane (lm, lq) sums the 32 partial sums of row lm (of the scaled rows
+        // kCs a).  Wave kGramAWave turns them into |a_k|' and beta', wave kGramPWave into
+        // the q scale.
         const float(*ns)[NSP] = sm.nsq[gram_a ? 1 : 0];
         float tot = 0.f;
 #pragma unroll
@@ -378,13 +393,13 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           const float4 v4 = ld<float4>(&ns[lm][g]);
           tot += (v4.x + v4.y) + (v4.z + v4.w);
         }
-        const float den = tot + a.L.l2_eps;
+        const float den = tot + (kCs * kCs) * a.L.l2_eps;
         if (lq == 0) {
           if (gram_a) {
-            KN.vk[lm] = sqrtf(den);
-            KN.beta[lm] = KN.beta[lm] / den;
+            KN.vk[lm] = __builtin_amdgcn_sqrtf(den) * kLn2;
+            KN.beta[lm] = KN.beta[lm] * frcp(den);
           } else {
-            KN.rq[lm] = (1.0f / sqrtf(den)) * kQScale;
+            KN.rq[lm] = __builtin_amdgcn_rsqf(den) * -kQScale;
           }
         }
         // Gram tiles of chunk i + 1: A = Kp Km^T (strict lower, times beta'_r), eliminated
@@ -410,11 +425,22 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           for (int s = 0; s < 4; ++s) sm.A[4 * lq + s][lm] = (lm < 4 * lq + s) ? bp[s] * acc[s] : 0.f;
         } else {
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
+          for (int s = 0; s < 4; s += 2) {
             const int r = 4 * lq + s, j = lm;
-            split_store(&KN.p[r][il16(j)], &KN.p[r][il16(j) + 4], (j <= r) ? acc[s] : 0.f);
+            split_store2(&KN.p[r][il16(j)], &KN.p[r][il16(j) + 4], &KN.p[r + 1][il16(j)], &KN.p[r + 1][il16(j) + 4],
+                         (j <= r) ? acc[s] : 0.f, (j <= r + 1) ? acc[s + 1] : 0.f);
           }
         }
+      }
+      if (i >= 0 && write_out && uwave == kNormWave && lane < C) {
+        // RMSNorm factor of chunk i's output row `lane` from the consumers' partial sums:
+        // the true row is rq O, and rq O / sqrt(mean (rq O)^2 + eps) = O rr with
+        // rr = rq / sqrt(rq^2 mean O^2 + eps)
+        float tot = sm.ss[0][lane];
+#pragma unroll
+        for (int wv = 1; wv < CWN; ++wv) tot += sm.ss[wv][lane];
+        const float rq = sm.kb[i & 1].rq[lane];
+        sm.rr[i & 1][lane] = rq * __builtin_amdgcn_rsqf(rq * rq * tot * (1.0f / kHeadDim) + a.L.rms_eps);
       }
       // this wave's transfers (raw rows of chunk i + 2, output gate of chunk i + 1) are
       // in LDS before the barrier that publishes them
@@ -468,13 +494,38 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       }
     };
 
-    // iteration i: consumers run chunk i
+    // Gated RMSNorm of chunk ic's output rows O and the store, with the row factors rr
+    // that the norm wave formed from every consumer wave's partial sums.
+    auto emit = [&](int ic, const f32x4_t& Oc) __attribute__((always_inline)) {
+      const int L = min(C, T - ic * C);
+      const float4 r4 = ld<float4>(&sm.rr[ic & 1][4 * lq]);
+      const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
+      float y[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const float g = fsigmoid(bf16_to_f32(graw_lds[ic & 1][4 * lq + s][col]));
+        y[s] = nw * Oc[s] * rr[s] * g;
+      }
+      bf16_t* po = static_cast<bf16_t*>(a.out) + (t0 + ic * C + 4 * lq) * Hd + static_cast<int64_t>(h) * kHeadDim + col;
+      if (L == C) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) po[s * Hd].bits = f32_to_bf16(y[s]);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          if (4 * lq + s < L) po[s * Hd].bits = f32_to_bf16(y[s]);
+      }
+    };
+
+    // iteration i: consumers run chunk i, and emit chunk i - 1's output rows
+    f32x4_t Oprev = {0.f, 0.f, 0.f, 0.f};
     for (int i = -1; i < nch; ++i) {
       KBuf& K = sm.kb[i & 1];
       f32x4_t O = {0.f, 0.f, 0.f, 0.f};  // Qa S + P U
       f32x4_t X = {0.f, 0.f, 0.f, 0.f};  // Ka S
 
       // ---------------------------------------------------------- interval 1
+      if (i >= 1 && write_out) emit(i - 1, Oprev);
       if (i >= 0) {
         if (cw == kElimCwA || cw == kElimCwB) {
           // T = (I + A)^-1 Diag(beta') by elimination with rows spread over lanes (DPP
@@ -499,10 +550,10 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
             eliminate_strided2<0, 0, 3>(tt, arow);
           else
             eliminate_strided2<0, 1, 2>(tt, arow);
-          split_store(&K.tm[lm][il16(lq + 4 * s0)], &K.tm[lm][il16(lq + 4 * s0) + 4], tt[0]);
-          split_store(&K.tm[lm][il16(lq + 4 * s1)], &K.tm[lm][il16(lq + 4 * s1) + 4], tt[1]);
+          split_store2(&K.tm[lm][il16(lq + 4 * s0)], &K.tm[lm][il16(lq + 4 * s0) + 4], &K.tm[lm][il16(lq + 4 * s1)],
+                       &K.tm[lm][il16(lq + 4 * s1) + 4], tt[0], tt[1]);
         }
-        // O = Qa S (rows still to be scaled by d^-1/2 / |a_q|') and X = Ka S, with S as
+        // O = Qa S (rows still to be scaled by the q scale rq) and X = Ka S, with S as
         // fp16 B operands (per 32 keys: 4 lq + s, then 16 + 4 lq + s)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -554,51 +605,12 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 
       // ---------------------------------------------------------- interval 3
       if (i >= 0) {
-        if (write_out) {
-          // gated RMSNorm of the chunk's output rows and the store.  The true rows are
-          // rq O: rq O / sqrt(mean (rq O)^2 + eps) = O rq / sqrt(rq^2 mean O^2 + eps).
-          const int L = min(C, T - i * C);
-          float tot[4];
-          {
-            const float4 s4 = ld<float4>(&sm.ss[0][4 * lq]);
-            tot[0] = s4.x;
-            tot[1] = s4.y;
-            tot[2] = s4.z;
-            tot[3] = s4.w;
-          }
-#pragma unroll
-          for (int wv = 1; wv < CWN; ++wv) {
-            const float4 s4 = ld<float4>(&sm.ss[wv][4 * lq]);
-            tot[0] += s4.x;
-            tot[1] += s4.y;
-            tot[2] += s4.z;
-            tot[3] += s4.w;
-          }
-          const float4 r4 = ld<float4>(&K.rq[4 * lq]);
-          const float rq[4] = {r4.x, r4.y, r4.z, r4.w};
-          float y[4];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const float rr =
-                rq[s] * __builtin_amdgcn_rsqf(rq[s] * rq[s] * tot[s] * (1.0f / kHeadDim) + a.L.rms_eps);
-            const float g = fsigmoid(bf16_to_f32(graw_lds[i & 1][4 * lq + s][col]));
-            y[s] = nw * O[s] * rr * g;
-          }
-          bf16_t* po = static_cast<bf16_t*>(a.out) + (t0 + i * C + 4 * lq) * Hd +
-                       static_cast<int64_t>(h) * kHeadDim + col;
-          if (L == C) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) po[s * Hd].bits = f32_to_bf16(y[s]);
-          } else {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-              if (4 * lq + s < L) po[s * Hd].bits = f32_to_bf16(y[s]);
-          }
-        }
         update_state(K);
       }
       lds_barrier();
+      Oprev = O;
     }
+    if (nch > 0 && write_out) emit(nch - 1, Oprev);
 
     float* dst = nullptr;
     if (a.pass == kPassTransfer)
