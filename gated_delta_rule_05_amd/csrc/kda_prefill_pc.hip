@@ -15,17 +15,17 @@
 //   * 8 producer waves build everything chunk c+1 needs from its raw rows alone: short
 //     conv + SiLU, gate and Gcum (interval 1); the MFMA-ready operands (bf16 hi/lo, fp16)
 //     and partial sums of squares of the q and k rows (interval 2); the Gram tiles
-//     A = Kp Km^T and P = Qp Km^T and the row norms (interval 3).  Each wave streams the
-//     next-but-one chunk's raw rows of its own slice from HBM straight into LDS.  In
-//     interval 3 one of them also turns the consumers' partial sums of squares of chunk
-//     c's output rows into the RMSNorm row factors.
+//     G = Kp Km^T and P = Qp Km^T, and on a third wave the row norms (interval 3).  Each
+//     wave streams the next-but-one chunk's raw rows of its own slice from HBM straight
+//     into LDS.  In interval 3 the norm wave also turns the consumers' partial sums of
+//     squares of chunk c's output rows into the RMSNorm row factors.
 //   * 8 consumer waves run chunk c's state pass, one 16-column value tile of the fp32
 //     128x128 state each, held in MFMA accumulators for the whole sequence: O = Qa S and
-//     X = Ka S, beside which two of them form T = (I + A)^-1 Diag(beta') (DPP
-//     elimination, once per chunk), and the gated RMSNorm epilogue of chunk c-1's rows
-//     (interval 1); then U = U~ - W S = T (V' - X) (with U~ = T V' and W = T Ka),
-//     O += P U and the rows' partial sums of squares (interval 2); then
-//     S <- Diag(e^Gcum_C) S + Kl^T U (interval 3).
+//     X = Ka S, beside which two of them form T = (I + A)^-1 Diag(beta') with
+//     A = Diag(beta') G (DPP elimination, once per chunk) (interval 1); then
+//     U = U~ - W S = T (V' - X) (with U~ = T V' and W = T Ka), O += P U and the rows'
+//     partial sums of squares (interval 2); then the gated RMSNorm epilogue of chunk
+//     c-1's rows and S <- Diag(e^Gcum_C) S + Kl^T U (interval 3).
 //
 // Operands that cross from producers to consumers are double-buffered by chunk parity.
 // Three LDS barriers per chunk.  With 16 waves per workgroup each SIMD holds two producer
@@ -46,12 +46,13 @@ constexpr int CWN = 8;                 // consumer waves
 constexpr int PT = 64 * PW;            // producer threads
 // Waves that also run the once-per-chunk jobs (wave w runs on SIMD w % 4): the T
 // elimination goes to two consumer waves, whose interval 1 is light; the two Gram tiles
-// to the v producer waves (SIMDs 0 and 1), which are otherwise idle in interval 3.
+// to the v producer waves (SIMDs 0 and 1) and the row norms to a z producer wave (SIMD 2),
+// which are otherwise idle in interval 3.
 constexpr int kElimCwA = 2;  // consumer waves PW + 2 and PW + 3, on SIMDs 2 and 3
 constexpr int kElimCwB = 3;
 constexpr int kGramAWave = 4;
 constexpr int kGramPWave = 5;
-// Producer wave (SIMD 2, idle in interval 3) that forms the RMSNorm row factors.
+// Producer wave that forms the row norms and the RMSNorm row factors.
 constexpr int kNormWave = 6;
 constexpr int NT = 64 * (PW + CWN);
 constexpr int LDP = 132;               // fp32 row stride of [16][128] arrays
@@ -97,7 +98,7 @@ struct alignas(16) PcSmem {
   float eg7[kHeadDim];          // exp(Gcum at the midpoint)
   float e157[kHeadDim];         // exp(Gcum at the end - Gcum at the midpoint)
   float nsq[2][C][NSP];         // per row: sums of squares of a_q (0) and a_k (1), per 4 channels
-  float A[C][20];               // A times beta' (strict lower), for the elimination
+  float A[C][20];               // G = Kp Km^T (strict lower), for the elimination
   float ss[CWN][C];             // per consumer wave, per row: sum of O^2 over its columns
   float rr[2][C];               // per row: the RMSNorm factor, by chunk parity
 };
@@ -105,7 +106,7 @@ struct alignas(16) PcSmem {
 // The LDS DMA targets are variables of their own: the compiler then knows that the
 // loads in flight cannot alias the other LDS data, and does not wait for them before
 // every LDS read.
-constexpr int kDmaBytes = (4 + 2) * C * kHeadDim * 2;
+constexpr int kDmaBytes = (4 + 3) * C * kHeadDim * 2;
 static_assert(sizeof(PcSmem) + kDmaBytes <= 160 * 1024, "LDS budget of one workgroup");
 // 16-byte LDS accesses (DMA targets, float4 and bf16x8 reads)
 static_assert(offsetof(PcSmem, kb) % 16 == 0 && sizeof(KBuf) % 16 == 0 &&
@@ -126,8 +127,9 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
   // raw rows of q, k, v, z of the next chunk, as [plane][channel half][row][64]: producer
   // wave w reads and refills slice [w / 2][w % 2] only
   __shared__ __attribute__((aligned(16))) uint16_t raw_lds[4][2][C][kHeadDim / 2];
-  // raw output-gate rows, double-buffered by chunk parity (read by the epilogue)
-  __shared__ __attribute__((aligned(16))) uint16_t graw_lds[2][C][kHeadDim];
+  // raw output-gate rows, three buffers by chunk index mod 3: the epilogue reads chunk c's
+  // in interval 3 of iteration c + 1, while chunk c + 2's arrives
+  __shared__ __attribute__((aligned(16))) uint16_t graw_lds[3][C][kHeadDim];
 
   // This workgroup's (sequence n, head h) and tokens [t0, t0 + T): a whole sequence, or
   // segment kseg of nsegs (see the passes in kda_internal.h).
@@ -330,9 +332,9 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 
       // ---------------------------------------------------------- interval 2
       if (has_next) {
-        // chunk i + 1's output gate, into the buffer whose previous chunk (i - 1) the
-        // consumers' epilogue read in interval 1
-        prefetch_gate((i + 1) * C, (i + 1) & 1);
+        // chunk i + 1's output gate, into the buffer of chunk i - 2, whose epilogue ran in
+        // the previous interval 3
+        prefetch_gate((i + 1) * C, (i + 1) % 3);
         // Every operand of chunk i + 1 for row r, channels c4 .. c4 + 3 (rows run fastest
         // across lanes, so the transposed Ka / Kl writes are 32 contiguous bytes per
         // channel).  With d = Gcum - Gcum_mid: Qp = a_q e^d, Kp = a_k e^d, Km = a_k e^-d;
@@ -383,27 +385,9 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       // ---------------------------------------------------------- interval 3
       if (has_next && (uwave == kGramAWave || uwave == kGramPWave)) {
         const bool gram_a = uwave == kGramAWave;
-        // Row norms: lane (lm, lq) sums the 32 partial sums of row lm (of the scaled rows
-        // kCs a).  Wave kGramAWave turns them into |a_k|' and beta', wave kGramPWave into
-        // the q scale.
-        const float(*ns)[NSP] = sm.nsq[gram_a ? 1 : 0];
-        float tot = 0.f;
-#pragma unroll
-        for (int g = 0; g < kHeadDim / 4; g += 4) {
-          const float4 v4 = ld<float4>(&ns[lm][g]);
-          tot += (v4.x + v4.y) + (v4.z + v4.w);
-        }
-        const float den = tot + (kCs * kCs) * a.L.l2_eps;
-        if (lq == 0) {
-          if (gram_a) {
-            KN.vk[lm] = __builtin_amdgcn_sqrtf(den) * kLn2;
-            KN.beta[lm] = KN.beta[lm] * frcp(den);
-          } else {
-            KN.rq[lm] = __builtin_amdgcn_rsqf(den) * -kQScale;
-          }
-        }
-        // Gram tiles of chunk i + 1: A = Kp Km^T (strict lower, times beta'_r), eliminated
-        // by consumer waves kElimCwA/B in the next interval 1; P = Qp Km^T (lower incl.)
+        // Gram tiles of chunk i + 1: G = Kp Km^T (strict lower; the elimination of consumer
+        // waves kElimCwA/B in the next interval 1 scales its rows by beta') and
+        // P = Qp Km^T (lower incl.)
         const __bf16(*Xh)[OPP] = gram_a ? sm.kp[0] : sm.qp[0];
         const __bf16(*Xl)[OPP] = gram_a ? sm.kp[1] : sm.qp[1];
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
@@ -418,11 +402,8 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         }
         acc += a1;
         if (gram_a) {
-          // beta' of rows 4 lq .. 4 lq + 3, written just above by this wave
-          const float4 b4 = ld<float4>(&KN.beta[4 * lq]);
-          const float bp[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-          for (int s = 0; s < 4; ++s) sm.A[4 * lq + s][lm] = (lm < 4 * lq + s) ? bp[s] * acc[s] : 0.f;
+          for (int s = 0; s < 4; ++s) sm.A[4 * lq + s][lm] = (lm < 4 * lq + s) ? acc[s] : 0.f;
         } else {
 #pragma unroll
           for (int s = 0; s < 4; s += 2) {
@@ -432,15 +413,41 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           }
         }
       }
-      if (i >= 0 && write_out && uwave == kNormWave && lane < C) {
-        // RMSNorm factor of chunk i's output row `lane` from the consumers' partial sums:
-        // the true row is rq O, and rq O / sqrt(mean (rq O)^2 + eps) = O rr with
-        // rr = rq / sqrt(rq^2 mean O^2 + eps)
-        float tot = sm.ss[0][lane];
+      if (uwave == kNormWave) {
+        const int r = lane & (C - 1);
+        if (lane < 2 * C) {
+          if (has_next) {
+            // Row norms of chunk i + 1 from the 32 partial sums of squares of each row (of
+            // the scaled rows kCs a): lanes 0..15 form |a_k|' and beta', lanes 16..31 the
+            // q scale.
+            const bool kk = lane < C;
+            const float(*ns)[NSP] = sm.nsq[kk ? 1 : 0];
+            float tot = 0.f;
 #pragma unroll
-        for (int wv = 1; wv < CWN; ++wv) tot += sm.ss[wv][lane];
-        const float rq = sm.kb[i & 1].rq[lane];
-        sm.rr[i & 1][lane] = rq * __builtin_amdgcn_rsqf(rq * rq * tot * (1.0f / kHeadDim) + a.L.rms_eps);
+            for (int g = 0; g < kHeadDim / 4; g += 4) {
+              const float4 v4 = ld<float4>(&ns[r][g]);
+              tot += (v4.x + v4.y) + (v4.z + v4.w);
+            }
+            const float den = tot + (kCs * kCs) * a.L.l2_eps;
+            if (kk) {
+              KN.vk[r] = __builtin_amdgcn_sqrtf(den) * kLn2;
+              KN.beta[r] = KN.beta[r] * frcp(den);
+            } else {
+              KN.rq[r] = __builtin_amdgcn_rsqf(den) * -kQScale;
+            }
+          }
+        } else if (lane < 3 * C) {
+          if (i >= 0 && write_out) {
+            // RMSNorm factor of chunk i's output row r from the consumers' partial sums:
+            // the true row is rq O, and rq O / sqrt(mean (rq O)^2 + eps) = O rr with
+            // rr = rq / sqrt(rq^2 mean O^2 + eps)
+            float tot = sm.ss[0][r];
+#pragma unroll
+            for (int wv = 1; wv < CWN; ++wv) tot += sm.ss[wv][r];
+            const float rq = sm.kb[i & 1].rq[r];
+            sm.rr[i & 1][r] = rq * __builtin_amdgcn_rsqf(rq * rq * tot * (1.0f / kHeadDim) + a.L.rms_eps);
+          }
+        }
       }
       // this wave's transfers (raw rows of chunk i + 2, output gate of chunk i + 1) are
       // in LDS before the barrier that publishes them
@@ -503,7 +510,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       float y[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const float g = fsigmoid(bf16_to_f32(graw_lds[ic & 1][4 * lq + s][col]));
+        const float g = fsigmoid(bf16_to_f32(graw_lds[ic % 3][4 * lq + s][col]));
         y[s] = nw * Oc[s] * rr[s] * g;
       }
       bf16_t* po = static_cast<bf16_t*>(a.out) + (t0 + ic * C + 4 * lq) * Hd + static_cast<int64_t>(h) * kHeadDim + col;
@@ -525,23 +532,23 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       f32x4_t X = {0.f, 0.f, 0.f, 0.f};  // Ka S
 
       // ---------------------------------------------------------- interval 1
-      if (i >= 1 && write_out) emit(i - 1, Oprev);
       if (i >= 0) {
         if (cw == kElimCwA || cw == kElimCwB) {
           // T = (I + A)^-1 Diag(beta') by elimination with rows spread over lanes (DPP
           // broadcasts inside each 16-lane row); A[r][j] = 0 for j >= r, so the update
           // is unconditional.  Lane (lm, lq) holds T[lm][lq + 4 s]; wave kElimCwA takes
           // slots s = 0, 3 and wave kElimCwB slots 1, 2.
+          // A = Diag(beta') G, row lm
           float arow[C], tt[2];
+          const float bl = K.beta[lm];
 #pragma unroll
           for (int j = 0; j < C; j += 4) {
             const float4 v4 = *reinterpret_cast<const float4*>(&sm.A[lm][j]);
-            arow[j] = v4.x;
-            arow[j + 1] = v4.y;
-            arow[j + 2] = v4.z;
-            arow[j + 3] = v4.w;
+            arow[j] = bl * v4.x;
+            arow[j + 1] = bl * v4.y;
+            arow[j + 2] = bl * v4.z;
+            arow[j + 3] = bl * v4.w;
           }
-          const float bl = K.beta[lm];
           const bool wa = cw == kElimCwA;
           const int s0 = wa ? 0 : 1, s1 = wa ? 3 : 2;
           tt[0] = (lq + 4 * s0 == lm) ? bl : 0.f;
@@ -604,6 +611,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       lds_barrier();
 
       // ---------------------------------------------------------- interval 3
+      if (i >= 1 && write_out) emit(i - 1, Oprev);
       if (i >= 0) {
         update_state(K);
       }
