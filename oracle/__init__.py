@@ -73,8 +73,11 @@ def _load():
             lib.kdao_prefill_units.restype = ctypes.c_int
             lib.kdao_prefill_units.argtypes = (
                 [ctypes.c_int32] * 4 + [ctypes.c_double] * 3 + [vp] * 4 + [ctypes.c_int]
-                + [vp] * 7 + [vp, vp] + [ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_int]
+                + [vp] * 7 + [vp] + [vp, vp] + [ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_int]
                 + [vp] * 7)
+            lib.kdao_gate_projection.restype = None
+            lib.kdao_gate_projection.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int64,
+                                                 ctypes.c_int32, ctypes.c_int64, vp]
             del dp
             _lib = lib
     return _lib
@@ -148,6 +151,20 @@ def gate_softplus(z: float, dt_bias: float, A_log: float) -> float:
 GATE_BOUNDED, GATE_SOFTPLUS = 0, 1
 
 
+def gate_projection(z_low, f_b, io: int) -> np.ndarray:
+    """The low-rank decay-gate projection z = z_low f_b^T in fp64: z_low [rows, r] and
+    f_b [channels, r] in the io dtype ("Kimi Delta Attention (KDA) -- analysis & C kernel
+    plan", "The KDA layer, precisely", fact 2; Retention-gate page, f_b_proj(f_a_proj(.)))."""
+    zl = _io_array(z_low, io)
+    fb = _io_array(f_b, io)
+    rows, r = zl.shape
+    ch, r2 = fb.shape
+    assert r == r2
+    z = np.empty((rows, ch))
+    _load().kdao_gate_projection(_ptr(zl), _ptr(fb), io, rows, r, ch, _ptr(z))
+    return z
+
+
 def l2norm(x, eps: float = 1e-6, scale: float = 1.0) -> np.ndarray:
     y = _f64(x).copy()
     _load().kdao_l2norm(_ptr(y), y.shape[-1], eps, scale)
@@ -196,11 +213,15 @@ def core_chunked(qh, kh, v, g, beta, S0=None, chunk: int = 64, tile: int = 16):
 # --------------------------------------------------------------------------- full mixer core
 
 class Layer:
-    """Per-layer parameters (fp32): conv_w [3*H*d, kconv], dt_bias [H*d], A_log [H], norm_w [d]."""
+    """Per-layer parameters (fp32): conv_w [3*H*d, kconv], dt_bias [H*d], A_log [H], norm_w [d].
+
+    ``f_b`` (optional, io dtype [H*d, d]) selects the low-rank decay gate: the z argument of
+    every call is then z_low [T, d] and the gate's pre-activation z_low f_b^T."""
 
     def __init__(self, num_heads, head_dim, conv_w, dt_bias, A_log, norm_w, conv_kernel=4,
-                 lower_bound=-5.0, l2_eps=1e-6, rms_eps=1e-5, gate_kind=GATE_BOUNDED):
+                 lower_bound=-5.0, l2_eps=1e-6, rms_eps=1e-5, gate_kind=GATE_BOUNDED, f_b=None):
         self.H = int(num_heads)
+        self.f_b = f_b
         self.gate_kind = int(gate_kind)
         self.d = int(head_dim)
         self.kconv = int(conv_kernel)
@@ -243,6 +264,9 @@ def prefill_units(layer: Layer, io: int, cu_seqlens, q, k, v, z, beta, gate_pre,
     st = np.empty((len(units), d, d))
     rg = np.empty((len(units), 3, d, R))
     arrs = [_io_array(a, io) for a in (q, k, v, z, beta, gate_pre)]
+    f_b = None if layer.f_b is None else _io_array(layer.f_b, io)
+    if f_b is not None:
+        assert f_b.shape == (H * d, d) and arrs[3].shape[-1] == d
     s_in = None if state_in is None else _np(state_in, np.float64)
     r_in = None if ring_in is None else _np(ring_in, np.float32)
     tr = {}
@@ -257,7 +281,7 @@ def prefill_units(layer: Layer, io: int, cu_seqlens, q, k, v, z, beta, gate_pre,
     rc = lib.kdao_prefill_units(
         H, d, layer.kconv, layer.gate_kind, layer.lower_bound, layer.l2_eps, layer.rms_eps,
         _ptr(layer.conv_w), _ptr(layer.dt_bias), _ptr(layer.A_log), _ptr(layer.norm_w),
-        io, _ptr(cu), *[_ptr(a) for a in arrs], _ptr(s_in), _ptr(r_in),
+        io, _ptr(cu), *[_ptr(a) for a in arrs], _ptr(f_b), _ptr(s_in), _ptr(r_in),
         len(units), _ptr(units), _ptr(offs), _ptr(out), _ptr(st), _ptr(rg), int(nthreads),
         *[_ptr(tr.get(key)) for key in ("q", "k", "v", "g", "beta", "o_raw", "S")])
     if rc != 0:

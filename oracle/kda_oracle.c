@@ -25,7 +25,12 @@
  *     kernel-1 multiplies the current token (PyTorch Conv1d semantics, [p1]);
  *   - the conv history ("ring") holds the kernel-1 most recent raw inputs, oldest first;
  *   - L2 norm: x * (sum x^2 + eps)^-1/2;
- *   - gated RMSNorm: normalise, multiply by the weight, then by sigmoid(gate).
+ *   - gated RMSNorm: normalise, multiply by the weight, then by sigmoid(gate);
+ *   - low-rank decay gate (optional): the gate's pre-activation is z = z_low f_b^T with
+ *     rank head_dim, f_b laid out [H*d][d] (output channel first, as a linear layer's
+ *     weight) in the io dtype ([p2] "The KDA layer, precisely", structural fact 2: hidden
+ *     -> head_dim -> H*head_dim; [p4] the model code's f_b_proj(f_a_proj(.)) and the
+ *     7,168 -> 128 -> 12,288 pair).
  *
  * Parity pins for every function here live in tests/test_oracle_pins.py.
  */
@@ -245,6 +250,25 @@ void kdao_core_chunked(int T, int dk, int dv, int C, int tau, const double* qh, 
   free(G); free(A); free(P); free(U); free(Snew);
 }
 
+/* ------------------------------------------------------------------ gate projection */
+
+/*
+ * The low-rank decay-gate projection: z[t][c] = sum_r z_low[t][r] f_b[c][r] for rows
+ * t < rows and channels c < channels, in double precision ([p2] "The KDA layer,
+ * precisely", fact 2; [p4] f_b_proj applied to the rank-128 f_a_proj output).  z_low is
+ * [rows][rank] and f_b [channels][rank], both io dtype; z is [rows][channels].
+ */
+void kdao_gate_projection(const void* z_low, const void* f_b, int io_dtype, int64_t rows,
+                          int32_t rank, int64_t channels, double* z) {
+  for (int64_t t = 0; t < rows; ++t)
+    for (int64_t c = 0; c < channels; ++c) {
+      double acc = 0.0;
+      for (int32_t r = 0; r < rank; ++r)
+        acc += load_io(z_low, io_dtype, t * rank + r) * load_io(f_b, io_dtype, c * rank + r);
+      z[t * channels + c] = acc;
+    }
+}
+
 /* ------------------------------------------------------------------ full mixer core */
 
 typedef struct {
@@ -262,6 +286,7 @@ typedef struct {
   int io_dtype;
   const int64_t* cu_seqlens; /* [N+1] */
   const void *q, *k, *v, *z, *beta, *gate; /* token-major [T_tot][H*d]; beta [T_tot][H] */
+  const void* f_b;           /* NULL, or [H*d][d]: then z is z_low [T_tot][d] */
   const double* state_in;    /* [N][H][d][d] or NULL (zero) */
   const float* ring_in;      /* [N][3*H*d][kconv-1] or NULL (zero) */
   /* per-unit outputs, in unit order: out [sum T][d], state [d][d], ring [3][d][kconv-1] */
@@ -332,7 +357,14 @@ static void run_unit(kdao_job* J, int u) {
     kdao_l2norm(a[1], d, L->l2_eps, 1.0);   /* k-hat */
     for (int i = 0; i < d; ++i) {
       const int64_t c = (int64_t)h * d + i;
-      const double zz = load_io(J->z, J->io_dtype, row * Hd + c);
+      double zz;
+      if (J->f_b) { /* low-rank gate: one row of z_low f_b^T, the reading in the header */
+        zz = 0.0;
+        for (int r = 0; r < d; ++r)
+          zz += load_io(J->z, J->io_dtype, row * d + r) * load_io(J->f_b, J->io_dtype, c * d + r);
+      } else {
+        zz = load_io(J->z, J->io_dtype, row * Hd + c);
+      }
       gv[i] = L->gate_kind == 1
                   ? kdao_gate_softplus(zz, (double)L->dt_bias[c], (double)L->A_log[h])
                   : kdao_gate(zz, (double)L->dt_bias[c], (double)L->A_log[h], L->lower_bound);
@@ -375,7 +407,9 @@ static void* worker(void* arg) {
  * Prefill over packed sequences for the listed (sequence, head) units, threaded over
  * units.  The caller lists units longest-first if it wants balanced threads.  Returns 0
  * on success, -1 on a bad argument.  `units` holds n_units (sequence, head) pairs.
- * If trace pointers are non-null, exactly one unit must be listed.
+ * If trace pointers are non-null, exactly one unit must be listed.  With f_b non-NULL
+ * ([H*d][head_dim], io dtype) z is the rank-head_dim input z_low [T_tot][head_dim] and
+ * the gate's pre-activation is its projection (kdao_gate_projection).
  */
 int kdao_prefill_units(int32_t num_heads, int32_t head_dim, int32_t conv_kernel,
                        int32_t gate_kind, double lower_bound, double l2_eps, double rms_eps,
@@ -383,7 +417,7 @@ int kdao_prefill_units(int32_t num_heads, int32_t head_dim, int32_t conv_kernel,
                        const float* dt_bias, const float* A_log, const float* norm_w,
                        int io_dtype, const int64_t* cu_seqlens, const void* q, const void* k,
                        const void* v, const void* z, const void* beta, const void* gate,
-                       const double* state_in, const float* ring_in,
+                       const void* f_b, const double* state_in, const float* ring_in,
                        int32_t n_units, const int32_t* units, const int64_t* out_offset, double* out,
                        double* state_out, double* ring_out, int nthreads, double* tr_q,
                        double* tr_k, double* tr_v, double* tr_g, double* tr_beta,
@@ -396,7 +430,7 @@ int kdao_prefill_units(int32_t num_heads, int32_t head_dim, int32_t conv_kernel,
   kdao_job J;
   memset(&J, 0, sizeof J);
   J.L = &L; J.io_dtype = io_dtype; J.cu_seqlens = cu_seqlens;
-  J.q = q; J.k = k; J.v = v; J.z = z; J.beta = beta; J.gate = gate;
+  J.q = q; J.k = k; J.v = v; J.z = z; J.beta = beta; J.gate = gate; J.f_b = f_b;
   J.state_in = state_in; J.ring_in = ring_in;
   J.units = units; J.n_units = n_units; J.out_offset = out_offset; J.out = out;
   J.state_out = state_out; J.ring_out = ring_out;

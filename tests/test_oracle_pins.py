@@ -456,3 +456,84 @@ def test_bf16_inputs_are_read_exactly():
     o_b, s_b, _ = oracle.prefill(L, oracle.BF16, [0, T], *[abf[n] for n in names])
     o_f, s_f, _ = oracle.prefill(L, oracle.F32, [0, T], *[a32r[n] for n in names])
     assert np.array_equal(o_b, o_f) and np.array_equal(s_b, s_f)
+
+
+# --------------------------------------------------------------------------- low-rank decay gate
+
+def test_gate_projection_against_numpy_and_orientation():
+    """The low-rank decay gate's pre-activation z = z_low f_b^T ("Kimi Delta Attention (KDA)
+    -- analysis & C kernel plan", "The KDA layer, precisely", fact 2: hidden -> head_dim ->
+    H * head_dim; Retention-gate page: f_b_proj(f_a_proj(.)), f_b a linear layer's weight
+    [out][in]).  The oracle's loops against numpy's fp64 matmul in fp32 and bf16 io, and
+    one-hot rows of f_b select columns of z_low, so a transposed f_b fails."""
+    zl = RNG.standard_normal((7, 128)).astype(np.float32)
+    fb = RNG.standard_normal((256, 128)).astype(np.float32)
+    z = oracle.gate_projection(zl, fb, oracle.F32)
+    assert rel(z, zl.astype(np.float64) @ fb.astype(np.float64).T) < 1e-14
+    zlb = torch.from_numpy(zl).to(torch.bfloat16)
+    fbb = torch.from_numpy(fb).to(torch.bfloat16)
+    z = oracle.gate_projection(zlb, fbb, oracle.BF16)
+    assert rel(z, zlb.double().numpy() @ fbb.double().numpy().T) < 1e-14
+    sel = RNG.integers(0, 128, 256)
+    onehot = np.zeros((256, 128), np.float32)
+    onehot[np.arange(256), sel] = 1.0
+    z = oracle.gate_projection(zl, onehot, oracle.F32)
+    assert np.array_equal(z, zl[:, sel].astype(np.float64))
+
+
+def _sparse_int_gate(H, d, T, seed):
+    """z_low with small integers and f_b with at most four entries of +-1, +-2 per row, so
+    that every z = z_low f_b^T is an integer of magnitude <= 32: exact in bf16 and fp32."""
+    r = np.random.default_rng(seed)
+    zl = r.integers(-4, 5, (T, d)).astype(np.float32)
+    fb = np.zeros((H * d, d), np.float32)
+    for c in range(H * d):
+        cols = r.choice(d, size=4, replace=False)
+        fb[c, cols] = r.choice([-2.0, -1.0, 1.0, 2.0], size=4)
+    z = zl.astype(np.float64) @ fb.astype(np.float64).T
+    assert np.all(np.abs(z) <= 32) and np.array_equal(z, np.round(z))
+    return zl, fb, z.astype(np.float32)
+
+
+@pytest.mark.parametrize("io", [oracle.F32, oracle.BF16])
+def test_low_rank_gate_full_path_equals_materialised_z(io):
+    """The full path with f_b equals the full path given z = z_low f_b^T directly, on inputs
+    where that z is exact in the io dtype; two heads, so that the head offset of f_b's rows
+    (channel c = h d + i) matters; varlen prefill with carried state and ring, then a decode
+    step from the returned state."""
+    H, d = 2, 8
+    lens = [6, 3]
+    T = sum(lens)
+    L = _layer(H, d, 41)
+    a = _acts(T, H, d, 42)
+    zl, fb, z = _sparse_int_gate(H, d, T + 1, 43)
+    r = np.random.default_rng(44)
+    S0 = r.normal(0, 0.02, (len(lens), H, d, d))
+    ring0 = r.normal(0, 1, (len(lens), 3 * H * d, 3)).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    if io == oracle.BF16:
+        conv = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16)
+    else:
+        conv = lambda x: np.ascontiguousarray(x)
+    Lf = oracle.Layer(H, d, L.conv_w, L.dt_bias, L.A_log, L.norm_w, f_b=conv(fb))
+    names = ("q", "k", "v", "beta", "gate")
+    aa = {n: conv(a[n]) for n in names}
+    o_f, s_f, r_f = oracle.prefill(Lf, io, cu, aa["q"], aa["k"], aa["v"], conv(zl[:T]), aa["beta"],
+                                   aa["gate"], S0, ring0)
+    o_m, s_m, r_m = oracle.prefill(L, io, cu, aa["q"], aa["k"], aa["v"], conv(z[:T]), aa["beta"],
+                                   aa["gate"], S0, ring0)
+    assert np.array_equal(o_f, o_m) and np.array_equal(s_f, s_m) and np.array_equal(r_f, r_m)
+    # the gate is not trivial on these inputs
+    assert np.std(z) > 1.0
+    # one decode step from the returned state of both sequences
+    B = len(lens)
+    r2 = np.random.default_rng(45)
+    d1 = {n: r2.normal(0, 1, (B, H * d if n != "beta" else H)).astype(np.float32) for n in names}
+    d1 = {n: conv(x) for n, x in d1.items()}
+    zl1, _, _ = _sparse_int_gate(H, d, B, 46)
+    z1 = (zl1.astype(np.float64) @ fb.astype(np.float64).T).astype(np.float32)
+    of, sf, rf = oracle.decode_step(Lf, io, d1["q"], d1["k"], d1["v"], conv(zl1), d1["beta"],
+                                    d1["gate"], s_f, r_f.astype(np.float32))
+    om, sm, rm = oracle.decode_step(L, io, d1["q"], d1["k"], d1["v"], conv(z1), d1["beta"],
+                                    d1["gate"], s_m, r_m.astype(np.float32))
+    assert np.array_equal(of, om) and np.array_equal(sf, sm) and np.array_equal(rf, rm)
