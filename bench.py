@@ -60,7 +60,7 @@ PREFILL_FLOPS_PER_TOKEN_HEAD = 6 * D * D + 5 * 64 * D + 64 * 64 // 3
 METRIC = "KDA tokens/s per layer (chunked prefill, decode); % of MFMA / HBM roofline"
 DECODE_KERNEL = "decode_kernel"
 PREFILL_KERNEL = "prefill_pc_kernel"  # the bf16 prefill kernel
-PREFILL_WORKLOADS = ("prefill_t4096_h32", "prefill_2x8192_h96", "varlen16_h64")
+PREFILL_WORKLOADS = ("prefill_t4096_h32", "prefill_2x8192_h96", "varlen16_h64", "prefill_2x8192_h96_lowrank")
 
 
 def kernel_source_hash(name: str) -> str:
@@ -193,6 +193,19 @@ def decode_traffic(steps_hash: str):
 
 # --------------------------------------------------------------------------- prefill
 
+def prefill_algorithmic_bytes(w) -> int:
+    """Bytes a prefill workload must move at least: the bf16 activation planes in and the
+    output out per token-head, the state and ring once per sequence (in only when given);
+    with the low-rank gate, z_low [T, 128] (shared by the heads) and f_b [H*128, 128] in
+    place of the full-rank z plane."""
+    N, H, T = len(w.seqlens), w.heads, sum(w.seqlens)
+    nbytes = (PREFILL_BYTES_PER_TOKEN_HEAD * T * H + N * H * D * D * 4 * (2 if w.init_state else 1)
+              + N * 3 * H * D * 3 * 4 * (2 if w.init_ring else 1))
+    if w.low_rank_gate:
+        nbytes += -D * 2 * T * H + D * 2 * T + H * D * D * 2
+    return nbytes
+
+
 def bench_prefill(name: str, reps: int, warmup: int = 3):
     import torch
 
@@ -235,12 +248,12 @@ def bench_prefill(name: str, reps: int, warmup: int = 3):
     times.sort()
     ms = times[len(times) // 2]
     H = w.heads
-    nbytes = (PREFILL_BYTES_PER_TOKEN_HEAD * T * H + N * H * D * D * 4 * (2 if w.init_state else 1)
-              + N * 3 * H * D * 3 * 4 * (2 if w.init_ring else 1))
+    nbytes = prefill_algorithmic_bytes(w)
     flops = PREFILL_FLOPS_PER_TOKEN_HEAD * T * H
     s = ms / 1e3
     res = dict(workload=name, sequences=N, tokens=T, heads=H,
                path="segment-parallel" if ws_bytes else "whole-sequence", workspace_bytes=ws_bytes,
+               decay_gate="low-rank (z_low f_b^T in the kernel)" if w.low_rank_gate else "full-rank z",
                ms=ms, ms_min=times[0], reps=reps,
                tokens_per_s=T / s, hbm_gbs=nbytes / s / 1e9, hbm_frac=nbytes / s / 1e9 / HBM_PEAK_GBS,
                mfma_tflops=flops / s / 1e12, mfma_frac=flops / s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
@@ -462,7 +475,7 @@ def summarize_prefill_pmc(root: str):
             return sum(v) if v else None
 
         def kernels(rows):
-            return sorted({re.findall(r"(\w+)\(", k)[0] for k, _, _ in rows if mine(k)})
+            return sorted({re.findall(r"(\w+(?:<\w+>)?)\(", k)[0] for k, _, _ in rows if mine(k)})
 
         w = synthetic.WORKLOADS[name]
         N, H, T = len(w.seqlens), w.heads, sum(w.seqlens)
@@ -470,8 +483,7 @@ def summarize_prefill_pmc(root: str):
         m = total(_read_pmc(d["mfma"], "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
         va = total(_read_pmc(d["mfma"], "SQ_INSTS_VALU"))
         mf = total(_read_pmc(d["mfma"], "SQ_INSTS_MFMA"))
-        alg = (PREFILL_BYTES_PER_TOKEN_HEAD * T * H + N * H * D * D * 4 * (2 if w.init_state else 1)
-               + N * 3 * H * D * 3 * 4 * (2 if w.init_ring else 1))
+        alg = prefill_algorithmic_bytes(w)
         traffic = (f * 1024 * f_scale + wr * 1024 * w_scale) if (f and wr and f_scale and w_scale) else None
         out[name] = dict(kernels=kernels(fetch), hbm_bytes=traffic, algorithmic_bytes=alg,
                          traffic_over_algorithmic=(traffic / alg) if traffic else None,

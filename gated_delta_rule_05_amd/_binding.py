@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 HEAD_DIM = 128
 CONV_KERNEL = 4
 
@@ -39,7 +39,7 @@ class KdaLayerC(ctypes.Structure):
                 ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("conv_w", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
                 ("A_log", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
-                ("gate_kind", ctypes.c_int32)]
+                ("gate_kind", ctypes.c_int32), ("f_b", ctypes.c_void_p)]
 
 GATE_BOUNDED, GATE_SOFTPLUS = 0, 1
 
@@ -122,11 +122,13 @@ def _need(t, name, shape, dtype, device):
 class Layer:
     """One layer's parameters on the GPU: conv_w [3*H*128, 4], dt_bias [H*128], A_log [H],
     norm_w [128], all fp32; the gate's lower bound, the two epsilons, and the gate formula
-    (GATE_BOUNDED, or GATE_SOFTPLUS for the unbounded softplus gate)."""
+    (GATE_BOUNDED, or GATE_SOFTPLUS for the unbounded softplus gate).  f_b (optional,
+    [H*128, 128] in the io dtype) selects the low-rank decay gate: the z argument of every
+    call is then z_low [rows, 128] and the gate's pre-activation z_low f_b^T."""
 
     def __init__(self, num_heads, conv_w, dt_bias, A_log, norm_w, lower_bound=-5.0,
                  l2_eps=1e-6, rms_eps=1e-5, head_dim=HEAD_DIM, conv_kernel=CONV_KERNEL,
-                 gate_kind=GATE_BOUNDED, **_):
+                 gate_kind=GATE_BOUNDED, f_b=None, **_):
         self.H = int(num_heads)
         dev = conv_w.device
         Hd = self.H * HEAD_DIM
@@ -134,11 +136,24 @@ class Layer:
         _need(dt_bias, "dt_bias", (Hd,), torch.float32, dev)
         _need(A_log, "A_log", (self.H,), torch.float32, dev)
         _need(norm_w, "norm_w", (HEAD_DIM,), torch.float32, dev)
+        if f_b is not None:
+            _need(f_b, "f_b", (Hd, HEAD_DIM), f_b.dtype, dev)
+            io_code(f_b.dtype)
+        self.f_b = f_b
         self.device = dev
-        self.tensors = (conv_w, dt_bias, A_log, norm_w)  # keep alive
+        self.tensors = (conv_w, dt_bias, A_log, norm_w, f_b)  # keep alive
         self.c = KdaLayerC(self.H, int(head_dim), int(conv_kernel), float(lower_bound),
                            float(l2_eps), float(rms_eps), conv_w.data_ptr(), dt_bias.data_ptr(),
-                           A_log.data_ptr(), norm_w.data_ptr(), int(gate_kind))
+                           A_log.data_ptr(), norm_w.data_ptr(), int(gate_kind),
+                           None if f_b is None else f_b.data_ptr())
+
+    def z_width(self, dt) -> int:
+        """Columns of the z argument: 128 (z_low) with the low-rank gate, else H*128."""
+        if self.f_b is None:
+            return self.H * HEAD_DIM
+        if self.f_b.dtype != dt:
+            raise TypeError(f"f_b has dtype {self.f_b.dtype}, the activations {dt}")
+        return HEAD_DIM
 
 
 def prefill_workspace_bytes(layer: Layer, io_dtype: torch.dtype, cu_seqlens_host) -> int:
@@ -174,8 +189,9 @@ def prefill(layer: Layer, q, k, v, z, beta, gate, cu_seqlens, cu_seqlens_host=No
     N = cu_h.numel() - 1
     T = int(cu_h[-1]) if N >= 0 else 0
     _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
-    for name, x in (("q", q), ("k", k), ("v", v), ("z", z), ("gate", gate)):
+    for name, x in (("q", q), ("k", k), ("v", v), ("gate", gate)):
         _need(x, name, (T, Hd), dt, dev)
+    _need(z, "z", (T, layer.z_width(dt)), dt, dev)
     _need(beta, "beta", (T, H), dt, dev)
     if state_in is not None:
         _need(state_in, "state_in", (N, H, HEAD_DIM, HEAD_DIM), torch.float32, dev)
@@ -222,8 +238,9 @@ def decode_step(layer: Layer, q, k, v, z, beta, gate, state, ring, out=None, str
     dt = q.dtype
     io = io_code(dt)
     B = q.shape[0]
-    for name, x in (("q", q), ("k", k), ("v", v), ("z", z), ("gate", gate)):
+    for name, x in (("q", q), ("k", k), ("v", v), ("gate", gate)):
         _need(x, name, (B, Hd), dt, dev)
+    _need(z, "z", (B, layer.z_width(dt)), dt, dev)
     _need(beta, "beta", (B, H), dt, dev)
     _need(state, "state", (B, H, HEAD_DIM, HEAD_DIM), torch.float32, dev)
     _need(ring, "ring", (B, 3 * Hd, CONV_KERNEL - 1), torch.float32, dev)
@@ -255,8 +272,9 @@ def decode_multi(layer: Layer, q, k, v, z, beta, gate, state_in, ring_in, state_
     dt = q.dtype
     io = io_code(dt)
     B, t = q.shape[0], q.shape[1]
-    for name, x in (("q", q), ("k", k), ("v", v), ("z", z), ("gate", gate)):
+    for name, x in (("q", q), ("k", k), ("v", v), ("gate", gate)):
         _need(x, name, (B, t, Hd), dt, dev)
+    _need(z, "z", (B, t, layer.z_width(dt)), dt, dev)
     _need(beta, "beta", (B, t, H), dt, dev)
     _need(state_in, "state_in", (B, H, HEAD_DIM, HEAD_DIM), torch.float32, dev)
     _need(ring_in, "ring_in", (B, 3 * Hd, CONV_KERNEL - 1), torch.float32, dev)

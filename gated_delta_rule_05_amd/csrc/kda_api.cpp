@@ -45,6 +45,7 @@ kda_status check_layer(const kda_layer* L, bool chunked) {
     return fail(KDA_ERR_INVALID_ARG, "epsilons must be finite and non-negative");
   if (L->gate_kind != KDA_GATE_BOUNDED && L->gate_kind != KDA_GATE_SOFTPLUS)
     return fail(KDA_ERR_INVALID_ARG, "unknown gate_kind %d", L->gate_kind);
+  if (L->f_b && !aligned16(L->f_b)) return fail(KDA_ERR_INVALID_ARG, "f_b must be 16-byte aligned");
   if (L->gate_kind == KDA_GATE_SOFTPLUS) return KDA_OK;  // lower_bound unused
   if (!std::isfinite(L->lower_bound) || L->lower_bound > 0.f)
     return fail(KDA_ERR_INVALID_ARG, "lower_bound must be finite and <= 0");
@@ -66,6 +67,7 @@ kda::LayerParams layer_params(const kda_layer* L) {
   p.dt_bias = L->dt_bias;
   p.A_log = L->A_log;
   p.norm_w = L->norm_w;
+  p.f_b = L->f_b;
   return p;
 }
 
@@ -257,7 +259,9 @@ kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
   a.out = out;
   a.state_out = state_out;
   a.ring_out = ring_out;
-  if (layer->gate_kind == KDA_GATE_SOFTPLUS)  // unbounded gate: no tile bound, run the scan
+  // The unbounded gate has no tile bound, and the fp32-io chunked kernel has no low-rank
+  // gate: both run the scan.
+  if (layer->gate_kind == KDA_GATE_SOFTPLUS || (layer->f_b && io == KDA_F32))
     return kda_prefill_scan(layer, io, num_seqs, cu_seqlens_dev, cu_seqlens_host, total_tokens,
                             q, k, v, z, beta, gate, state_in, ring_in, out, state_out, ring_out,
                             stream);

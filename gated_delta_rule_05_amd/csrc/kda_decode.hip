@@ -27,6 +27,39 @@
 
 namespace kda {
 
+// The low-rank decay gate's pre-activation of one channel, sum_r z_low[r] f_b[c][r] over
+// the 128 ranks ("Kimi Delta Attention (KDA) -- analysis & C kernel plan", "The KDA layer,
+// precisely", fact 2; the Retention-gate page's f_b_proj(f_a_proj(.))): 16-byte loads of
+// both rows, four partial sums.
+__device__ __forceinline__ float low_rank_z(const float* zrow, const float* frow) {
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < kHeadDim; r += 4) {
+    const float4 z4 = *reinterpret_cast<const float4*>(zrow + r);
+    const float4 f4 = *reinterpret_cast<const float4*>(frow + r);
+    acc[0] = fmaf(z4.x, f4.x, acc[0]);
+    acc[1] = fmaf(z4.y, f4.y, acc[1]);
+    acc[2] = fmaf(z4.z, f4.z, acc[2]);
+    acc[3] = fmaf(z4.w, f4.w, acc[3]);
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+__device__ __forceinline__ float low_rank_z(const bf16_t* zrow, const bf16_t* frow) {
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < kHeadDim; r += 8) {
+    const uint4 z8 = *reinterpret_cast<const uint4*>(zrow + r);
+    const uint4 f8 = *reinterpret_cast<const uint4*>(frow + r);
+    const uint32_t zw[4] = {z8.x, z8.y, z8.z, z8.w}, fw[4] = {f8.x, f8.y, f8.z, f8.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[j] = fmaf(__uint_as_float(zw[j] << 16), __uint_as_float(fw[j] << 16), acc[j]);
+      acc[j] = fmaf(__uint_as_float(zw[j] & 0xffff0000u), __uint_as_float(fw[j] & 0xffff0000u), acc[j]);
+    }
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 template <typename IO>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int H = a.L.H;
@@ -71,13 +104,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // output gate of channel i.  Raw io values are kept (converted only where used), and
   // every thread loads the same way through its own plane pointers, so no load is waited
   // for before it is needed.
+  // with the low-rank gate, z holds z_low [rows][128]: read whole in the prologue instead
+  const IO* f_b = static_cast<const IO*>(a.L.f_b);
   const IO* pa = t < kHeadDim ? x_q : x_v;
-  const IO* pb = t < kHeadDim ? x_k : x_z;
+  const IO* pb = t < kHeadDim ? x_k : (f_b ? nullptr : x_z);
   IO xa{}, xb{}, xc{}, xbeta{};
   auto fetch = [&](int tok) __attribute__((always_inline)) {
     const int64_t row = row0 + tok;
     xa = pa[row * Hd + c];
-    xb = pb[row * Hd + c];
+    if (pb) xb = pb[row * Hd + c];
     xc = x_g[row * Hd + c];
     xbeta = x_b[row * H + h];
   };
@@ -151,9 +186,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       hist[0][1] = hist[0][2];
       hist[0][2] = x;
       a_v[i] = siluf_(y);
-      const float g = a.L.gate_kind == KDA_GATE_SOFTPLUS
-                          ? kda_gate_softplus(io_to_f32(xb), dtb, ascale)
-                          : kda_gate(io_to_f32(xb), dtb, ascale, a.L.lower_bound);
+      const float zv = f_b ? low_rank_z(x_z + (row0 + tok) * kHeadDim, f_b + c * kHeadDim) : io_to_f32(xb);
+      const float g = a.L.gate_kind == KDA_GATE_SOFTPLUS ? kda_gate_softplus(zv, dtb, ascale)
+                                                         : kda_gate(zv, dtb, ascale, a.L.lower_bound);
       eg[i] = expf(g);
       sg[i] = sigmoidf_(io_to_f32(xc));
     }

@@ -18,6 +18,7 @@ struct LayerParams {
   const float* dt_bias;
   const float* A_log;
   const float* norm_w;
+  const void* f_b;    // low-rank decay gate: [H d][d] io, or null (z is full rank)
 };
 
 // Decode of up to `tokens` consecutive tokens per sequence (one token: the decode step).

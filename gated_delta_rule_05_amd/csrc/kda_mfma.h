@@ -37,6 +37,12 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
+// A DPP move whose lanes without a source lane in their row (row_shr past the row start)
+// read 0.
+template <int CTRL>
+__device__ __forceinline__ float dpp_z(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
 template <int N>
 __device__ __forceinline__ float row_bcast(float x) {
   return dpp<0x150 + N>(x);

@@ -52,8 +52,10 @@ constexpr int kElimCwA = 2;  // consumer waves PW + 2 and PW + 3, on SIMDs 2 and
 constexpr int kElimCwB = 3;
 constexpr int kGramAWave = 4;
 constexpr int kGramPWave = 5;
-// Producer wave that forms the row norms and the RMSNorm row factors.
+// Producer wave that forms the row norms and the RMSNorm row factors; with the low-rank
+// gate the k and z waves form the gate in interval 3, and a q wave (SIMD 1) takes it.
 constexpr int kNormWave = 6;
+constexpr int kNormWaveFb = 1;
 constexpr int NT = 64 * (PW + CWN);
 constexpr int LDP = 132;               // fp32 row stride of [16][128] arrays
 constexpr int OPP = 136;               // bf16 row stride of [16][128] operands
@@ -63,8 +65,8 @@ constexpr float kQScale = 0.08838834764831845f;  // d^-1/2
 // The producers keep the SiLU conv outputs of q, k and v scaled by kCs = -log2 e: with
 // conv weights scaled by kCs, the conv sum is the exponent of SiLU's sigmoid in base 2,
 // and kCs a = ys / (1 + 2^ys).  The constant cancels in the per-row factors: with
-// a~ = kCs a, |a|'^2 = (|a~|^2 + kCs^2 eps) / kCs^2, so beta' = beta / (|a~|^2 + kCs^2 eps),
-// V' = |a_k|' (kCs v) and the q scale d^-1/2 / (kCs |a_q|') = -d^-1/2 / sqrt(|a~_q|^2 + kCs^2 eps).
+// a~ = kCs a, |a|'^2 = |a~|^2 / kCs^2 + eps, beta' = beta / (kCs^2 |a_k|'^2),
+// V' = |a_k|' (kCs v) and the q scale d^-1/2 / (kCs |a_q|') = -ln 2 d^-1/2 / |a_q|'.
 constexpr float kCs = -1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;  // 1 / |kCs|
 
@@ -101,13 +103,16 @@ struct alignas(16) PcSmem {
   float A[C][20];               // G = Kp Km^T (strict lower), for the elimination
   float ss[CWN][C];             // per consumer wave, per row: sum of O^2 over its columns
   float rr[2][C];               // per row: the RMSNorm factor, by chunk parity
+  float gbias[kHeadDim];        // low-rank gate: -log2 e exp(A_log) dt_bias per channel
+  float eg15n[kHeadDim];        // low-rank gate: e^Gcum_end of the chunk formed ahead
 };
 
 // The LDS DMA targets are variables of their own: the compiler then knows that the
 // loads in flight cannot alias the other LDS data, and does not wait for them before
 // every LDS read.
 constexpr int kDmaBytes = (4 + 3) * C * kHeadDim * 2;
-static_assert(sizeof(PcSmem) + kDmaBytes <= 160 * 1024, "LDS budget of one workgroup");
+constexpr int kZlowBytes = C * kHeadDim * 2;  // low-rank gate: one z_low chunk
+static_assert(sizeof(PcSmem) + kDmaBytes + kZlowBytes <= 160 * 1024, "LDS budget of one workgroup");
 // 16-byte LDS accesses (DMA targets, float4 and bf16x8 reads)
 static_assert(offsetof(PcSmem, kb) % 16 == 0 && sizeof(KBuf) % 16 == 0 &&
                   offsetof(KBuf, qa) % 16 == 0 && offsetof(KBuf, eg15) % 16 == 0 &&
@@ -122,6 +127,12 @@ static_assert(offsetof(PcSmem, kb) % 16 == 0 && sizeof(KBuf) % 16 == 0 &&
                   offsetof(PcSmem, kp) % 16 == 0 && offsetof(PcSmem, km) % 16 == 0,
               "16-byte aligned LDS members");
 
+// kFb: the low-rank decay gate (z is z_low [T][128] and the pre-activation z_low f_b^T;
+// "Kimi Delta Attention (KDA) -- analysis & C kernel plan", "The KDA layer, precisely",
+// fact 2; the Retention-gate page's f_b_proj(f_a_proj(.))).  The two z waves then stream
+// the whole z_low chunk into buffers of their own and form the pre-activations of their 64
+// channels on MFMA, with f_b's rows fetched from L2 as operands; nothing else changes.
+template <bool kFb>
 __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder order, SplitPlan plan) {
   __shared__ PcSmem sm;
   // raw rows of q, k, v, z of the next chunk, as [plane][channel half][row][64]: producer
@@ -130,6 +141,10 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
   // raw output-gate rows, three buffers by chunk index mod 3: the epilogue reads chunk c's
   // in interval 3 of iteration c + 1, while chunk c + 2's arrives
   __shared__ __attribute__((aligned(16))) uint16_t graw_lds[3][C][kHeadDim];
+  // low-rank gate: the z_low rows of the chunk whose gate is formed next, 16-byte pieces
+  // XOR-swizzled by row (piece p of row r holds piece p ^ r) so that the MFMA operand
+  // reads of 16 rows hit distinct banks
+  __shared__ __attribute__((aligned(16))) uint16_t zlow_lds[kFb ? C : 1][kHeadDim];
 
   // This workgroup's (sequence n, head h) and tokens [t0, t0 + T): a whole sequence, or
   // segment kseg of nsegs (see the passes in kda_internal.h).
@@ -207,6 +222,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     const float ascale = expf(a.L.A_log[h]);
     const float ga = -kLog2e * ascale, gb = -kLog2e * ascale * a.L.dt_bias[c];
     const float lb2 = kLog2e * a.L.lower_bound;
+    if (kFb && urole == 3) sm.gbias[ch] = gb;
 
     // Raw rows of a chunk, straight into LDS.  Each wave fetches exactly the slice it reads
     // itself in interval 1 (plane urole, channels 64 hf .. + 63, all 16 rows) as two
@@ -229,10 +245,24 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     uint16_t braw = 0;  // raw beta of row t (threads t < C), one chunk ahead
     auto prefetch = [&](int c0n) __attribute__((always_inline)) {
       const int Ln = min(C, T - c0n);
+      if (kFb && urole == 3) {
+        // z_low rows 8 hf .. + 7 of the chunk: row 8 hf + 4 j + lane / 16, swizzled piece
+        // lane % 16
+        // (lane-dependent parts recomputed here rather than kept live across the loop)
+        const char* zb = pz + (t0 + c0n) * (kHeadDim * 2);
+        const int ln = opaque(lane);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int row = 8 * hf + 4 * j + (ln >> 4);
+          lds_dma16(zb + min(row, Ln - 1) * (kHeadDim * 2) + 16 * ((ln & 15) ^ row), &zlow_lds[8 * hf + 4 * j][0]);
+        }
+        return;
+      }
       const char* base = plane_base + (t0 + c0n) * Hd * 2;
+      const int slice = opaque(2 * urole + hf);  // recomputed here, not kept live across the loop
 #pragma unroll
       for (int k = 0; k < 2; ++k)
-        lds_dma16(base + min(8 * k + (lane >> 3), Ln - 1) * row_bytes, &raw_lds[urole][hf][8 * k][0]);
+        lds_dma16(base + min(8 * k + (lane >> 3), Ln - 1) * row_bytes, &raw_lds[slice >> 1][slice & 1][8 * k][0]);
       if (t < C) braw = x_b[(t0 + c0n + min(t, Ln - 1)) * H + h].bits;
     };
     auto prefetch_gate = [&](int c0n, int buf) __attribute__((always_inline)) {
@@ -245,11 +275,74 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       }
     };
 
+    // Low-rank gate of a chunk for channels 32 gq .. + 31 of this head, on the four gate
+    // waves (k and z, all otherwise idle in interval 3): per 16-channel tile,
+    // z^T = f_b[tile] z_low^T on four MFMAs, so lane (lm, lq) holds row lm of channels
+    // 4 lq + s; then g per element, the cumulative sum over the rows (the 16 lanes of a DPP
+    // row) and the per-channel factors, as the full-rank path.  Both tiles' f_b operands
+    // are fetched (from L2, buffer loads off one lane offset) before the first product.
+    // e^Gcum_end goes to eg15n: the chunk's KBuf is still the consumers' when this runs,
+    // and the z waves copy it over one interval later.
+    const bool gate_wave = kFb && (urole == 1 || urole == 3);
+    const int gq = (urole == 3 ? 2 : 0) + hf;
+    auto gate_low_rank = [&](int Ln) __attribute__((always_inline)) {
+      const __amdgpu_buffer_rsrc_t fbr =
+          buffer_rsrc(static_cast<const __bf16*>(a.L.f_b) + static_cast<int64_t>(h) * kHeadDim * kHeadDim,
+                      kHeadDim * kHeadDim * 2);
+      const int fvo = opaque(((32 * gq + lm) * kHeadDim + 8 * lq) * 2);
+      bf16x8_t fa[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          fa[u][kb] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(fbr, fvo, (16 * u * kHeadDim + 32 * kb) * 2, 0));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        f32x4_t zt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) zt = mma32(fa[u][kb], ld<bf16x8_t>(&zlow_lds[lm][8 * ((4 * kb + lq) ^ lm)]), zt);
+        const int cb = 32 * gq + 16 * u + 4 * lq;
+        const float4 g4 = ld<float4>(&sm.gbias[cb]);
+        const float gbv[4] = {g4.x, g4.y, g4.z, g4.w};
+        // lanes lm < 4 own channel cb + lm for the per-channel factors
+        float G[4], g7 = 0.f, g15 = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          float g = lb2 * frcp(1.0f + fexp2(fmaf(zt[s], ga, gbv[s])));
+          g = lm < Ln ? g : 0.f;
+          g += dpp_z<0x111>(g);  // inclusive prefix over the rows: row_shr 1, 2, 4, 8
+          g += dpp_z<0x112>(g);
+          g += dpp_z<0x114>(g);
+          g += dpp_z<0x118>(g);
+          G[s] = g;
+          const float b7 = row_bcast<C / 2 - 1>(g), b15 = row_bcast<C - 1>(g);
+          g7 = lm == s ? b7 : g7;
+          g15 = lm == s ? b15 : g15;
+        }
+        *reinterpret_cast<float4*>(&sm.gam[lm][opaque(cb)]) = make_float4(G[0], G[1], G[2], G[3]);
+        const float e15 = fexp2(g15), e7 = fexp2(g7), e157 = fexp2(g15 - g7);
+        if (lm < 4) {
+          const int cc = opaque(cb + lm);  // recomputed here, not kept live across the loop
+          sm.eg15n[cc] = e15;
+          sm.g7[cc] = g7;
+          sm.eg7[cc] = e7;
+          sm.e157[cc] = e157;
+        }
+      }
+    };
+
     if (T > 0) {
       prefetch(0);
       wait_vm();
     }
     lds_barrier();
+    // low-rank gate: the gate waves form chunk c's gate in interval 3 of iteration c - 2,
+    // the interval before the one in which the other producers build chunk c; chunk 0's
+    // here (the consumers keep the barrier count with a barrier of their own)
+    if (kFb) {
+      if (gate_wave && T > 0) gate_low_rank(min(C, T));
+      lds_barrier();
+    }
 
     // iteration i: producers build chunk i + 1
     for (int i = -1; i < nch; ++i) {
@@ -264,8 +357,10 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         // a sequence's last is full, and takes a path without per-row liveness tests so
         // that the rows' exp/rcp chains interleave.
         uint16_t xr[C];
+        if (!(kFb && urole == 3)) {
 #pragma unroll
-        for (int r = 0; r < C; ++r) xr[r] = raw_lds[urole][hf][r][lane];
+          for (int r = 0; r < C; ++r) xr[r] = raw_lds[urole][hf][r][lane];
+        }
         const bool full = Ln == C;
         if (urole == 2 && transfer_m) {
           // the transfer matrix is the end state from the identity with v = 0
@@ -297,6 +392,12 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
               dst[r][ch] = live ? ys * frcp(1.0f + fexp2(ys)) : 0.f;
             }
           }
+        } else if (kFb) {
+          // this chunk's gate was formed one interval 3 earlier (or before the loop); the
+          // z_low rows of chunk i + 2 are fetched now and waited for at the end of interval 2
+          const int cc = opaque(ch);  // recomputed here, not kept live across the loop
+          KN.eg15[cc] = sm.eg15n[cc];
+          if (i + 2 < nch) prefetch((i + 2) * C);
         } else {
           float G = 0.f, G7 = 0.f;
           if (full) {
@@ -323,7 +424,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         if (t < C) KN.beta[t] = (t < Ln) ? fsigmoid(bf16_to_f32(braw)) : 0.f;
         // this wave's raw slice is consumed: refill it with chunk i + 2 (the reads are
         // complete before the transfer is issued)
-        if (i + 2 < nch) {
+        if (i + 2 < nch && !(kFb && urole == 3)) {
           lds_wait();
           prefetch((i + 2) * C);
         }
@@ -380,6 +481,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           split_store2(&KN.klt[c4 + v][il16(r)], &KN.klt[c4 + v][il16(r) + 4], &KN.klt[c4 + v + 1][il16(r)],
                        &KN.klt[c4 + v + 1][il16(r) + 4], kl[v], kl[v + 1]);
       }
+      if (kFb && urole == 3) wait_vm();  // z_low of chunk i + 2, read in interval 3
       lds_barrier();
 
       // ---------------------------------------------------------- interval 3
@@ -413,7 +515,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           }
         }
       }
-      if (uwave == kNormWave) {
+      if (uwave == (kFb ? kNormWaveFb : kNormWave)) {
         const int r = lane & (C - 1);
         if (lane < 2 * C) {
           if (has_next) {
@@ -428,12 +530,13 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
               const float4 v4 = ld<float4>(&ns[r][g]);
               tot += (v4.x + v4.y) + (v4.z + v4.w);
             }
-            const float den = tot + (kCs * kCs) * a.L.l2_eps;
+            // |a|'^2 = |kCs a|^2 / kCs^2 + eps
+            const float den = fmaf(tot, kLn2 * kLn2, a.L.l2_eps);
             if (kk) {
-              KN.vk[r] = __builtin_amdgcn_sqrtf(den) * kLn2;
-              KN.beta[r] = KN.beta[r] * frcp(den);
+              KN.vk[r] = __builtin_amdgcn_sqrtf(den);
+              KN.beta[r] = KN.beta[r] * frcp(den) * (kLn2 * kLn2);
             } else {
-              KN.rq[r] = __builtin_amdgcn_rsqf(den) * -kQScale;
+              KN.rq[r] = __builtin_amdgcn_rsqf(den) * (-kQScale * kLn2);
             }
           }
         } else if (lane < 3 * C) {
@@ -449,6 +552,9 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           }
         }
       }
+      // low-rank gate of chunk i + 2 (the readers of gam and of the per-channel factors of
+      // chunk i + 1 ran in interval 2)
+      if (gate_wave && i + 2 < nch) gate_low_rank(min(C, T - (i + 2) * C));
       // this wave's transfers (raw rows of chunk i + 2, output gate of chunk i + 1) are
       // in LDS before the barrier that publishes them
       wait_vm();
@@ -485,6 +591,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         for (int s = 0; s < 4; ++s) S[it][s] = (transfer_m && 16 * it + 4 * lq + s == col) ? 1.f : 0.f;
     }
     lds_barrier();
+    if (kFb) lds_barrier();  // the producers' low-rank gate of chunk 0
 
     const float nw = a.L.norm_w[col];
     bf16x8_t u_l0 = {}, u_hh = {};  // U as the B operands of mma16p
@@ -645,7 +752,10 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, const int32_t* order_host, 
   PrefillArgs w = a;
   w.pass = kPassWhole;
   const dim3 grid(static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.L.H));
-  hipLaunchKernelGGL(prefill_pc_kernel, grid, dim3(NT), 0, stream, w, ord, none);
+  if (a.L.f_b)
+    hipLaunchKernelGGL(prefill_pc_kernel<true>, grid, dim3(NT), 0, stream, w, ord, none);
+  else
+    hipLaunchKernelGGL(prefill_pc_kernel<false>, grid, dim3(NT), 0, stream, w, ord, none);
   return hipGetLastError();
 }
 
@@ -715,7 +825,8 @@ hipError_t launch_prefill_bf16_split(const PrefillArgs& a, const SplitPlan& plan
   const unsigned H = static_cast<unsigned>(a.L.H);
   PrefillArgs w = a;
   w.pass = kPassTransfer;
-  hipLaunchKernelGGL(prefill_pc_kernel, dim3(2u * plan.nseg * H), dim3(NT), 0, stream, w, none, plan);
+  const auto pass = a.L.f_b ? prefill_pc_kernel<true> : prefill_pc_kernel<false>;
+  hipLaunchKernelGGL(pass, dim3(2u * plan.nseg * H), dim3(NT), 0, stream, w, none, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(a.num_seqs) * H * (kHeadDim / 16)),
@@ -723,7 +834,7 @@ hipError_t launch_prefill_bf16_split(const PrefillArgs& a, const SplitPlan& plan
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   w.pass = kPassFinal;
-  hipLaunchKernelGGL(prefill_pc_kernel, dim3(plan.nseg * H), dim3(NT), 0, stream, w, none, plan);
+  hipLaunchKernelGGL(pass, dim3(plan.nseg * H), dim3(NT), 0, stream, w, none, plan);
   return hipGetLastError();
 }
 

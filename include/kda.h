@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 typedef enum {
   KDA_OK = 0,
@@ -82,6 +82,16 @@ typedef enum {
  * lower_bound is the gate's lower bound (-5 in the pages' models); l2_eps the q/k L2
  * epsilon (1e-6); rms_eps the output RMSNorm epsilon; gate_kind selects the decay-gate
  * formula (kda_gate_kind).
+ *
+ * f_b selects the low-rank decay gate ("Kimi Delta Attention (KDA) -- analysis & C kernel
+ * plan", "The KDA layer, precisely", fact 2: hidden -> head_dim -> H * head_dim; the
+ * Retention-gate page: g = f_b_proj(f_a_proj(hidden)), a 7,168 -> 128 -> 12,288 pair).
+ * NULL: the z argument of every entry point is the full pre-activation [rows][H * d].
+ * Otherwise f_b is the second projection's weight, [H * d][d] row-major in the io dtype
+ * (device memory, 16-byte aligned, owned by the caller), the z argument is the rank-d
+ * input z_low [rows][d] (io dtype), and the pre-activation of channel c is
+ * sum_r z_low[row][r] * f_b[c][r], accumulated in fp32.  The full-rank z plane then never
+ * passes through memory.  With fp32 io, kda_prefill runs the sequential scan for it.
  */
 typedef struct kda_layer {
   int32_t num_heads;
@@ -95,6 +105,7 @@ typedef struct kda_layer {
   const float* A_log;
   const float* norm_w;
   int32_t gate_kind;   /* kda_gate_kind */
+  const void* f_b;     /* NULL, or the low-rank gate's [H * d][d] weight (io dtype) */
 } kda_layer;
 
 /*
@@ -114,7 +125,8 @@ size_t kda_prefill_workspace_bytes(const kda_layer* layer, kda_dtype io, int32_t
  *   cu_seqlens_dev / cu_seqlens_host  int32 [num_seqs + 1], the same offsets in device and
  *       host memory, non-decreasing, starting at 0 and ending at total_tokens.  Empty
  *       sequences are allowed (their state and ring pass through unchanged).
- *   q, k, v, z, gate  [total_tokens][H * d] io;  beta [total_tokens][H] io (raw, pre-sigmoid)
+ *   q, k, v, z, gate  [total_tokens][H * d] io (z: [total_tokens][d] with layer->f_b);
+ *                     beta [total_tokens][H] io (raw, pre-sigmoid)
  *   state_in  fp32 [num_seqs][H][d][d] or NULL (zero initial state)
  *   ring_in   fp32 [num_seqs][3 * H * d][kernel - 1] or NULL (zero history)
  *   out       [total_tokens][H * d] io

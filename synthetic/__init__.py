@@ -14,11 +14,16 @@ Workloads (all head_dim 128, short-conv kernel 4, lower bound -5):
   initial state ~ N(0, 0.02) and ring ~ N(0, 1), then 32 decode steps;
 * ``short256x64_h32``     -- 256 prompts x 64 tokens, 32 heads, bf16 io, carried state and
   ring: the short-prompt case on which the chunked and the sequential-scan prefill are
-  compared.
+  compared;
+* ``prefill_2x8192_h96_lowrank`` -- ``prefill_2x8192_h96`` with the low-rank decay gate:
+  z_low [T, 128] and f_b [96*128, 128] in place of the full-rank z.
 
 Distributions: raw q/k/v, decay pre-activation z and output-gate pre-activation ~ N(0, 1);
 raw beta ~ N(0, 1); conv weights ~ U(-0.5, 0.5); dt_bias ~ N(0, 0.1); A_log = log U(1, 16)
-per head; RMSNorm weight = 1 + N(0, 0.02).  N(0, s) means standard deviation s.  Values
+per head; RMSNorm weight = 1 + N(0, 0.02).  With the low-rank decay gate, z_low ~ N(0, 1)
+and f_b ~ N(0, 128^-1/2), so that the gate's pre-activation z_low f_b^T keeps unit
+variance; they take z's place in the draw order and f_b is drawn last.  N(0, s) means
+standard deviation s.  Values
 are drawn in fp32 by torch's generator on the requested device and rounded once (round to
 nearest even) to the io dtype.
 """
@@ -48,6 +53,7 @@ class Workload:
     init_ring: bool = False
     decode_after: int = 0          # decode steps that continue a prefill
     seed: int = 0
+    low_rank_gate: bool = False    # z_low [T, 128] and f_b [H*128, 128] instead of z
 
     @property
     def total_tokens(self) -> int:
@@ -72,6 +78,8 @@ WORKLOADS = {
     # reference's configurations)
     "short256x64_h32": Workload("short256x64_h32", "prefill", "bf16", 32, [64] * 256,
                                 init_state=True, init_ring=True, seed=20265),
+    "prefill_2x8192_h96_lowrank": Workload("prefill_2x8192_h96_lowrank", "prefill", "bf16", 96,
+                                           [8192, 8192], seed=20266, low_rank_gate=True),
 }
 
 
@@ -98,13 +106,15 @@ def layer_params(H: int, g: torch.Generator, device="cpu", d: int = HEAD_DIM,
 
 
 def activations(T: int, H: int, io: str, g: torch.Generator, device="cpu", d: int = HEAD_DIM,
-                lead=()) -> dict:
-    """Raw q, k, v, z, gate [*lead, T, H*d] and raw beta [*lead, T, H] ~ N(0, 1) in io dtype."""
+                lead=(), low_rank_gate: bool = False) -> dict:
+    """Raw q, k, v, z, gate [*lead, T, H*d] and raw beta [*lead, T, H] ~ N(0, 1) in io dtype;
+    with the low-rank gate z is z_low [*lead, T, d]."""
     dt = torch_io_dtype(io)
     shp = tuple(lead) + (T, H * d)
     out = {}
     for name in ("q", "k", "v", "z", "gate"):
-        out[name] = torch.randn(shp, generator=g, device=device).to(dt)
+        s = tuple(lead) + (T, d) if (name == "z" and low_rank_gate) else shp
+        out[name] = torch.randn(s, generator=g, device=device).to(dt)
     out["beta"] = torch.randn(tuple(lead) + (T, H), generator=g, device=device).to(dt)
     return out
 
@@ -126,28 +136,39 @@ def cu_seqlens(seqlens) -> torch.Tensor:
     return torch.tensor(cu, dtype=torch.int32)
 
 
+def low_rank_weight(H: int, io: str, g: torch.Generator, device="cpu", d: int = HEAD_DIM):
+    """f_b [H*d, d] ~ N(0, d^-1/2) in the io dtype."""
+    return (torch.randn(H * d, d, generator=g, device=device) * d ** -0.5).to(torch_io_dtype(io))
+
+
 def make_prefill(seqlens, H: int, io: str, seed: int, device="cpu", init_state=False,
-                 init_ring=False, d: int = HEAD_DIM) -> dict:
-    """A packed varlen prefill problem.  Draw order: layer params, activations, state, ring."""
+                 init_ring=False, d: int = HEAD_DIM, low_rank_gate: bool = False) -> dict:
+    """A packed varlen prefill problem.  Draw order: layer params, activations, state, ring,
+    then f_b with the low-rank gate (layer["f_b"]; z is then z_low [T, d])."""
     g = gen(seed, device)
     p = layer_params(H, g, device, d)
     T = int(sum(seqlens))
-    a = activations(T, H, io, g, device, d)
+    a = activations(T, H, io, g, device, d, low_rank_gate=low_rank_gate)
     N = len(seqlens)
     st = initial_state(N, H, g, device, d) if init_state else None
     rg = initial_ring(N, H, g, device, d) if init_ring else None
+    if low_rank_gate:
+        p["f_b"] = low_rank_weight(H, io, g, device, d)
     return dict(layer=p, io=io, seqlens=list(map(int, seqlens)), cu_seqlens=cu_seqlens(seqlens),
                 state_in=st, ring_in=rg, **a)
 
 
 def make_decode(B: int, H: int, io: str, steps: int, seed: int, device="cpu",
-                d: int = HEAD_DIM) -> dict:
-    """A decode problem: params, per-step activations [steps, B, ...], state, ring."""
+                d: int = HEAD_DIM, low_rank_gate: bool = False) -> dict:
+    """A decode problem: params, per-step activations [steps, B, ...], state, ring (then
+    f_b with the low-rank gate)."""
     g = gen(seed, device)
     p = layer_params(H, g, device, d)
-    a = activations(B, H, io, g, device, d, lead=(steps,))
+    a = activations(B, H, io, g, device, d, lead=(steps,), low_rank_gate=low_rank_gate)
     st = initial_state(B, H, g, device, d)
     rg = initial_ring(B, H, g, device, d)
+    if low_rank_gate:
+        p["f_b"] = low_rank_weight(H, io, g, device, d)
     return dict(layer=p, io=io, batch=B, steps=steps, state=st, ring=rg, **a)
 
 
@@ -155,4 +176,5 @@ def make_workload(name: str, device="cpu") -> dict:
     w = WORKLOADS[name]
     if w.kind == "decode":
         return make_decode(w.batch, w.heads, w.io, w.steps, w.seed, device)
-    return make_prefill(w.seqlens, w.heads, w.io, w.seed, device, w.init_state, w.init_ring)
+    return make_prefill(w.seqlens, w.heads, w.io, w.seed, device, w.init_state, w.init_ring,
+                        low_rank_gate=w.low_rank_gate)

@@ -23,12 +23,14 @@ def head_layer(params: dict, h: int) -> oracle.Layer:
     Hd = H * D
     cw = _cpu(params["conv_w"]).numpy()
     rows = np.concatenate([cw[p * Hd + h * D:p * Hd + (h + 1) * D] for p in range(3)])
+    f_b = params.get("f_b")
     return oracle.Layer(1, D, conv_w=rows,
                         dt_bias=_cpu(params["dt_bias"]).numpy()[h * D:(h + 1) * D],
                         A_log=_cpu(params["A_log"]).numpy()[h:h + 1],
                         norm_w=_cpu(params["norm_w"]).numpy(),
                         lower_bound=params["lower_bound"], l2_eps=params["l2_eps"],
-                        rms_eps=params["rms_eps"], gate_kind=params.get("gate_kind", 0))
+                        rms_eps=params["rms_eps"], gate_kind=params.get("gate_kind", 0),
+                        f_b=None if f_b is None else _cpu(f_b[h * D:(h + 1) * D]).contiguous())
 
 
 def io_code(dtype) -> int:
@@ -42,7 +44,10 @@ def unit_inputs(prob: dict, n: int, h: int):
     Hd = H * D
     lo, hi = cu[n], cu[n + 1]
     cols = slice(h * D, (h + 1) * D)
-    acts = {name: _cpu(prob[name][lo:hi, cols]).contiguous() for name in ("q", "k", "v", "z", "gate")}
+    acts = {name: _cpu(prob[name][lo:hi, cols]).contiguous() for name in ("q", "k", "v", "gate")}
+    # the low-rank gate's z_low is shared by every head
+    low_rank = prob["layer"].get("f_b") is not None
+    acts["z"] = _cpu(prob["z"][lo:hi] if low_rank else prob["z"][lo:hi, cols]).contiguous()
     acts["beta"] = _cpu(prob["beta"][lo:hi, h:h + 1]).contiguous()
     st = None if prob.get("state_in") is None else _cpu(prob["state_in"][n, h]).double().numpy()[None, None]
     rg = None
@@ -78,7 +83,9 @@ def decode_as_prefill(dec: dict, steps: int, b: int, h: int) -> dict:
     H = dec["layer"]["num_heads"]
     Hd = H * D
     cols = slice(h * D, (h + 1) * D)
-    prob = {name: _cpu(dec[name][:steps, b, cols]) for name in ("q", "k", "v", "z", "gate")}
+    prob = {name: _cpu(dec[name][:steps, b, cols]) for name in ("q", "k", "v", "gate")}
+    low_rank = dec["layer"].get("f_b") is not None
+    prob["z"] = _cpu(dec["z"][:steps, b] if low_rank else dec["z"][:steps, b, cols])
     prob["beta"] = _cpu(dec["beta"][:steps, b, h:h + 1])
     prob["state_in"] = _cpu(dec["state"][b:b + 1, h:h + 1])
     r = _cpu(dec["ring"][b]).numpy()
@@ -89,7 +96,8 @@ def decode_as_prefill(dec: dict, steps: int, b: int, h: int) -> dict:
     prob["layer"] = dict(num_heads=1, conv_w=torch.from_numpy(lay.conv_w),
                          dt_bias=torch.from_numpy(lay.dt_bias), A_log=torch.from_numpy(lay.A_log),
                          norm_w=torch.from_numpy(lay.norm_w), lower_bound=lay.lower_bound,
-                         l2_eps=lay.l2_eps, rms_eps=lay.rms_eps, gate_kind=lay.gate_kind)
+                         l2_eps=lay.l2_eps, rms_eps=lay.rms_eps, gate_kind=lay.gate_kind,
+                         f_b=lay.f_b)
     return prob
 
 
