@@ -52,10 +52,10 @@ constexpr int kElimCwA = 2;  // consumer waves PW + 2 and PW + 3, on SIMDs 2 and
 constexpr int kElimCwB = 3;
 constexpr int kGramAWave = 4;
 constexpr int kGramPWave = 5;
-// Producer wave that forms the row norms and the RMSNorm row factors; with the low-rank
-// gate the k and z waves form the gate in interval 3, and a q wave (SIMD 1) takes it.
+// Producer wave that forms the row norms and the RMSNorm row factors (also with the
+// low-rank gate, where every producer wave forms a tile of the gate in interval 3).
 constexpr int kNormWave = 6;
-constexpr int kNormWaveFb = 1;
+constexpr int kNormWaveFb = 6;
 constexpr int NT = 64 * (PW + CWN);
 constexpr int LDP = 132;               // fp32 row stride of [16][128] arrays
 constexpr int OPP = 136;               // bf16 row stride of [16][128] operands
@@ -111,7 +111,7 @@ struct alignas(16) PcSmem {
 // loads in flight cannot alias the other LDS data, and does not wait for them before
 // every LDS read.
 constexpr int kDmaBytes = (4 + 3) * C * kHeadDim * 2;
-constexpr int kZlowBytes = C * kHeadDim * 2;  // low-rank gate: one z_low chunk
+constexpr int kZlowBytes = 2 * C * kHeadDim * 2;  // low-rank gate: two z_low chunks
 static_assert(sizeof(PcSmem) + kDmaBytes + kZlowBytes <= 160 * 1024, "LDS budget of one workgroup");
 // 16-byte LDS accesses (DMA targets, float4 and bf16x8 reads)
 static_assert(offsetof(PcSmem, kb) % 16 == 0 && sizeof(KBuf) % 16 == 0 &&
@@ -141,10 +141,10 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
   // raw output-gate rows, three buffers by chunk index mod 3: the epilogue reads chunk c's
   // in interval 3 of iteration c + 1, while chunk c + 2's arrives
   __shared__ __attribute__((aligned(16))) uint16_t graw_lds[3][C][kHeadDim];
-  // low-rank gate: the z_low rows of the chunk whose gate is formed next, 16-byte pieces
-  // XOR-swizzled by row (piece p of row r holds piece p ^ r) so that the MFMA operand
-  // reads of 16 rows hit distinct banks
-  __shared__ __attribute__((aligned(16))) uint16_t zlow_lds[kFb ? C : 1][kHeadDim];
+  // low-rank gate: the z_low rows of a chunk, by chunk parity, 16-byte pieces XOR-swizzled
+  // by row (piece p of row r holds piece p ^ r) so that the MFMA operand reads of 16 rows
+  // hit distinct banks
+  __shared__ __attribute__((aligned(16))) uint16_t zlow_lds[kFb ? 2 : 1][kFb ? C : 1][kHeadDim];
 
   // This workgroup's (sequence n, head h) and tokens [t0, t0 + T): a whole sequence, or
   // segment kseg of nsegs (see the passes in kda_internal.h).
@@ -245,19 +245,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     uint16_t braw = 0;  // raw beta of row t (threads t < C), one chunk ahead
     auto prefetch = [&](int c0n) __attribute__((always_inline)) {
       const int Ln = min(C, T - c0n);
-      if (kFb && urole == 3) {
-        // z_low rows 8 hf .. + 7 of the chunk: row 8 hf + 4 j + lane / 16, swizzled piece
-        // lane % 16
-        // (lane-dependent parts recomputed here rather than kept live across the loop)
-        const char* zb = pz + (t0 + c0n) * (kHeadDim * 2);
-        const int ln = opaque(lane);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int row = 8 * hf + 4 * j + (ln >> 4);
-          lds_dma16(zb + min(row, Ln - 1) * (kHeadDim * 2) + 16 * ((ln & 15) ^ row), &zlow_lds[8 * hf + 4 * j][0]);
-        }
-        return;
-      }
+      if (kFb && urole == 3) return;  // the z plane is z_low, fetched by prefetch_zlow
       const char* base = plane_base + (t0 + c0n) * Hd * 2;
       const int slice = opaque(2 * urole + hf);  // recomputed here, not kept live across the loop
 #pragma unroll
@@ -275,72 +263,93 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       }
     };
 
-    // Low-rank gate of a chunk for channels 32 gq .. + 31 of this head, on the four gate
-    // waves (k and z, all otherwise idle in interval 3): per 16-channel tile,
-    // z^T = f_b[tile] z_low^T on four MFMAs, so lane (lm, lq) holds row lm of channels
-    // 4 lq + s; then g per element, the cumulative sum over the rows (the 16 lanes of a DPP
-    // row) and the per-channel factors, as the full-rank path.  Both tiles' f_b operands
-    // are fetched (from L2, buffer loads off one lane offset) before the first product.
-    // e^Gcum_end goes to eg15n: the chunk's KBuf is still the consumers' when this runs,
-    // and the z waves copy it over one interval later.
-    const bool gate_wave = kFb && (urole == 1 || urole == 3);
-    const int gq = (urole == 3 ? 2 : 0) + hf;
-    auto gate_low_rank = [&](int Ln) __attribute__((always_inline)) {
+    // low-rank gate: z_low rows 8 hf .. + 7 of chunk c0n / C into its parity's buffer (the q
+    // waves, at the end of their interval 1 like their own rows): row 8 hf + 4 j + lane / 16,
+    // swizzled piece lane % 16 (lane-dependent parts recomputed here rather than kept live
+    // across the loop)
+    auto prefetch_zlow = [&](int c0n) __attribute__((always_inline)) {
+      const int Ln = min(C, T - c0n);
+      const char* zb = pz + (t0 + c0n) * (kHeadDim * 2);
+      const int ln = opaque(lane);
+      const int buf = (c0n / C) & 1;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = 8 * hf + 4 * j + (ln >> 4);
+        lds_dma16(zb + min(row, Ln - 1) * (kHeadDim * 2) + 16 * ((ln & 15) ^ row), &zlow_lds[buf][8 * hf + 4 * j][0]);
+      }
+    };
+
+    // Low-rank gate of a chunk for channels 16 w .. + 15 of this head on producer wave w
+    // (interval 3, beside the Gram tiles and the norms): the tile z^T = f_b[tile] z_low^T on
+    // four MFMAs, so lane (lm, lq) holds row lm of channels 4 lq + s, with the f_b operands
+    // fetched from L2 by buffer loads off one lane offset; then g per element, the
+    // cumulative sum over the rows (the 16 lanes of a DPP row) and the per-channel factors,
+    // as the full-rank path.  e^Gcum_end goes to eg15n: the chunk's KBuf is still the
+    // consumers' when this runs, and the z waves copy it over one interval later.
+    const bool gate_wave = kFb;
+    auto gate_fetch = [&](bf16x8_t* fa) __attribute__((always_inline)) {
       const __amdgpu_buffer_rsrc_t fbr =
           buffer_rsrc(static_cast<const __bf16*>(a.L.f_b) + static_cast<int64_t>(h) * kHeadDim * kHeadDim,
                       kHeadDim * kHeadDim * 2);
-      const int fvo = opaque(((32 * gq + lm) * kHeadDim + 8 * lq) * 2);
-      bf16x8_t fa[2][4];
+      const int fvo = opaque(((16 * uwave + lm) * kHeadDim + 8 * lq) * 2);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int kb = 0; kb < 4; ++kb)
+        fa[kb] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(fbr, fvo, 32 * kb * 2, 0));
+    };
+    auto gate_low_rank = [&](int cidx, const bf16x8_t* fa) __attribute__((always_inline)) {
+      const int Ln = min(C, T - cidx * C);
+      const uint16_t(*zl)[kHeadDim] = zlow_lds[cidx & 1];
+      f32x4_t zt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          fa[u][kb] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(fbr, fvo, (16 * u * kHeadDim + 32 * kb) * 2, 0));
+      for (int kb = 0; kb < 4; ++kb) zt = mma32(fa[kb], ld<bf16x8_t>(&zl[lm][8 * ((4 * kb + lq) ^ lm)]), zt);
+      const int cb = 16 * uwave + 4 * lq;
+      const float4 g4 = ld<float4>(&sm.gbias[cb]);
+      const float gbv[4] = {g4.x, g4.y, g4.z, g4.w};
+      // lanes lm < 4 own channel cb + lm for the per-channel factors
+      float G[4], g7 = 0.f, g15 = 0.f;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        f32x4_t zt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) zt = mma32(fa[u][kb], ld<bf16x8_t>(&zlow_lds[lm][8 * ((4 * kb + lq) ^ lm)]), zt);
-        const int cb = 32 * gq + 16 * u + 4 * lq;
-        const float4 g4 = ld<float4>(&sm.gbias[cb]);
-        const float gbv[4] = {g4.x, g4.y, g4.z, g4.w};
-        // lanes lm < 4 own channel cb + lm for the per-channel factors
-        float G[4], g7 = 0.f, g15 = 0.f;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          float g = lb2 * frcp(1.0f + fexp2(fmaf(zt[s], ga, gbv[s])));
-          g = lm < Ln ? g : 0.f;
-          g += dpp_z<0x111>(g);  // inclusive prefix over the rows: row_shr 1, 2, 4, 8
-          g += dpp_z<0x112>(g);
-          g += dpp_z<0x114>(g);
-          g += dpp_z<0x118>(g);
-          G[s] = g;
-          const float b7 = row_bcast<C / 2 - 1>(g), b15 = row_bcast<C - 1>(g);
-          g7 = lm == s ? b7 : g7;
-          g15 = lm == s ? b15 : g15;
-        }
-        *reinterpret_cast<float4*>(&sm.gam[lm][opaque(cb)]) = make_float4(G[0], G[1], G[2], G[3]);
-        const float e15 = fexp2(g15), e7 = fexp2(g7), e157 = fexp2(g15 - g7);
-        if (lm < 4) {
-          const int cc = opaque(cb + lm);  // recomputed here, not kept live across the loop
-          sm.eg15n[cc] = e15;
-          sm.g7[cc] = g7;
-          sm.eg7[cc] = e7;
-          sm.e157[cc] = e157;
-        }
+      for (int s = 0; s < 4; ++s) {
+        float g = lb2 * frcp(1.0f + fexp2(fmaf(zt[s], ga, gbv[s])));
+        g = lm < Ln ? g : 0.f;
+        g += dpp_z<0x111>(g);  // inclusive prefix over the rows: row_shr 1, 2, 4, 8
+        g += dpp_z<0x112>(g);
+        g += dpp_z<0x114>(g);
+        g += dpp_z<0x118>(g);
+        G[s] = g;
+        const float b7 = row_bcast<C / 2 - 1>(g), b15 = row_bcast<C - 1>(g);
+        g7 = lm == s ? b7 : g7;
+        g15 = lm == s ? b15 : g15;
+      }
+      *reinterpret_cast<float4*>(&sm.gam[lm][opaque(cb)]) = make_float4(G[0], G[1], G[2], G[3]);
+      const float e15 = fexp2(g15), e7 = fexp2(g7), e157 = fexp2(g15 - g7);
+      if (lm < 4) {
+        const int cc = opaque(cb + lm);  // recomputed here, not kept live across the loop
+        sm.eg15n[cc] = e15;
+        sm.g7[cc] = g7;
+        sm.eg7[cc] = e7;
+        sm.e157[cc] = e157;
       }
     };
 
     if (T > 0) {
       prefetch(0);
+      if (kFb && urole == 0) {
+        prefetch_zlow(0);
+        if (nch > 1) prefetch_zlow(C);
+      }
       wait_vm();
     }
     lds_barrier();
     // low-rank gate: the gate waves form chunk c's gate in interval 3 of iteration c - 2,
-    // the interval before the one in which the other producers build chunk c; chunk 0's
-    // here (the consumers keep the barrier count with a barrier of their own)
+    // the interval before the one in which the other producers build chunk c, from z_low
+    // rows fetched in interval 1 of iteration c - 3; chunk 0's here (the consumers keep the
+    // barrier count with a barrier of their own)
     if (kFb) {
-      if (gate_wave && T > 0) gate_low_rank(min(C, T));
+      if (gate_wave && T > 0) {
+        bf16x8_t fa[4];
+        gate_fetch(fa);
+        gate_low_rank(0, fa);
+      }
       lds_barrier();
     }
 
@@ -393,11 +402,9 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
             }
           }
         } else if (kFb) {
-          // this chunk's gate was formed one interval 3 earlier (or before the loop); the
-          // z_low rows of chunk i + 2 are fetched now and waited for at the end of interval 2
+          // this chunk's gate was formed one interval 3 earlier (or before the loop)
           const int cc = opaque(ch);  // recomputed here, not kept live across the loop
           KN.eg15[cc] = sm.eg15n[cc];
-          if (i + 2 < nch) prefetch((i + 2) * C);
         } else {
           float G = 0.f, G7 = 0.f;
           if (full) {
@@ -428,6 +435,10 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           lds_wait();
           prefetch((i + 2) * C);
         }
+        // low-rank gate: chunk i + 3's z_low rows (their buffer's chunk i + 1 was read in the
+        // previous interval 3), waited for with this wave's other transfers
+        if (kFb && urole == 0 && i + 3 < nch) prefetch_zlow((i + 3) * C);
+
       }
       lds_barrier();
 
@@ -481,7 +492,6 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           split_store2(&KN.klt[c4 + v][il16(r)], &KN.klt[c4 + v][il16(r) + 4], &KN.klt[c4 + v + 1][il16(r)],
                        &KN.klt[c4 + v + 1][il16(r) + 4], kl[v], kl[v + 1]);
       }
-      if (kFb && urole == 3) wait_vm();  // z_low of chunk i + 2, read in interval 3
       lds_barrier();
 
       // ---------------------------------------------------------- interval 3
@@ -554,7 +564,11 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       }
       // low-rank gate of chunk i + 2 (the readers of gam and of the per-channel factors of
       // chunk i + 1 ran in interval 2)
-      if (gate_wave && i + 2 < nch) gate_low_rank(min(C, T - (i + 2) * C));
+      if (gate_wave && i + 2 < nch) {
+        bf16x8_t fa[4];
+        gate_fetch(fa);
+        gate_low_rank(i + 2, fa);
+      }
       // this wave's transfers (raw rows of chunk i + 2, output gate of chunk i + 1) are
       // in LDS before the barrier that publishes them
       wait_vm();
