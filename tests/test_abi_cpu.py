@@ -157,3 +157,20 @@ def test_prefill_scan_validation():
     assert scan([0, 5], 5, q=0) == 1           # null activation
     assert scan([0, 5], 5, q=FAKE + 2) == 1    # misaligned activation
     assert lib.kda_prefill_scan(ctypes.byref(lay), 1, 0, None, None, 0, *([None] * 11), None) == 0
+
+
+def test_low_rank_gate_validation():
+    """kda_layer.f_b (ABI 5): NULL keeps the full-rank gate; a misaligned weight is rejected
+    by every entry point before any launch; the layer struct carries it after gate_kind."""
+    kda, lib = _lib()
+    assert kda._binding.KdaLayerC.f_b.offset > kda._binding.KdaLayerC.gate_kind.offset
+    lay = _layer(kda)
+    assert lay.f_b is None
+    lay.f_b = FAKE + 2
+    assert _decode(lib, lay) == 1
+    assert b"f_b" in lib.kda_last_error()
+    assert _multi(lib, lay) == 1
+    assert _prefill(lib, lay, [0, 4], 4) == 1
+    lay.f_b = FAKE
+    assert _decode(lib, lay, batch=0) == 0
+    assert _prefill(lib, lay, [0, 5, 3], 3) == 1  # the other checks still apply
