@@ -27,6 +27,9 @@
 //     partial sums of squares (interval 2); then the gated RMSNorm epilogue of chunk
 //     c-1's rows and S <- Diag(e^Gcum_C) S + Kl^T U (interval 3).
 //
+// With the low-rank decay gate (kFb below) every producer wave also forms one 16-channel
+// tile of chunk c+2's gate in interval 3.
+//
 // Operands that cross from producers to consumers are double-buffered by chunk parity.
 // Three LDS barriers per chunk.  With 16 waves per workgroup each SIMD holds two producer
 // and two consumer waves, so the VALU-heavy and MFMA-heavy halves hide each other's
@@ -55,7 +58,6 @@ constexpr int kGramPWave = 5;
 // Producer wave that forms the row norms and the RMSNorm row factors (also with the
 // low-rank gate, where every producer wave forms a tile of the gate in interval 3).
 constexpr int kNormWave = 6;
-constexpr int kNormWaveFb = 6;
 constexpr int NT = 64 * (PW + CWN);
 constexpr int LDP = 132;               // fp32 row stride of [16][128] arrays
 constexpr int OPP = 136;               // bf16 row stride of [16][128] operands
@@ -124,14 +126,17 @@ static_assert(offsetof(PcSmem, kb) % 16 == 0 && sizeof(KBuf) % 16 == 0 &&
                   offsetof(PcSmem, g7) % 16 == 0 && offsetof(PcSmem, qp) % 16 == 0 &&
                   offsetof(PcSmem, nsq) % 16 == 0 && offsetof(KBuf, beta) % 16 == 0 &&
                   offsetof(KBuf, vk) % 16 == 0 && offsetof(KBuf, rq) % 16 == 0 &&
-                  offsetof(PcSmem, kp) % 16 == 0 && offsetof(PcSmem, km) % 16 == 0,
+                  offsetof(PcSmem, kp) % 16 == 0 && offsetof(PcSmem, km) % 16 == 0 &&
+                  offsetof(PcSmem, rr) % 16 == 0 && offsetof(PcSmem, gbias) % 16 == 0,
               "16-byte aligned LDS members");
 
 // kFb: the low-rank decay gate (z is z_low [T][128] and the pre-activation z_low f_b^T;
 // "Kimi Delta Attention (KDA) -- analysis & C kernel plan", "The KDA layer, precisely",
-// fact 2; the Retention-gate page's f_b_proj(f_a_proj(.))).  The two z waves then stream
-// the whole z_low chunk into buffers of their own and form the pre-activations of their 64
-// channels on MFMA, with f_b's rows fetched from L2 as operands; nothing else changes.
+// fact 2; the Retention-gate page's f_b_proj(f_a_proj(.))).  The q waves then also copy
+// z_low rows into a buffer by chunk parity, three chunks ahead, in place of the z waves'
+// raw z rows; every producer wave forms one 16-channel tile of a chunk's gate on MFMA in
+// interval 3 two chunks ahead, with its f_b rows fetched from L2 as operands; and the z
+// waves only move the chunk's e^Gcum_end into its buffer.  The rest is unchanged.
 template <bool kFb>
 __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder order, SplitPlan plan) {
   __shared__ PcSmem sm;
@@ -525,7 +530,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           }
         }
       }
-      if (uwave == (kFb ? kNormWaveFb : kNormWave)) {
+      if (uwave == kNormWave) {
         const int r = lane & (C - 1);
         if (lane < 2 * C) {
           if (has_next) {
