@@ -82,10 +82,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     n = a.ntok ? min(max(a.ntok[b], 0), a.tokens) : a.tokens;
   }
 
-  __shared__ float a_q[kHeadDim], a_k[kHeadDim], a_v[kHeadDim], eg[kHeadDim], sg[kHeadDim];
+  // the token's vectors; the output gate by token parity, since the last readers of a
+  // token's gate run while the next token's prologue writes
+  __shared__ float a_q[kHeadDim], a_k[kHeadDim], a_v[kHeadDim], eg[kHeadDim], sg[2][kHeadDim];
   __shared__ float dlt[kHeadDim];
   __shared__ float part[2][3];
-  __shared__ float red[4][2][kHeadDim];
+  // each half-wave's partial sums of u and w over its 16 key rows
+  __shared__ float red[8][2][kHeadDim];
   __shared__ float part2[2];
 
   const IO* x_q = static_cast<const IO*>(a.q);
@@ -161,7 +164,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int p = 0; p < 2; ++p) {  // planes q, k
         const float x = xs[p];
-        const float* w = a.L.conv_w + (p * Hd + c) * kConvTaps;  // re-read per token (L2)
+        // re-read per token (L2): held in registers they cost the one-token step 5%
+        const float* w = a.L.conv_w + (p * Hd + c) * kConvTaps;
         const float y = w[3] * x + w[0] * hist[p][0] + w[1] * hist[p][1] + w[2] * hist[p][2];
         hist[p][0] = hist[p][1];
         hist[p][1] = hist[p][2];
@@ -189,15 +193,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const float zv = f_b ? low_rank_z(x_z + (row0 + tok) * kHeadDim, f_b + c * kHeadDim) : io_to_f32(xb);
       const float g = a.L.gate_kind == KDA_GATE_SOFTPLUS ? kda_gate_softplus(zv, dtb, ascale)
                                                          : kda_gate(zv, dtb, ascale, a.L.lower_bound);
-      eg[i] = expf(g);
-      sg[i] = sigmoidf_(io_to_f32(xc));
+      eg[i] = exp_fast(g);
+      sg[tok & 1][i] = sigmoidf_(io_to_f32(xc));
     }
     if (tok + 1 < n) fetch(tok + 1);
     __syncthreads();
 
     // 3. decay the state and form both GEMVs, u = S'^T k-hat and w = S'^T q-hat
-    const float rq = 1.0f / sqrtf(part[0][0] + part[1][0] + a.L.l2_eps) * 0.08838834764831845f;
-    const float rk = 1.0f / sqrtf(part[0][1] + part[1][1] + a.L.l2_eps);
+    const float rq = __builtin_amdgcn_rsqf(part[0][0] + part[1][0] + a.L.l2_eps) * 0.08838834764831845f;
+    const float rk = __builtin_amdgcn_rsqf(part[0][1] + part[1][1] + a.L.l2_eps);
     const float qk = (part[0][2] + part[1][2]) * rq * rk;  // k-hat . q-hat
     float kh[16];
     float u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f, w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
@@ -220,26 +224,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       w2 += s[m].z * qh;
       w3 += s[m].w * qh;
     }
-    u0 += __shfl_xor(u0, 32, 64);
-    u1 += __shfl_xor(u1, 32, 64);
-    u2 += __shfl_xor(u2, 32, 64);
-    u3 += __shfl_xor(u3, 32, 64);
-    w0 += __shfl_xor(w0, 32, 64);
-    w1 += __shfl_xor(w1, 32, 64);
-    w2 += __shfl_xor(w2, 32, 64);
-    w3 += __shfl_xor(w3, 32, 64);
-    if ((t & 32) == 0) {
-      *reinterpret_cast<float4*>(&red[wave][0][cg * 4]) = make_float4(u0, u1, u2, u3);
-      *reinterpret_cast<float4*>(&red[wave][1][cg * 4]) = make_float4(w0, w1, w2, w3);
-    }
+    // the two halves of a wave hold different rows of the same columns: both partial sums
+    // go to LDS, which is cheaper than combining them through lane exchanges first
+    *reinterpret_cast<float4*>(&red[rg][0][cg * 4]) = make_float4(u0, u1, u2, u3);
+    *reinterpret_cast<float4*>(&red[rg][1][cg * 4]) = make_float4(w0, w1, w2, w3);
     __syncthreads();
 
     // 4. delta and the readout for column j = t
     float o = 0.f;
     if (t < kHeadDim) {
       const int j = t;
-      const float uj = red[0][0][j] + red[1][0][j] + red[2][0][j] + red[3][0][j];
-      const float wj = red[0][1][j] + red[1][1][j] + red[2][1][j] + red[3][1][j];
+      const float uj = ((red[0][0][j] + red[1][0][j]) + (red[2][0][j] + red[3][0][j])) +
+                       ((red[4][0][j] + red[5][0][j]) + (red[6][0][j] + red[7][0][j]));
+      const float wj = ((red[0][1][j] + red[1][1][j]) + (red[2][1][j] + red[3][1][j])) +
+                       ((red[4][1][j] + red[5][1][j]) + (red[6][1][j] + red[7][1][j]));
       const float d = beta * (a_v[j] - uj);
       dlt[j] = d;
       o = wj + qk * d;
@@ -264,11 +262,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
     if (t < kHeadDim && a.out) {
       const int j = t;
-      const float r = 1.0f / sqrtf((part2[0] + part2[1]) * (1.0f / kHeadDim) + a.L.rms_eps);
+      const float r = __builtin_amdgcn_rsqf((part2[0] + part2[1]) * (1.0f / kHeadDim) + a.L.rms_eps);
       store_io(static_cast<IO*>(a.out), xrow + static_cast<int64_t>(h) * kHeadDim + j,
-               nw * o * r * sg[j]);
+               nw * o * r * sg[tok & 1][j]);
     }
-    if (tok + 1 < n) __syncthreads();  // the next token rewrites the LDS rows read above
+    // Three barriers per token, none here: the next token's prologue writes a_q, a_k,
+    // a_v, eg and part, all read before this token's last barrier, and the other parity
+    // of sg; red, dlt and part2 are rewritten only after the next token's first barrier.
   }
 
   // 6. no token: the state passes through; then the conv history

@@ -80,8 +80,13 @@ __device__ __forceinline__ void store_streaming(float4* p, const float4& v) {
   __builtin_nontemporal_store(x, reinterpret_cast<f32x4_nt*>(p));
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
-__device__ __forceinline__ float siluf_(float x) { return x / (1.0f + expf(-x)); }
+// e^x, sigmoid and SiLU on the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32, about
+// 1 ulp each): e^x = 2^(x log2 e), whose relative error grows as |x| 6e-8 from the rounding
+// of the product (under 2e-6 for |x| < 30); e^x reaches 0 and inf where fp32 does, so the
+// sigmoid and SiLU go to their limits.
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + exp_fast(-x)); }
+__device__ __forceinline__ float siluf_(float x) { return x * __builtin_amdgcn_rcpf(1.0f + exp_fast(-x)); }
 
 // Lower-bounded per-channel log decay: lb * sigmoid(exp(A_log) * (z + dt_bias)).
 __device__ __forceinline__ float kda_gate(float z, float dt_bias, float a_scale, float lb) {
@@ -95,19 +100,33 @@ __device__ __forceinline__ float kda_gate_softplus(float z, float dt_bias, float
   return -a_scale * (x > 20.f ? x + log1pf(expf(-x)) : log1pf(expf(x)));
 }
 
-// Sum over the 64 lanes of a wave; every lane receives the total.
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+// Inclusive prefix sum over each 16-lane DPP row: row_shr 1, 2, 4, 8 with zero fill for
+// the lanes whose source lies before the row.  Lane 15 of a row ends with the row's total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_shr_zero(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_prefix16(float x) {
+  x += dpp_shr_zero<0x111>(x);
+  x += dpp_shr_zero<0x112>(x);
+  x += dpp_shr_zero<0x114>(x);
+  x += dpp_shr_zero<0x118>(x);
   return x;
 }
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
 
-// Sum over aligned groups of `W` consecutive lanes (W a power of two <= 64).
-template <int W>
-__device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int m = W / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-  return x;
+// Sum over the 64 lanes of a wave (all active); every lane receives the total.
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row_prefix16(x);
+  return (lane_value(x, 15) + lane_value(x, 31)) + (lane_value(x, 47) + lane_value(x, 63));
+}
+
+// Sum over lanes 0 .. 31 of a wave (active); every lane receives the total.
+__device__ __forceinline__ float half_wave_sum(float x) {
+  x = row_prefix16(x);
+  return lane_value(x, 15) + lane_value(x, 31);
 }
 
 }  // namespace kda
