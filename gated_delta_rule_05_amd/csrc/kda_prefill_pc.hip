@@ -130,6 +130,34 @@ static_assert(offsetof(PcSmem, kb) % 16 == 0 && sizeof(KBuf) % 16 == 0 &&
                   offsetof(PcSmem, rr) % 16 == 0 && offsetof(PcSmem, gbias) % 16 == 0,
               "16-byte aligned LDS members");
 
+// Softplus gate: the Gram operands of one level, bf16 hi and lo, 24 rows each (the level's
+// earlier-half rows Y, then its later-half rows as Xk, then as Xq), stored where the bounded
+// gate keeps Qp, Kp and Km (the same 26 KB).
+struct LevelOps {
+  __bf16 h[3 * C / 2][OPP];
+  __bf16 l[3 * C / 2][OPP];
+};
+static_assert(offsetof(PcSmem, kp) == offsetof(PcSmem, qp) + sizeof(PcSmem::qp) &&
+                  offsetof(PcSmem, km) == offsetof(PcSmem, kp) + sizeof(PcSmem::kp) &&
+                  2 * sizeof(LevelOps) == 3 * sizeof(PcSmem::qp) && offsetof(PcSmem, qp) % 16 == 0,
+              "the two levels' operands fill Qp, Kp and Km exactly");
+__device__ __forceinline__ LevelOps* level_ops(PcSmem& sm) {
+  return reinterpret_cast<LevelOps*>(&sm.qp[0][0][0]);
+}
+
+// The softplus gate's per-token log2 decay, log2 e g = -e^A_log log2 e softplus(z + dt_bias),
+// with u = (z + dt_bias) log2 e (spb = dt_bias log2 e): log2 e softplus = max(u, 0) +
+// log2(1 + 2^-|u|).  The log2 of w = 1 + e is corrected for the rounding of the sum,
+// log2(1 + e) = log2 w + (e - (w - 1)) / (w ln 2), so small decays keep their relative
+// precision.
+__device__ __forceinline__ float softplus_gate2(float z, float spb, float ascale) {
+  const float u = fmaf(z, kLog2e, spb);
+  const float e = fexp2(-fabsf(u));
+  const float w = 1.0f + e;
+  const float l2 = __builtin_amdgcn_logf(w) + (e - (w - 1.0f)) * frcp(w) * kLog2e;
+  return -ascale * (fmaxf(u, 0.f) + l2);
+}
+
 // kFb: the low-rank decay gate (z is z_low [T][128] and the pre-activation z_low f_b^T;
 // "Kimi Delta Attention (KDA) -- analysis & C kernel plan", "The KDA layer, precisely",
 // fact 2; the Retention-gate page's f_b_proj(f_a_proj(.))).  The q waves then also copy
@@ -137,8 +165,22 @@ static_assert(offsetof(PcSmem, kb) % 16 == 0 && sizeof(KBuf) % 16 == 0 &&
 // raw z rows; every producer wave forms one 16-channel tile of a chunk's gate on MFMA in
 // interval 3 two chunks ahead, with its f_b rows fetched from L2 as operands; and the z
 // waves only move the chunk's e^Gcum_end into its buffer.  The rest is unchanged.
-template <bool kFb>
+//
+// kSp: the unbounded softplus decay gate, g = -e^A_log softplus(z + dt_bias) (Kimi-Linear's
+// gate, "Kimi Delta Attention (KDA) -- analysis & C kernel plan", status note).  Without a
+// lower bound the in-chunk decay range of a channel is unbounded, so the Gram tiles cannot
+// take one reference row (OpenModelAtlas "Kimi K3 - Retention gate", "Why": the unbounded
+// form needs position pairs on the diagonal tiles).  Here every pair i > j of a chunk is
+// formed relative to a boundary row that lies between them, so that both factors
+// x_i 2^(Gcum_i - Gcum_b) and k_j 2^(Gcum_b - Gcum_j) are at most |x_i| and |k_j|:
+//   level 1, rows 8..15 against rows 0..7, boundary row 7 (MFMA);
+//   level 2, rows 4..7 against 0..3 and 12..15 against 8..11, boundary rows 3 and 11 (MFMA);
+//   the pairs inside aligned groups of four rows and P's diagonal, one exponential per pair
+//   and channel on the vector ALU (interval 2, all producer waves).
+// Qa, Ka and Kl take their factors directly (2^Gcum, 2^(Gcum_end - Gcum), both <= 1).
+template <bool kFb, bool kSp>
 __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder order, SplitPlan plan) {
+  static_assert(!(kFb && kSp), "the low-rank gate is built for the bounded gate only");
   __shared__ PcSmem sm;
   // raw rows of q, k, v, z of the next chunk, as [plane][channel half][row][64]: producer
   // wave w reads and refills slice [w / 2][w % 2] only
@@ -150,6 +192,9 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
   // by row (piece p of row r holds piece p ^ r) so that the MFMA operand reads of 16 rows
   // hit distinct banks
   __shared__ __attribute__((aligned(16))) uint16_t zlow_lds[kFb ? 2 : 1][kFb ? C : 1][kHeadDim];
+  // softplus gate: per row i, the in-group pair sums over two halves of the channels,
+  // [G(i, i-1), G(i, i-2), G(i, i-3), P(i, i-1), P(i, i-2), P(i, i-3), P(i, i), -]
+  __shared__ __attribute__((aligned(16))) float pair_lds[kSp ? C : 1][2][8];
 
   // This workgroup's (sequence n, head h) and tokens [t0, t0 + T): a whole sequence, or
   // segment kseg of nsegs (see the passes in kda_internal.h).
@@ -227,6 +272,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     const float ascale = expf(a.L.A_log[h]);
     const float ga = -kLog2e * ascale, gb = -kLog2e * ascale * a.L.dt_bias[c];
     const float lb2 = kLog2e * a.L.lower_bound;
+    const float spb = kLog2e * a.L.dt_bias[c];  // softplus gate: (z + dt_bias) log2 e = z log2 e + spb
     if (kFb && urole == 3) sm.gbias[ch] = gb;
 
     // Raw rows of a chunk, straight into LDS.  Each wave fetches exactly the slice it reads
@@ -411,11 +457,16 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           const int cc = opaque(ch);  // recomputed here, not kept live across the loop
           KN.eg15[cc] = sm.eg15n[cc];
         } else {
+          // the per-token log2 decay of either gate
+          auto gate2 = [&](uint16_t xz) __attribute__((always_inline)) {
+            return kSp ? softplus_gate2(bf16_to_f32(xz), spb, ascale)
+                       : lb2 * frcp(1.0f + fexp2(fmaf(bf16_to_f32(xz), ga, gb)));
+          };
           float G = 0.f, G7 = 0.f;
           if (full) {
 #pragma unroll
             for (int r = 0; r < C; ++r) {
-              G += lb2 * frcp(1.0f + fexp2(fmaf(bf16_to_f32(xr[r]), ga, gb)));
+              G += gate2(xr[r]);
               sm.gam[r][ch] = G;
               if (r == C / 2 - 1) G7 = G;
             }
@@ -423,15 +474,17 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 #pragma unroll
             for (int r = 0; r < C; ++r) {
               const bool live = r < Ln;
-              G += live ? lb2 * frcp(1.0f + fexp2(fmaf(bf16_to_f32(xr[r]), ga, gb))) : 0.f;
+              G += live ? gate2(xr[r]) : 0.f;
               sm.gam[r][ch] = G;
               if (r == C / 2 - 1) G7 = G;
             }
           }
-          sm.g7[ch] = G7;
           KN.eg15[ch] = fexp2(G);
-          sm.eg7[ch] = fexp2(G7);
-          sm.e157[ch] = fexp2(G - G7);
+          if (!kSp) {
+            sm.g7[ch] = G7;
+            sm.eg7[ch] = fexp2(G7);
+            sm.e157[ch] = fexp2(G - G7);
+          }
         }
         if (t < C) KN.beta[t] = (t < Ln) ? fsigmoid(bf16_to_f32(braw)) : 0.f;
         // this wave's raw slice is consumed: refill it with chunk i + 2 (the reads are
@@ -461,32 +514,108 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         const float4 qv = ld<float4>(&sm.aq[r][c4]);
         const float4 kv = ld<float4>(&sm.ak[r][c4]);
         const float4 gv = ld<float4>(&sm.gam[r][c4]);
-        const float4 g7 = ld<float4>(&sm.g7[c4]);
-        const float4 e7 = ld<float4>(&sm.eg7[c4]);
-        const float4 e157 = ld<float4>(&sm.e157[c4]);
         const float q4[4] = {qv.x, qv.y, qv.z, qv.w};
         const float k4[4] = {kv.x, kv.y, kv.z, kv.w};
-        const float d4[4] = {gv.x - g7.x, gv.y - g7.y, gv.z - g7.z, gv.w - g7.w};
-        const float m7[4] = {e7.x, e7.y, e7.z, e7.w};
-        const float m157[4] = {e157.x, e157.y, e157.z, e157.w};
-        float qp[4], kp[4], km[4], qa[4], ka[4], kl[4], sq = 0.f, sk = 0.f;
+        float qa[4], ka[4], kl[4], sq = 0.f, sk = 0.f;
+        if constexpr (kSp) {
+          // Qa, Ka and Kl from 2^Gcum and 2^(Gcum_end - Gcum); the level operands of the
+          // Gram tiles (see the kernel's kSp note): at level l a row r in the later half of
+          // its block (of 16 or 8 rows) gives Xk = a_k 2^(Gcum - Gcum_b) and Xq = a_q 2^(.)
+          // (rows 8 + x and 16 + x of the level's [24] operand rows), a row in the earlier
+          // half Y = a_k 2^(Gcum_b - Gcum) (row x), with b the block's boundary row and x the
+          // row's index among the level's later or earlier rows
+          const float4 ge = ld<float4>(&sm.gam[C - 1][c4]);
+          const float4 b1 = ld<float4>(&sm.gam[C / 2 - 1][c4]);
+          const float4 b2 = ld<float4>(&sm.gam[(r & 8) + 3][c4]);
+          const float gr[4] = {gv.x, gv.y, gv.z, gv.w}, gend[4] = {ge.x, ge.y, ge.z, ge.w};
+          const float gb1[4] = {b1.x, b1.y, b1.z, b1.w}, gb2[4] = {b2.x, b2.y, b2.z, b2.w};
+          const bool late1 = r >= 8, late2 = (r & 4) != 0;
+          float x1k[4], x1q[4], x2k[4], x2q[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float el = fexp2(d4[v]), er = fexp2(-d4[v]);
-          qp[v] = q4[v] * el;
-          kp[v] = k4[v] * el;
-          km[v] = k4[v] * er;
-          qa[v] = qp[v] * m7[v];
-          ka[v] = kp[v] * m7[v];
-          kl[v] = km[v] * m157[v];
-          sq = fmaf(q4[v], q4[v], sq);
-          sk = fmaf(k4[v], k4[v], sk);
+          for (int v = 0; v < 4; ++v) {
+            const float e = fexp2(gr[v]);
+            qa[v] = q4[v] * e;
+            ka[v] = k4[v] * e;
+            kl[v] = k4[v] * fexp2(gend[v] - gr[v]);
+            const float f1 = fexp2(late1 ? gr[v] - gb1[v] : gb1[v] - gr[v]);
+            const float f2 = fexp2(late2 ? gr[v] - gb2[v] : gb2[v] - gr[v]);
+            x1k[v] = k4[v] * f1;
+            x1q[v] = q4[v] * f1;
+            x2k[v] = k4[v] * f2;
+            x2q[v] = q4[v] * f2;
+            sq = fmaf(q4[v], q4[v], sq);
+            sk = fmaf(k4[v], k4[v], sk);
+          }
+          LevelOps& L1 = level_ops(sm)[0];
+          LevelOps& L2 = level_ops(sm)[1];
+          const int x1 = r & 7, x2 = ((r >> 3) << 2) + (r & 3);
+          store4(&L1.h[late1 ? 8 + x1 : x1][c4], &L1.l[late1 ? 8 + x1 : x1][c4], x1k);
+          store4(&L2.h[late2 ? 8 + x2 : x2][c4], &L2.l[late2 ? 8 + x2 : x2][c4], x2k);
+          if (late1) store4(&L1.h[16 + x1][c4], &L1.l[16 + x1][c4], x1q);
+          if (late2) store4(&L2.h[16 + x2][c4], &L2.l[16 + x2][c4], x2q);
+          // The pairs inside each aligned group of four rows, and P's diagonal: row pr,
+          // channels pc .. pc + 3 per thread (two 16-lane DPP rows per row of the chunk),
+          // summed over the DPP row and stored per half of the channels.
+          {
+            const int pr = t >> 5, pc = 4 * (t & 31);
+            const float4 pq = ld<float4>(&sm.aq[pr][pc]);
+            const float4 pk = ld<float4>(&sm.ak[pr][pc]);
+            const float4 pg = ld<float4>(&sm.gam[pr][pc]);
+            const float qi[4] = {pq.x, pq.y, pq.z, pq.w}, ki[4] = {pk.x, pk.y, pk.z, pk.w};
+            const float gi[4] = {pg.x, pg.y, pg.z, pg.w};
+            float ps[7];
+            ps[6] = (qi[0] * ki[0] + qi[1] * ki[1]) + (qi[2] * ki[2] + qi[3] * ki[3]);
+#pragma unroll
+            for (int jj = 1; jj <= 3; ++jj) {
+              const bool ok = (pr & 3) >= jj;  // row pr - jj is in pr's group of four
+              const int j = ok ? pr - jj : pr;
+              const float4 kj4 = ld<float4>(&sm.ak[j][pc]);
+              const float4 gj4 = ld<float4>(&sm.gam[j][pc]);
+              const float kj[4] = {kj4.x, kj4.y, kj4.z, kj4.w}, gj[4] = {gj4.x, gj4.y, gj4.z, gj4.w};
+              float sg = 0.f, sp = 0.f;
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const float kf = kj[v] * fexp2(gi[v] - gj[v]);  // 2^(Gcum_i - Gcum_j) <= 1
+                sg = fmaf(ki[v], kf, sg);
+                sp = fmaf(qi[v], kf, sp);
+              }
+              ps[jj - 1] = ok ? sg : 0.f;
+              ps[2 + jj] = ok ? sp : 0.f;
+            }
+#pragma unroll
+            for (int x = 0; x < 7; ++x) ps[x] = row_sum16(ps[x]);
+            if ((lane & 15) == 0) {
+              float* dst = &pair_lds[pr][(lane >> 4) & 1][0];
+              *reinterpret_cast<float4*>(dst) = make_float4(ps[0], ps[1], ps[2], ps[3]);
+              *reinterpret_cast<float4*>(dst + 4) = make_float4(ps[4], ps[5], ps[6], 0.f);
+            }
+          }
+        } else {
+          const float4 g7 = ld<float4>(&sm.g7[c4]);
+          const float4 e7 = ld<float4>(&sm.eg7[c4]);
+          const float4 e157 = ld<float4>(&sm.e157[c4]);
+          const float d4[4] = {gv.x - g7.x, gv.y - g7.y, gv.z - g7.z, gv.w - g7.w};
+          const float m7[4] = {e7.x, e7.y, e7.z, e7.w};
+          const float m157[4] = {e157.x, e157.y, e157.z, e157.w};
+          float qp[4], kp[4], km[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float el = fexp2(d4[v]), er = fexp2(-d4[v]);
+            qp[v] = q4[v] * el;
+            kp[v] = k4[v] * el;
+            km[v] = k4[v] * er;
+            qa[v] = qp[v] * m7[v];
+            ka[v] = kp[v] * m7[v];
+            kl[v] = km[v] * m157[v];
+            sq = fmaf(q4[v], q4[v], sq);
+            sk = fmaf(k4[v], k4[v], sk);
+          }
+          store4(&sm.qp[0][r][c4], &sm.qp[1][r][c4], qp);
+          store4(&sm.kp[0][r][c4], &sm.kp[1][r][c4], kp);
+          store4(&sm.km[0][r][c4], &sm.km[1][r][c4], km);
         }
         sm.nsq[0][r][t >> 4] = sq;
         sm.nsq[1][r][t >> 4] = sk;
-        store4(&sm.qp[0][r][c4], &sm.qp[1][r][c4], qp);
-        store4(&sm.kp[0][r][c4], &sm.kp[1][r][c4], kp);
-        store4(&sm.km[0][r][c4], &sm.km[1][r][c4], km);
         // Qa and Ka in the key order of the .S products: channels 32 kb + 4 m .. + 3 sit
         // at 32 kb + 8 (m % 4) + 4 (m / 4)
         const int pa = 32 * (c4 >> 5) + 8 * ((c4 >> 2) & 3) + 4 * ((c4 >> 4) & 1);
@@ -505,19 +634,59 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         // Gram tiles of chunk i + 1: G = Kp Km^T (strict lower; the elimination of consumer
         // waves kElimCwA/B in the next interval 1 scales its rows by beta') and
         // P = Qp Km^T (lower incl.)
-        const __bf16(*Xh)[OPP] = gram_a ? sm.kp[0] : sm.qp[0];
-        const __bf16(*Xl)[OPP] = gram_a ? sm.kp[1] : sm.qp[1];
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (kSp) {
+          // levels 1 and 2 as products of the level operands (lane row lm: Xk or Xq if lm is
+          // in the later half of its block, else Y), each kept where its level owns the
+          // pair; the in-group pairs and the diagonal from the interval-2 sums
+          f32x4_t lvl[2];
 #pragma unroll
-        for (int kb = 0; kb < kHeadDim / 32; ++kb) {
-          const int o = 32 * kb + 8 * lq;
-          const bf16x8_t xh = ld<bf16x8_t>(&Xh[lm][o]), xl = ld<bf16x8_t>(&Xl[lm][o]);
-          const bf16x8_t mh = ld<bf16x8_t>(&sm.km[0][lm][o]), ml = ld<bf16x8_t>(&sm.km[1][lm][o]);
-          acc = mma32(xh, mh, acc);
-          a1 = mma32(xh, ml, a1);
-          a1 = mma32(xl, mh, a1);
+          for (int l = 0; l < 2; ++l) {
+            const LevelOps& L = level_ops(sm)[l];
+            const bool late = (lm & (8 >> l)) != 0;
+            const int x = l == 0 ? (lm & 7) : ((lm >> 3) << 2) + (lm & 3);
+            const int ra = late ? (gram_a ? 8 : 16) + x : x, rb = late ? 8 + x : x;
+            f32x4_t x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < kHeadDim / 32; ++kb) {
+              const int o = 32 * kb + 8 * lq;
+              const bf16x8_t xh = ld<bf16x8_t>(&L.h[ra][o]), xl = ld<bf16x8_t>(&L.l[ra][o]);
+              const bf16x8_t mh = ld<bf16x8_t>(&L.h[rb][o]), ml = ld<bf16x8_t>(&L.l[rb][o]);
+              x0 = mma32(xh, mh, x0);
+              x1 = mma32(xh, ml, x1);
+              x1 = mma32(xl, mh, x1);
+            }
+            lvl[l] = x0 + x1;
+          }
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int ri = 4 * lq + s, d = ri ^ lm, jj = ri - lm;
+            float v = 0.f;
+            if (d >= 8) {
+              v = lvl[0][s];
+            } else if (d >= 4) {
+              v = lvl[1][s];
+            } else if (jj > 0 || (jj == 0 && !gram_a)) {
+              const int xi = gram_a ? jj - 1 : (jj == 0 ? 6 : 2 + jj);
+              v = pair_lds[ri][0][xi] + pair_lds[ri][1][xi];
+            }
+            acc[s] = v;
+          }
+        } else {
+          const __bf16(*Xh)[OPP] = gram_a ? sm.kp[0] : sm.qp[0];
+          const __bf16(*Xl)[OPP] = gram_a ? sm.kp[1] : sm.qp[1];
+          f32x4_t a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < kHeadDim / 32; ++kb) {
+            const int o = 32 * kb + 8 * lq;
+            const bf16x8_t xh = ld<bf16x8_t>(&Xh[lm][o]), xl = ld<bf16x8_t>(&Xl[lm][o]);
+            const bf16x8_t mh = ld<bf16x8_t>(&sm.km[0][lm][o]), ml = ld<bf16x8_t>(&sm.km[1][lm][o]);
+            acc = mma32(xh, mh, acc);
+            a1 = mma32(xh, ml, a1);
+            a1 = mma32(xl, mh, a1);
+          }
+          acc += a1;
         }
-        acc += a1;
         if (gram_a) {
 #pragma unroll
           for (int s = 0; s < 4; ++s) sm.A[4 * lq + s][lm] = (lm < 4 * lq + s) ? acc[s] : 0.f;
@@ -763,6 +932,14 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 
 }  // namespace
 
+// The kernel variant for the layer's decay gate (the low-rank gate is built for the
+// bounded gate; the launch sites route the other combinations to the scan).
+using PcKernel = void (*)(PrefillArgs, PcOrder, SplitPlan);
+static PcKernel pc_kernel_for(const PrefillArgs& a) {
+  if (a.L.gate_kind == KDA_GATE_SOFTPLUS) return prefill_pc_kernel<false, true>;
+  return a.L.f_b ? prefill_pc_kernel<true, false> : prefill_pc_kernel<false, false>;
+}
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, const int32_t* order_host, hipStream_t stream) {
   PcOrder ord;
   const int nord = a.num_seqs < kMaxOrdered ? a.num_seqs : kMaxOrdered;
@@ -771,10 +948,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, const int32_t* order_host, 
   PrefillArgs w = a;
   w.pass = kPassWhole;
   const dim3 grid(static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.L.H));
-  if (a.L.f_b)
-    hipLaunchKernelGGL(prefill_pc_kernel<true>, grid, dim3(NT), 0, stream, w, ord, none);
-  else
-    hipLaunchKernelGGL(prefill_pc_kernel<false>, grid, dim3(NT), 0, stream, w, ord, none);
+  hipLaunchKernelGGL(pc_kernel_for(a), grid, dim3(NT), 0, stream, w, ord, none);
   return hipGetLastError();
 }
 
@@ -844,7 +1018,7 @@ hipError_t launch_prefill_bf16_split(const PrefillArgs& a, const SplitPlan& plan
   const unsigned H = static_cast<unsigned>(a.L.H);
   PrefillArgs w = a;
   w.pass = kPassTransfer;
-  const auto pass = a.L.f_b ? prefill_pc_kernel<true> : prefill_pc_kernel<false>;
+  const auto pass = pc_kernel_for(a);
   hipLaunchKernelGGL(pass, dim3(2u * plan.nseg * H), dim3(NT), 0, stream, w, none, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

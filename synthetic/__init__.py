@@ -16,7 +16,11 @@ Workloads (all head_dim 128, short-conv kernel 4, lower bound -5):
   ring: the short-prompt case on which the chunked and the sequential-scan prefill are
   compared;
 * ``prefill_2x8192_h96_lowrank`` -- ``prefill_2x8192_h96`` with the low-rank decay gate:
-  z_low [T, 128] and f_b [96*128, 128] in place of the full-rank z.
+  z_low [T, 128] and f_b [96*128, 128] in place of the full-rank z;
+* ``prefill_2x8192_h96_softplus`` -- ``prefill_2x8192_h96`` with Kimi-Linear's unbounded
+  softplus decay gate (layer["gate_kind"] = GATE_SOFTPLUS, the ABI's value) in place of the
+  lower-bounded one; with A_log = log U(1, 16) and z ~ N(0, 1) a token's decay reaches
+  tens of nats, so a 16-token chunk spans up to several hundred.
 
 Distributions: raw q/k/v, decay pre-activation z and output-gate pre-activation ~ N(0, 1);
 raw beta ~ N(0, 1); conv weights ~ U(-0.5, 0.5); dt_bias ~ N(0, 0.1); A_log = log U(1, 16)
@@ -36,6 +40,7 @@ import torch
 HEAD_DIM = 128
 CONV_KERNEL = 4
 LOWER_BOUND = -5.0
+GATE_SOFTPLUS = 1  # kda_layer.gate_kind of the unbounded gate (include/kda.h)
 L2_EPS = 1e-6
 RMS_EPS = 1e-5
 
@@ -54,6 +59,7 @@ class Workload:
     decode_after: int = 0          # decode steps that continue a prefill
     seed: int = 0
     low_rank_gate: bool = False    # z_low [T, 128] and f_b [H*128, 128] instead of z
+    softplus_gate: bool = False    # the unbounded softplus decay gate
 
     @property
     def total_tokens(self) -> int:
@@ -80,6 +86,8 @@ WORKLOADS = {
                                 init_state=True, init_ring=True, seed=20265),
     "prefill_2x8192_h96_lowrank": Workload("prefill_2x8192_h96_lowrank", "prefill", "bf16", 96,
                                            [8192, 8192], seed=20266, low_rank_gate=True),
+    "prefill_2x8192_h96_softplus": Workload("prefill_2x8192_h96_softplus", "prefill", "bf16", 96,
+                                            [8192, 8192], seed=20267, softplus_gate=True),
 }
 
 
@@ -142,11 +150,15 @@ def low_rank_weight(H: int, io: str, g: torch.Generator, device="cpu", d: int = 
 
 
 def make_prefill(seqlens, H: int, io: str, seed: int, device="cpu", init_state=False,
-                 init_ring=False, d: int = HEAD_DIM, low_rank_gate: bool = False) -> dict:
+                 init_ring=False, d: int = HEAD_DIM, low_rank_gate: bool = False,
+                 softplus_gate: bool = False) -> dict:
     """A packed varlen prefill problem.  Draw order: layer params, activations, state, ring,
-    then f_b with the low-rank gate (layer["f_b"]; z is then z_low [T, d])."""
+    then f_b with the low-rank gate (layer["f_b"]; z is then z_low [T, d]).  The softplus
+    gate draws nothing of its own."""
     g = gen(seed, device)
     p = layer_params(H, g, device, d)
+    if softplus_gate:
+        p["gate_kind"] = GATE_SOFTPLUS
     T = int(sum(seqlens))
     a = activations(T, H, io, g, device, d, low_rank_gate=low_rank_gate)
     N = len(seqlens)
@@ -177,4 +189,4 @@ def make_workload(name: str, device="cpu") -> dict:
     if w.kind == "decode":
         return make_decode(w.batch, w.heads, w.io, w.steps, w.seed, device)
     return make_prefill(w.seqlens, w.heads, w.io, w.seed, device, w.init_state, w.init_ring,
-                        low_rank_gate=w.low_rank_gate)
+                        low_rank_gate=w.low_rank_gate, softplus_gate=w.softplus_gate)

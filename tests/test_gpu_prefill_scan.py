@@ -83,9 +83,9 @@ def test_scan_takes_any_lower_bound():
 
 
 def test_softplus_gate_prefill_and_decode():
-    """Kimi-Linear's unbounded gate g = -exp(A_log) softplus(z + dt_bias): kda_prefill runs
-    the scan for it (the chunked tile factors need the lower bound), equal bit for bit to
-    the explicit scan arm and to the oracle; decode steps continue from its states."""
+    """Kimi-Linear's unbounded gate g = -exp(A_log) softplus(z + dt_bias) with slow decay
+    (the state carried over many chunks): the chunked kda_prefill and the scan arm both
+    against the oracle, the same ring bits, and decode steps continuing from the states."""
     import gated_delta_rule_05_amd as kda
     from kda_testutil import assert_close, decode_as_prefill, oracle_units
     lens = [45, 3, 0, 60]
@@ -98,9 +98,9 @@ def test_softplus_gate_prefill_and_decode():
                          state_in=prob["state_in"], ring_in=prob["ring_in"])
     torch.cuda.synchronize()
     scan = _scan(prob)
-    for x, y in zip(res, scan):
-        assert torch.equal(x, y)
+    assert torch.equal(res[2], scan[2])
     _check(prob, res, _all_units(prob), "softplus_prefill")
+    _check(prob, scan, _all_units(prob), "softplus_scan")
     # decode from the returned states: 5 steps on 4 sequences, against the oracle run over
     # the decode tokens from those states (which the prefill check pinned)
     layer = kda.Layer(**prob["layer"])
