@@ -145,17 +145,13 @@ __device__ __forceinline__ LevelOps* level_ops(PcSmem& sm) {
   return reinterpret_cast<LevelOps*>(&sm.qp[0][0][0]);
 }
 
-// The softplus gate's per-token log2 decay, log2 e g = -e^A_log log2 e softplus(z + dt_bias),
-// with u = (z + dt_bias) log2 e (spb = dt_bias log2 e): log2 e softplus = max(u, 0) +
-// log2(1 + 2^-|u|).  The log2 of w = 1 + e is corrected for the rounding of the sum,
-// log2(1 + e) = log2 w + (e - (w - 1)) / (w ln 2), so small decays keep their relative
-// precision.
+// The softplus gate's per-token log2 decay, log2 e g = -e^A_log log2 e softplus(z + dt_bias):
+// with u = (z + dt_bias) log2 e (spb = dt_bias log2 e), log2 e softplus = log2(1 + 2^u),
+// one exp2 and one log2 (u beyond 24: u itself).  The absolute error stays near 1e-7 (the
+// rounding of 1 + 2^u), which is what the decay factors 2^Gcum see.
 __device__ __forceinline__ float softplus_gate2(float z, float spb, float ascale) {
   const float u = fmaf(z, kLog2e, spb);
-  const float e = fexp2(-fabsf(u));
-  const float w = 1.0f + e;
-  const float l2 = __builtin_amdgcn_logf(w) + (e - (w - 1.0f)) * frcp(w) * kLog2e;
-  return -ascale * (fmaxf(u, 0.f) + l2);
+  return -ascale * (u > 24.f ? u : __builtin_amdgcn_logf(1.0f + fexp2(u)));
 }
 
 // kFb: the low-rank decay gate (z is z_low [T][128] and the pre-activation z_low f_b^T;
@@ -176,7 +172,7 @@ __device__ __forceinline__ float softplus_gate2(float z, float spb, float ascale
 //   level 1, rows 8..15 against rows 0..7, boundary row 7 (MFMA);
 //   level 2, rows 4..7 against 0..3 and 12..15 against 8..11, boundary rows 3 and 11 (MFMA);
 //   the pairs inside aligned groups of four rows and P's diagonal, one exponential per pair
-//   and channel on the vector ALU (interval 2, all producer waves).
+//   and channel on the vector ALU (interval 3, on the four q and k waves).
 // Qa, Ka and Kl take their factors directly (2^Gcum, 2^(Gcum_end - Gcum), both <= 1).
 template <bool kFb, bool kSp>
 __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder order, SplitPlan plan) {
@@ -192,9 +188,6 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
   // by row (piece p of row r holds piece p ^ r) so that the MFMA operand reads of 16 rows
   // hit distinct banks
   __shared__ __attribute__((aligned(16))) uint16_t zlow_lds[kFb ? 2 : 1][kFb ? C : 1][kHeadDim];
-  // softplus gate: per row i, the in-group pair sums over two halves of the channels,
-  // [G(i, i-1), G(i, i-2), G(i, i-3), P(i, i-1), P(i, i-2), P(i, i-3), P(i, i), -]
-  __shared__ __attribute__((aligned(16))) float pair_lds[kSp ? C : 1][2][8];
 
   // This workgroup's (sequence n, head h) and tokens [t0, t0 + T): a whole sequence, or
   // segment kseg of nsegs (see the passes in kda_internal.h).
@@ -553,43 +546,6 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           store4(&L2.h[late2 ? 8 + x2 : x2][c4], &L2.l[late2 ? 8 + x2 : x2][c4], x2k);
           if (late1) store4(&L1.h[16 + x1][c4], &L1.l[16 + x1][c4], x1q);
           if (late2) store4(&L2.h[16 + x2][c4], &L2.l[16 + x2][c4], x2q);
-          // The pairs inside each aligned group of four rows, and P's diagonal: row pr,
-          // channels pc .. pc + 3 per thread (two 16-lane DPP rows per row of the chunk),
-          // summed over the DPP row and stored per half of the channels.
-          {
-            const int pr = t >> 5, pc = 4 * (t & 31);
-            const float4 pq = ld<float4>(&sm.aq[pr][pc]);
-            const float4 pk = ld<float4>(&sm.ak[pr][pc]);
-            const float4 pg = ld<float4>(&sm.gam[pr][pc]);
-            const float qi[4] = {pq.x, pq.y, pq.z, pq.w}, ki[4] = {pk.x, pk.y, pk.z, pk.w};
-            const float gi[4] = {pg.x, pg.y, pg.z, pg.w};
-            float ps[7];
-            ps[6] = (qi[0] * ki[0] + qi[1] * ki[1]) + (qi[2] * ki[2] + qi[3] * ki[3]);
-#pragma unroll
-            for (int jj = 1; jj <= 3; ++jj) {
-              const bool ok = (pr & 3) >= jj;  // row pr - jj is in pr's group of four
-              const int j = ok ? pr - jj : pr;
-              const float4 kj4 = ld<float4>(&sm.ak[j][pc]);
-              const float4 gj4 = ld<float4>(&sm.gam[j][pc]);
-              const float kj[4] = {kj4.x, kj4.y, kj4.z, kj4.w}, gj[4] = {gj4.x, gj4.y, gj4.z, gj4.w};
-              float sg = 0.f, sp = 0.f;
-#pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                const float kf = kj[v] * fexp2(gi[v] - gj[v]);  // 2^(Gcum_i - Gcum_j) <= 1
-                sg = fmaf(ki[v], kf, sg);
-                sp = fmaf(qi[v], kf, sp);
-              }
-              ps[jj - 1] = ok ? sg : 0.f;
-              ps[2 + jj] = ok ? sp : 0.f;
-            }
-#pragma unroll
-            for (int x = 0; x < 7; ++x) ps[x] = row_sum16(ps[x]);
-            if ((lane & 15) == 0) {
-              float* dst = &pair_lds[pr][(lane >> 4) & 1][0];
-              *reinterpret_cast<float4*>(dst) = make_float4(ps[0], ps[1], ps[2], ps[3]);
-              *reinterpret_cast<float4*>(dst + 4) = make_float4(ps[4], ps[5], ps[6], 0.f);
-            }
-          }
         } else {
           const float4 g7 = ld<float4>(&sm.g7[c4]);
           const float4 e7 = ld<float4>(&sm.eg7[c4]);
@@ -629,49 +585,99 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       lds_barrier();
 
       // ---------------------------------------------------------- interval 3
-      if (has_next && (uwave == kGramAWave || uwave == kGramPWave)) {
-        const bool gram_a = uwave == kGramAWave;
+      // softplus gate: the 4x4 diagonal blocks of chunk i + 1's G and P as position pairs,
+      // on four waves with no interval-3 job of their own.  Wave w takes rows 4w .. 4w + 3
+      // (local rows 0..3): the first half-wave the pairs (1,0), (2,0), (2,1) and P's diagonal
+      // at rows 0..2, the second the pairs (3,0), (3,1), (3,2) and the diagonal at row 3;
+      // lane l of a half takes channels 4 (l % 32) .. + 3.  A pair (a, b) costs one
+      // exponential 2^(Gcum_a - Gcum_b) <= 1 per channel.  The sums over the half's 32 lanes
+      // (DPP row sums, then the two rows) are written by its first 12 (rows 0..2) or 4
+      // (row 3) lanes, one entry of G and of P each.
+      if (kSp && has_next && uwave < 4) {
+        const int hh = lane >> 5, pc = 4 * (lane & 31), r0 = 4 * uwave;
+        float qv[4][4], kv[4][4], gv[4][4];
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const float4 q = ld<float4>(&sm.aq[r0 + a4][pc]), k = ld<float4>(&sm.ak[r0 + a4][pc]);
+          const float4 g = ld<float4>(&sm.gam[r0 + a4][pc]);
+          qv[a4][0] = q.x; qv[a4][1] = q.y; qv[a4][2] = q.z; qv[a4][3] = q.w;
+          kv[a4][0] = k.x; kv[a4][1] = k.y; kv[a4][2] = k.z; kv[a4][3] = k.w;
+          gv[a4][0] = g.x; gv[a4][1] = g.y; gv[a4][2] = g.z; gv[a4][3] = g.w;
+        }
+        float ps[9];  // G and P of the half's three pairs, then three diagonal entries
+#pragma unroll
+        for (int sl = 0; sl < 3; ++sl) {
+          // pair sl of this half: (2 - (sl == 0), sl == 2) in the first, (3, sl) in the second
+          const int ra = sl == 0 ? 1 : 2, rb = sl == 2 ? 1 : 0;
+          float sg = 0.f, sp = 0.f;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float ga = hh ? gv[3][v] : gv[ra][v], gb = hh ? gv[sl][v] : gv[rb][v];
+            const float kb = hh ? kv[sl][v] : kv[rb][v];
+            const float ka = hh ? kv[3][v] : kv[ra][v], qa = hh ? qv[3][v] : qv[ra][v];
+            const float kf = kb * fexp2(ga - gb);
+            sg = fmaf(ka, kf, sg);
+            sp = fmaf(qa, kf, sp);
+          }
+          ps[sl] = sg;
+          ps[3 + sl] = sp;
+        }
+#pragma unroll
+        for (int dg = 0; dg < 3; ++dg) {
+          const int ad = hh ? 3 : dg;
+          float sd = 0.f;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sd = fmaf(qv[ad][v], kv[ad][v], sd);
+          ps[6 + dg] = sd;
+        }
+#pragma unroll
+        for (int x = 0; x < 9; ++x) {
+          ps[x] = row_sum16(ps[x]);
+          ps[x] += __shfl_xor(ps[x], 16, 64);
+        }
+        const int cl = lane & 31;
+        if (cl < (hh ? 4 : 12)) {
+          const int a = hh ? 3 : cl >> 2, b = cl & 3;
+          // pair (a, b), b < a: its slot in this half
+          const int sl = hh ? b : (a == 1 ? 0 : 1 + b);
+          const float gsel = sl == 0 ? ps[0] : sl == 1 ? ps[1] : ps[2];
+          const float psel = sl == 0 ? ps[3] : sl == 1 ? ps[4] : ps[5];
+          const float dsel = hh ? ps[6] : (a == 0 ? ps[6] : a == 1 ? ps[7] : ps[8]);
+          const float gv_ = b < a ? gsel : 0.f;
+          const float pv_ = b < a ? psel : (b == a ? dsel : 0.f);
+          sm.A[r0 + a][r0 + b] = gv_;
+          split_store(&KN.p[r0 + a][il16(r0 + b)], &KN.p[r0 + a][il16(r0 + b) + 4], pv_);
+        }
+      }
+      // (softplus gate: level 1 of G and P on the Gram waves, level 2 on waves 7 and 6,
+      // so that each SIMD issues one level tile)
+      if (has_next && (uwave == kGramAWave || uwave == kGramPWave || (kSp && uwave >= 6))) {
+        const bool gram_a = uwave == kGramAWave || uwave == 7;
+        const int lv = kSp && uwave >= 6 ? 1 : 0;  // softplus gate: this wave's level
         // Gram tiles of chunk i + 1: G = Kp Km^T (strict lower; the elimination of consumer
         // waves kElimCwA/B in the next interval 1 scales its rows by beta') and
         // P = Qp Km^T (lower incl.)
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         if constexpr (kSp) {
-          // levels 1 and 2 as products of the level operands (lane row lm: Xk or Xq if lm is
-          // in the later half of its block, else Y), each kept where its level owns the
-          // pair; the in-group pairs and the diagonal from the interval-2 sums
-          f32x4_t lvl[2];
+          // level lv + 1 as the product of its operands (lane row lm: Xk or Xq if lm is in
+          // the later half of its block, else Y); a lane's rows 4 lq .. + 3 and column lm
+          // belong to level 1 if lm is in the other half of the 16 rows, to level 2 if in
+          // the other group of four of the same half, else to the pair waves
+          const LevelOps& L = level_ops(sm)[lv];
+          const bool late = (lm & (8 >> lv)) != 0;
+          const int x = lv == 0 ? (lm & 7) : ((lm >> 3) << 2) + (lm & 3);
+          const int ra = late ? (gram_a ? 8 : 16) + x : x, rb = late ? 8 + x : x;
+          f32x4_t x1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int l = 0; l < 2; ++l) {
-            const LevelOps& L = level_ops(sm)[l];
-            const bool late = (lm & (8 >> l)) != 0;
-            const int x = l == 0 ? (lm & 7) : ((lm >> 3) << 2) + (lm & 3);
-            const int ra = late ? (gram_a ? 8 : 16) + x : x, rb = late ? 8 + x : x;
-            f32x4_t x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < kHeadDim / 32; ++kb) {
-              const int o = 32 * kb + 8 * lq;
-              const bf16x8_t xh = ld<bf16x8_t>(&L.h[ra][o]), xl = ld<bf16x8_t>(&L.l[ra][o]);
-              const bf16x8_t mh = ld<bf16x8_t>(&L.h[rb][o]), ml = ld<bf16x8_t>(&L.l[rb][o]);
-              x0 = mma32(xh, mh, x0);
-              x1 = mma32(xh, ml, x1);
-              x1 = mma32(xl, mh, x1);
-            }
-            lvl[l] = x0 + x1;
+          for (int kb = 0; kb < kHeadDim / 32; ++kb) {
+            const int o = 32 * kb + 8 * lq;
+            const bf16x8_t xh = ld<bf16x8_t>(&L.h[ra][o]), xl = ld<bf16x8_t>(&L.l[ra][o]);
+            const bf16x8_t mh = ld<bf16x8_t>(&L.h[rb][o]), ml = ld<bf16x8_t>(&L.l[rb][o]);
+            acc = mma32(xh, mh, acc);
+            x1 = mma32(xh, ml, x1);
+            x1 = mma32(xl, mh, x1);
           }
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const int ri = 4 * lq + s, d = ri ^ lm, jj = ri - lm;
-            float v = 0.f;
-            if (d >= 8) {
-              v = lvl[0][s];
-            } else if (d >= 4) {
-              v = lvl[1][s];
-            } else if (jj > 0 || (jj == 0 && !gram_a)) {
-              const int xi = gram_a ? jj - 1 : (jj == 0 ? 6 : 2 + jj);
-              v = pair_lds[ri][0][xi] + pair_lds[ri][1][xi];
-            }
-            acc[s] = v;
-          }
+          acc += x1;
         } else {
           const __bf16(*Xh)[OPP] = gram_a ? sm.kp[0] : sm.qp[0];
           const __bf16(*Xl)[OPP] = gram_a ? sm.kp[1] : sm.qp[1];
@@ -687,7 +693,9 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           }
           acc += a1;
         }
-        if (gram_a) {
+        if (kSp && (lv == 0 ? (lm >> 3) == (lq >> 1) : ((lm >> 3) != (lq >> 1) || (lm >> 2) == lq))) {
+          // entries of another level or of the pair waves
+        } else if (gram_a) {
 #pragma unroll
           for (int s = 0; s < 4; ++s) sm.A[4 * lq + s][lm] = (lm < 4 * lq + s) ? acc[s] : 0.f;
         } else {
