@@ -68,8 +68,11 @@ typedef enum {
      Retention gate", gate.py; Kimi K3) */
   KDA_GATE_BOUNDED = 0,
   /* g = -exp(A_log) * softplus(z + dt_bias), unbounded (Kimi-Linear, per the analysis
-     page's status note); lower_bound is ignored.  The chunked prefill's tile factors need
-     the bound, so kda_prefill runs the sequential scan for this gate. */
+     page's status note); lower_bound is ignored.  Without the bound a chunk's decay range
+     is unbounded; the bf16 chunked prefill forms every intra-chunk pair against a boundary
+     row between its two rows (two MFMA levels, position pairs on the 4x4 diagonal blocks;
+     OpenModelAtlas "Kimi K3 - Retention gate", "Why").  With fp32 io, or together with the
+     low-rank gate (f_b), kda_prefill runs the sequential scan for it. */
   KDA_GATE_SOFTPLUS = 1
 } kda_gate_kind;
 
