@@ -20,7 +20,7 @@ launch over the whole batch.  Printed as one JSON line with:
                 fraction at its algorithmic bytes);
 * prefill    -- the chunked prefill on the 1 x 4096 x 32-head, 2 x 8192 x 96-head and
                 16-sequence varlen x 64-head workloads, and on 2 x 8192 x 96 heads with
-                the low-rank decay gate and with the softplus gate (3 warm-up runs, median of 20, each
+                the low-rank decay gate, the softplus gate, and both (3 warm-up runs, median of 20, each
                 after a 768 MB write that flushes the 256 MB MALL): tokens/s, the fraction
                 of HBM and of dense bf16 MFMA peak at the algorithmic byte and flop counts,
                 and the roofline fraction max(bytes / HBM peak, flops / MFMA peak) / time;
@@ -62,7 +62,7 @@ METRIC = "KDA tokens/s per layer (chunked prefill, decode); % of MFMA / HBM roof
 DECODE_KERNEL = "decode_kernel"
 PREFILL_KERNEL = "prefill_pc_kernel"  # the bf16 prefill kernel
 PREFILL_WORKLOADS = ("prefill_t4096_h32", "prefill_2x8192_h96", "varlen16_h64", "prefill_2x8192_h96_lowrank",
-                     "prefill_2x8192_h96_softplus")
+                     "prefill_2x8192_h96_softplus", "prefill_2x8192_h96_softplus_lowrank")
 
 
 def kernel_source_hash(name: str) -> str:
@@ -255,8 +255,8 @@ def bench_prefill(name: str, reps: int, warmup: int = 3):
     s = ms / 1e3
     res = dict(workload=name, sequences=N, tokens=T, heads=H,
                path="segment-parallel" if ws_bytes else "whole-sequence", workspace_bytes=ws_bytes,
-               decay_gate=("low-rank (z_low f_b^T in the kernel)" if w.low_rank_gate else
-                           "softplus (unbounded)" if w.softplus_gate else "full-rank z"),
+               decay_gate=(("softplus, " if w.softplus_gate else "") +
+                           ("low-rank (z_low f_b^T in the kernel)" if w.low_rank_gate else "full-rank z")),
                ms=ms, ms_min=times[0], reps=reps,
                tokens_per_s=T / s, hbm_gbs=nbytes / s / 1e9, hbm_frac=nbytes / s / 1e9 / HBM_PEAK_GBS,
                mfma_tflops=flops / s / 1e12, mfma_frac=flops / s / 1e12 / MFMA_BF16_PEAK_TFLOPS,

@@ -259,10 +259,9 @@ kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
   a.out = out;
   a.state_out = state_out;
   a.ring_out = ring_out;
-  // The fp32-io chunked kernel has neither the softplus gate nor the low-rank gate, and
-  // the bf16 one not both at once: those combinations run the scan.
-  const bool softplus = layer->gate_kind == KDA_GATE_SOFTPLUS;
-  if ((io == KDA_F32 && (softplus || layer->f_b)) || (softplus && layer->f_b))
+  // The fp32-io chunked kernel has neither the softplus gate nor the low-rank gate: with
+  // either, fp32 io runs the scan.
+  if (io == KDA_F32 && (layer->gate_kind == KDA_GATE_SOFTPLUS || layer->f_b))
     return kda_prefill_scan(layer, io, num_seqs, cu_seqlens_dev, cu_seqlens_host, total_tokens,
                             q, k, v, z, beta, gate, state_in, ring_in, out, state_out, ring_out,
                             stream);

@@ -76,9 +76,10 @@ __device__ __forceinline__ void lds_barrier() {
 // target, which stalls on HBM latency.  The vmcnt waits the compiler does compute for its
 // own loads stay correct (vector memory operations complete in issue order, so extra
 // ones in flight only make those waits longer).
+// The LDS address is the low half of the pointer's flat address (the LDS aperture puts
+// the offset there), taken without an address-space cast and its null test.
 __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)lds_wave_base)));
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_wave_base)));
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(gsrc), "s"(lds)

@@ -176,7 +176,6 @@ __device__ __forceinline__ float softplus_gate2(float z, float spb, float ascale
 // Qa, Ka and Kl take their factors directly (2^Gcum, 2^(Gcum_end - Gcum), both <= 1).
 template <bool kFb, bool kSp>
 __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder order, SplitPlan plan) {
-  static_assert(!(kFb && kSp), "the low-rank gate is built for the bounded gate only");
   __shared__ PcSmem sm;
   // raw rows of q, k, v, z of the next chunk, as [plane][channel half][row][64]: producer
   // wave w reads and refills slice [w / 2][w % 2] only
@@ -266,7 +265,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     const float ga = -kLog2e * ascale, gb = -kLog2e * ascale * a.L.dt_bias[c];
     const float lb2 = kLog2e * a.L.lower_bound;
     const float spb = kLog2e * a.L.dt_bias[c];  // softplus gate: (z + dt_bias) log2 e = z log2 e + spb
-    if (kFb && urole == 3) sm.gbias[ch] = gb;
+    if (kFb && urole == 3) sm.gbias[ch] = kSp ? spb : gb;
 
     // Raw rows of a chunk, straight into LDS.  Each wave fetches exactly the slice it reads
     // itself in interval 1 (plane urole, channels 64 hf .. + 63, all 16 rows) as two
@@ -353,7 +352,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       float G[4], g7 = 0.f, g15 = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        float g = lb2 * frcp(1.0f + fexp2(fmaf(zt[s], ga, gbv[s])));
+        float g = kSp ? softplus_gate2(zt[s], gbv[s], ascale) : lb2 * frcp(1.0f + fexp2(fmaf(zt[s], ga, gbv[s])));
         g = lm < Ln ? g : 0.f;
         g += dpp_z<0x111>(g);  // inclusive prefix over the rows: row_shr 1, 2, 4, 8
         g += dpp_z<0x112>(g);
@@ -369,9 +368,75 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       if (lm < 4) {
         const int cc = opaque(cb + lm);  // recomputed here, not kept live across the loop
         sm.eg15n[cc] = e15;
-        sm.g7[cc] = g7;
-        sm.eg7[cc] = e7;
-        sm.e157[cc] = e157;
+        if (!kSp) {
+          sm.g7[cc] = g7;
+          sm.eg7[cc] = e7;
+          sm.e157[cc] = e157;
+        }
+      }
+    };
+
+    // softplus gate: the 4x4 diagonal blocks of chunk i + 1's G and P as position pairs,
+    // on the four q and k waves: in interval 3, where they have no other job, or with the
+    // low-rank gate in interval 2, since its interval 3 rewrites Gcum for chunk c + 2.  Wave w takes rows 4w .. 4w + 3
+    // (local rows 0..3): the first half-wave the pairs (1,0), (2,0), (2,1) and P's diagonal
+    // at rows 0..2, the second the pairs (3,0), (3,1), (3,2) and the diagonal at row 3;
+    // lane l of a half takes channels 4 (l % 32) .. + 3.  A pair (a, b) costs one
+    // exponential 2^(Gcum_a - Gcum_b) <= 1 per channel.  The sums over the half's 32 lanes
+    // (DPP row sums, then the two rows) are written by its first 12 (rows 0..2) or 4
+    // (row 3) lanes, one entry of G and of P each.
+    auto pair_blocks = [&](int kbuf) __attribute__((always_inline)) {
+      KBuf& KP = sm.kb[kbuf];
+      const int hh = lane >> 5, pc = 4 * (lane & 31), r0 = 4 * uwave;
+      auto row4 = [&](const float(*arr)[LDP], int row, float* x) __attribute__((always_inline)) {
+        const float4 v = ld<float4>(&arr[r0 + row][pc]);
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+      };
+      float ps[9];  // G and P of the half's three pairs, then three diagonal entries
+#pragma unroll
+      for (int sl = 0; sl < 3; ++sl) {
+        // pair sl of this half: (1, 0), (2, 0), (2, 1) in the first, (3, sl) in the second
+        const int ra = hh ? 3 : (sl == 0 ? 1 : 2), rb = hh ? sl : (sl == 2 ? 1 : 0);
+        float qa[4], ka[4], ga[4], kb[4], gb[4];
+        row4(sm.aq, ra, qa);
+        row4(sm.ak, ra, ka);
+        row4(sm.gam, ra, ga);
+        row4(sm.ak, rb, kb);
+        row4(sm.gam, rb, gb);
+        float sg = 0.f, sp = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float kf = kb[v] * fexp2(ga[v] - gb[v]);
+          sg = fmaf(ka[v], kf, sg);
+          sp = fmaf(qa[v], kf, sp);
+        }
+        ps[sl] = sg;
+        ps[3 + sl] = sp;
+      }
+#pragma unroll
+      for (int dg = 0; dg < 3; ++dg) {
+        float qd[4], kd[4];
+        row4(sm.aq, hh ? 3 : dg, qd);
+        row4(sm.ak, hh ? 3 : dg, kd);
+        ps[6 + dg] = (qd[0] * kd[0] + qd[1] * kd[1]) + (qd[2] * kd[2] + qd[3] * kd[3]);
+      }
+#pragma unroll
+      for (int x = 0; x < 9; ++x) {
+        ps[x] = row_sum16(ps[x]);
+        ps[x] += __shfl_xor(ps[x], 16, 64);
+      }
+      const int cl = lane & 31;
+      if (cl < (hh ? 4 : 12)) {
+        const int a = hh ? 3 : cl >> 2, b = cl & 3;
+        // pair (a, b), b < a: its slot in this half
+        const int sl = hh ? b : (a == 1 ? 0 : 1 + b);
+        const float gsel = sl == 0 ? ps[0] : sl == 1 ? ps[1] : ps[2];
+        const float psel = sl == 0 ? ps[3] : sl == 1 ? ps[4] : ps[5];
+        const float dsel = hh ? ps[6] : (a == 0 ? ps[6] : a == 1 ? ps[7] : ps[8]);
+        const float gv_ = b < a ? gsel : 0.f;
+        const float pv_ = b < a ? psel : (b == a ? dsel : 0.f);
+        sm.A[r0 + a][r0 + b] = gv_;
+        split_store(&KP.p[r0 + a][il16(r0 + b)], &KP.p[r0 + a][il16(r0 + b) + 4], pv_);
       }
     };
 
@@ -581,74 +646,12 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         for (int v = 0; v < 4; v += 2)
           split_store2(&KN.klt[c4 + v][il16(r)], &KN.klt[c4 + v][il16(r) + 4], &KN.klt[c4 + v + 1][il16(r)],
                        &KN.klt[c4 + v + 1][il16(r) + 4], kl[v], kl[v + 1]);
+        if (kSp && kFb && uwave < 4) pair_blocks((i + 1) & 1);
       }
       lds_barrier();
 
       // ---------------------------------------------------------- interval 3
-      // softplus gate: the 4x4 diagonal blocks of chunk i + 1's G and P as position pairs,
-      // on four waves with no interval-3 job of their own.  Wave w takes rows 4w .. 4w + 3
-      // (local rows 0..3): the first half-wave the pairs (1,0), (2,0), (2,1) and P's diagonal
-      // at rows 0..2, the second the pairs (3,0), (3,1), (3,2) and the diagonal at row 3;
-      // lane l of a half takes channels 4 (l % 32) .. + 3.  A pair (a, b) costs one
-      // exponential 2^(Gcum_a - Gcum_b) <= 1 per channel.  The sums over the half's 32 lanes
-      // (DPP row sums, then the two rows) are written by its first 12 (rows 0..2) or 4
-      // (row 3) lanes, one entry of G and of P each.
-      if (kSp && has_next && uwave < 4) {
-        const int hh = lane >> 5, pc = 4 * (lane & 31), r0 = 4 * uwave;
-        float qv[4][4], kv[4][4], gv[4][4];
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const float4 q = ld<float4>(&sm.aq[r0 + a4][pc]), k = ld<float4>(&sm.ak[r0 + a4][pc]);
-          const float4 g = ld<float4>(&sm.gam[r0 + a4][pc]);
-          qv[a4][0] = q.x; qv[a4][1] = q.y; qv[a4][2] = q.z; qv[a4][3] = q.w;
-          kv[a4][0] = k.x; kv[a4][1] = k.y; kv[a4][2] = k.z; kv[a4][3] = k.w;
-          gv[a4][0] = g.x; gv[a4][1] = g.y; gv[a4][2] = g.z; gv[a4][3] = g.w;
-        }
-        float ps[9];  // G and P of the half's three pairs, then three diagonal entries
-#pragma unroll
-        for (int sl = 0; sl < 3; ++sl) {
-          // pair sl of this half: (2 - (sl == 0), sl == 2) in the first, (3, sl) in the second
-          const int ra = sl == 0 ? 1 : 2, rb = sl == 2 ? 1 : 0;
-          float sg = 0.f, sp = 0.f;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float ga = hh ? gv[3][v] : gv[ra][v], gb = hh ? gv[sl][v] : gv[rb][v];
-            const float kb = hh ? kv[sl][v] : kv[rb][v];
-            const float ka = hh ? kv[3][v] : kv[ra][v], qa = hh ? qv[3][v] : qv[ra][v];
-            const float kf = kb * fexp2(ga - gb);
-            sg = fmaf(ka, kf, sg);
-            sp = fmaf(qa, kf, sp);
-          }
-          ps[sl] = sg;
-          ps[3 + sl] = sp;
-        }
-#pragma unroll
-        for (int dg = 0; dg < 3; ++dg) {
-          const int ad = hh ? 3 : dg;
-          float sd = 0.f;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) sd = fmaf(qv[ad][v], kv[ad][v], sd);
-          ps[6 + dg] = sd;
-        }
-#pragma unroll
-        for (int x = 0; x < 9; ++x) {
-          ps[x] = row_sum16(ps[x]);
-          ps[x] += __shfl_xor(ps[x], 16, 64);
-        }
-        const int cl = lane & 31;
-        if (cl < (hh ? 4 : 12)) {
-          const int a = hh ? 3 : cl >> 2, b = cl & 3;
-          // pair (a, b), b < a: its slot in this half
-          const int sl = hh ? b : (a == 1 ? 0 : 1 + b);
-          const float gsel = sl == 0 ? ps[0] : sl == 1 ? ps[1] : ps[2];
-          const float psel = sl == 0 ? ps[3] : sl == 1 ? ps[4] : ps[5];
-          const float dsel = hh ? ps[6] : (a == 0 ? ps[6] : a == 1 ? ps[7] : ps[8]);
-          const float gv_ = b < a ? gsel : 0.f;
-          const float pv_ = b < a ? psel : (b == a ? dsel : 0.f);
-          sm.A[r0 + a][r0 + b] = gv_;
-          split_store(&KN.p[r0 + a][il16(r0 + b)], &KN.p[r0 + a][il16(r0 + b) + 4], pv_);
-        }
-      }
+      if (kSp && !kFb && has_next && uwave < 4) pair_blocks((i + 1) & 1);
       // (softplus gate: level 1 of G and P on the Gram waves, level 2 on waves 7 and 6,
       // so that each SIMD issues one level tile)
       if (has_next && (uwave == kGramAWave || uwave == kGramPWave || (kSp && uwave >= 6))) {
@@ -940,12 +943,13 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 
 }  // namespace
 
-// The kernel variant for the layer's decay gate (the low-rank gate is built for the
-// bounded gate; the launch sites route the other combinations to the scan).
+// The kernel variant for the layer's decay gate: low-rank or full-rank pre-activation,
+// bounded or softplus gate.
 using PcKernel = void (*)(PrefillArgs, PcOrder, SplitPlan);
 static PcKernel pc_kernel_for(const PrefillArgs& a) {
-  if (a.L.gate_kind == KDA_GATE_SOFTPLUS) return prefill_pc_kernel<false, true>;
-  return a.L.f_b ? prefill_pc_kernel<true, false> : prefill_pc_kernel<false, false>;
+  const bool sp = a.L.gate_kind == KDA_GATE_SOFTPLUS;
+  if (a.L.f_b) return sp ? prefill_pc_kernel<true, true> : prefill_pc_kernel<true, false>;
+  return sp ? prefill_pc_kernel<false, true> : prefill_pc_kernel<false, false>;
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, const int32_t* order_host, hipStream_t stream) {

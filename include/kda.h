@@ -71,8 +71,8 @@ typedef enum {
      page's status note); lower_bound is ignored.  Without the bound a chunk's decay range
      is unbounded; the bf16 chunked prefill forms every intra-chunk pair against a boundary
      row between its two rows (two MFMA levels, position pairs on the 4x4 diagonal blocks;
-     OpenModelAtlas "Kimi K3 - Retention gate", "Why").  With fp32 io, or together with the
-     low-rank gate (f_b), kda_prefill runs the sequential scan for it. */
+     OpenModelAtlas "Kimi K3 - Retention gate", "Why"), also together with the low-rank
+     gate (f_b).  With fp32 io, kda_prefill runs the sequential scan for it. */
   KDA_GATE_SOFTPLUS = 1
 } kda_gate_kind;
 

@@ -20,7 +20,9 @@ Workloads (all head_dim 128, short-conv kernel 4, lower bound -5):
 * ``prefill_2x8192_h96_softplus`` -- ``prefill_2x8192_h96`` with Kimi-Linear's unbounded
   softplus decay gate (layer["gate_kind"] = GATE_SOFTPLUS, the ABI's value) in place of the
   lower-bounded one; with A_log = log U(1, 16) and z ~ N(0, 1) a token's decay reaches
-  tens of nats, so a 16-token chunk spans up to several hundred.
+  tens of nats, so a 16-token chunk spans up to several hundred;
+* ``prefill_2x8192_h96_softplus_lowrank`` -- both: Kimi-Linear's pairing of the softplus gate
+  with the low-rank pre-activation.
 
 Distributions: raw q/k/v, decay pre-activation z and output-gate pre-activation ~ N(0, 1);
 raw beta ~ N(0, 1); conv weights ~ U(-0.5, 0.5); dt_bias ~ N(0, 0.1); A_log = log U(1, 16)
@@ -88,6 +90,9 @@ WORKLOADS = {
                                            [8192, 8192], seed=20266, low_rank_gate=True),
     "prefill_2x8192_h96_softplus": Workload("prefill_2x8192_h96_softplus", "prefill", "bf16", 96,
                                             [8192, 8192], seed=20267, softplus_gate=True),
+    "prefill_2x8192_h96_softplus_lowrank": Workload("prefill_2x8192_h96_softplus_lowrank", "prefill",
+                                                    "bf16", 96, [8192, 8192], seed=20268,
+                                                    low_rank_gate=True, softplus_gate=True),
 }
 
 

@@ -121,3 +121,53 @@ def test_softplus_prefill_2x8192_h96():
     rng = np.random.default_rng(9)
     units = sorted({(0, 0), (1, 95)} | {(int(rng.integers(0, 2)), int(rng.integers(0, 96))) for _ in range(3)})
     _check(prob, res, units, "softplus_2x8192_h96")
+
+
+def test_softplus_low_rank_prefill_varlen():
+    """Kimi-Linear's pairing: the softplus gate with the low-rank pre-activation z_low f_b^T
+    formed inside the kernel (the position pairs then run in interval 2), ragged sequences,
+    carried state and ring, every unit; then decode steps from the returned states."""
+    from kda_testutil import decode_as_prefill
+    kda = _kda()
+    lens = [37, 1, 0, 16, 2, 130, 33]
+    prob = synthetic.make_prefill(lens, H=3, io="bf16", seed=504, device=DEV, init_state=True,
+                                  init_ring=True, low_rank_gate=True, softplus_gate=True)
+    assert prob["z"].shape == (sum(lens), D)
+    res = _prefill(prob, allow_split=False)
+    _check(prob, res, _all_units(prob), "softplus_low_rank_varlen")
+    layer = kda.Layer(**prob["layer"])
+    dec = synthetic.make_decode(B=len(lens), H=3, io="bf16", steps=3, seed=505, device=DEV,
+                                low_rank_gate=True)
+    dec["layer"] = prob["layer"]
+    dec["state"], dec["ring"] = res[1].clone(), res[2].clone()
+    st, rg = dec["state"].clone(), dec["ring"].clone()
+    outs = torch.stack([kda.decode_step(layer, dec["q"][s], dec["k"][s], dec["v"][s], dec["z"][s],
+                                        dec["beta"][s], dec["gate"][s], st, rg) for s in range(3)])
+    torch.cuda.synchronize()
+    for b in (0, 5):
+        for h in range(3):
+            (o_ref, s_ref, _), = oracle_units(decode_as_prefill(dec, 3, b, h), [(0, 0)], workers=1)
+            assert_close(outs[:, b, h * D:(h + 1) * D].float().cpu().numpy(), o_ref, True,
+                         f"softplus low-rank decode out (b={b}, h={h})", stored_bf16=True)
+            assert_close(st[b, h].cpu().numpy(), s_ref, True, f"softplus low-rank decode state (b={b}, h={h})")
+
+
+def test_softplus_low_rank_segment_parallel():
+    """The softplus and low-rank gates together on the segment-parallel path, every unit."""
+    prob = synthetic.make_prefill([1500, 300], H=2, io="bf16", seed=506, device=DEV,
+                                  init_state=True, init_ring=True, low_rank_gate=True,
+                                  softplus_gate=True)
+    kda = _kda()
+    assert kda.prefill_workspace_bytes(kda.Layer(**prob["layer"]), torch.bfloat16, prob["cu_seqlens"]) > 0
+    _check(prob, _prefill(prob), _all_units(prob), "softplus_low_rank_segment_parallel")
+
+
+def test_softplus_low_rank_prefill_2x8192_h96():
+    """2 x 8192 tokens, 96 heads, softplus and low-rank gates (the bench's Kimi-Linear
+    workload): sampled units against the oracle."""
+    prob = synthetic.make_workload("prefill_2x8192_h96_softplus_lowrank", device=DEV)
+    res = _prefill(prob)
+    assert torch.isfinite(res[0].float()).all() and torch.isfinite(res[1]).all()
+    rng = np.random.default_rng(10)
+    units = sorted({(0, 0), (1, 95)} | {(int(rng.integers(0, 2)), int(rng.integers(0, 96))) for _ in range(3)})
+    _check(prob, res, units, "softplus_low_rank_2x8192_h96")
