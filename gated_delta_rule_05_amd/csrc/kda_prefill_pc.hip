@@ -172,7 +172,8 @@ __device__ __forceinline__ float softplus_gate2(float z, float spb, float ascale
 //   level 1, rows 8..15 against rows 0..7, boundary row 7 (MFMA);
 //   level 2, rows 4..7 against 0..3 and 12..15 against 8..11, boundary rows 3 and 11 (MFMA);
 //   the pairs inside aligned groups of four rows and P's diagonal, one exponential per pair
-//   and channel on the vector ALU (interval 3, on the four q and k waves).
+//   and channel on the vector ALU (on the four q and k waves: interval 3, or interval 2
+//   with the low-rank gate).
 // Qa, Ka and Kl take their factors directly (2^Gcum, 2^(Gcum_end - Gcum), both <= 1).
 template <bool kFb, bool kSp>
 __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder order, SplitPlan plan) {
@@ -378,13 +379,13 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 
     // softplus gate: the 4x4 diagonal blocks of chunk i + 1's G and P as position pairs,
     // on the four q and k waves: in interval 3, where they have no other job, or with the
-    // low-rank gate in interval 2, since its interval 3 rewrites Gcum for chunk c + 2.  Wave w takes rows 4w .. 4w + 3
-    // (local rows 0..3): the first half-wave the pairs (1,0), (2,0), (2,1) and P's diagonal
-    // at rows 0..2, the second the pairs (3,0), (3,1), (3,2) and the diagonal at row 3;
-    // lane l of a half takes channels 4 (l % 32) .. + 3.  A pair (a, b) costs one
-    // exponential 2^(Gcum_a - Gcum_b) <= 1 per channel.  The sums over the half's 32 lanes
-    // (DPP row sums, then the two rows) are written by its first 12 (rows 0..2) or 4
-    // (row 3) lanes, one entry of G and of P each.
+    // low-rank gate in interval 2, since there interval 3 overwrites Gcum with chunk i + 2's.
+    // Wave w takes rows 4w .. 4w + 3 (local rows 0..3): the first half-wave the pairs
+    // (1,0), (2,0), (2,1) and P's diagonal at rows 0..2, the second the pairs (3,0), (3,1),
+    // (3,2) and the diagonal at row 3; lane l of a half takes channels 4 (l % 32) .. + 3.  A
+    // pair (a, b) costs one exponential 2^(Gcum_a - Gcum_b) <= 1 per channel.  The sums over
+    // the half's 32 lanes (DPP row sums, then the two rows) are written by its first 12
+    // (rows 0..2) or 4 (row 3) lanes, one entry of G and of P each.
     auto pair_blocks = [&](int kbuf) __attribute__((always_inline)) {
       KBuf& KP = sm.kb[kbuf];
       const int hh = lane >> 5, pc = 4 * (lane & 31), r0 = 4 * uwave;
