@@ -146,3 +146,26 @@ def test_zero_tokens_copies_through():
     torch.cuda.synchronize()
     assert out.shape[1] == 0
     assert torch.equal(s1, dec["state"]) and torch.equal(r1, dec["ring"])
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_multi_softplus_gate_is_bit_identical_to_chained_steps(io):
+    """The same per-row bit-identity with the unbounded softplus gate (its fast decays make
+    the state forget within a few rows, so every row's own arithmetic shows)."""
+    kda = _kda()
+    B, H, t = 4, 2, 5
+    dec = synthetic.make_decode(B=B, H=H, io=io, steps=t, seed=307, device=DEV)
+    dec["layer"]["gate_kind"] = synthetic.GATE_SOFTPLUS
+    layer = kda.Layer(**dec["layer"])
+    ref_out, ref_st, ref_rg = _chain(layer, dec, t, dec["state"], dec["ring"])
+    rows = _rows(dec, t)
+    st, rg = dec["state"].clone(), dec["ring"].clone()
+    out = kda.decode_multi(layer, *(rows[n] for n in NAMES), st, rg)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(st, ref_st) and torch.equal(rg, ref_rg)
+    for b in (0, B - 1):
+        for h in range(H):
+            (o_ref, s_ref, _), = oracle_units(decode_as_prefill(dec, t, b, h), [(0, 0)], workers=1)
+            assert_close(out[b, :, h * D:(h + 1) * D].float().cpu().numpy(), o_ref, io == "bf16",
+                         f"softplus multi out (b={b}, h={h})", stored_bf16=io == "bf16")
+            assert_close(st[b, h].cpu().numpy(), s_ref, io == "bf16", f"softplus multi state (b={b}, h={h})")
