@@ -175,7 +175,10 @@ __device__ __forceinline__ float softplus_gate2(float z, float spb, float ascale
 //   and channel on the vector ALU (on the four q and k waves: interval 3, or interval 2
 //   with the low-rank gate).
 // Qa, Ka and Kl take their factors directly (2^Gcum, 2^(Gcum_end - Gcum), both <= 1).
-template <bool kFb, bool kSp>
+//
+// kXfer: the Transfer pass of the segment-parallel path, which forms end states only: the
+// q plane and everything built from it (Qa, P, O, the output rows) are left out.
+template <bool kFb, bool kSp, bool kXfer>
 __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder order, SplitPlan plan) {
   __shared__ PcSmem sm;
   // raw rows of q, k, v, z of the next chunk, as [plane][channel half][row][64]: producer
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     // the Transfer pass needs neither the last segment's end state nor the first's M
     if (a.pass == kPassTransfer && (kseg == nsegs - 1 || (transfer_m && kseg == 0))) return;
   }
-  const bool write_out = a.pass != kPassTransfer;
+  constexpr bool write_out = !kXfer;  // a.pass == kPassTransfer exactly when kXfer
   const bool last_seg = kseg == nsegs - 1;
   const int64_t Hd = static_cast<int64_t>(H) * kHeadDim;
   const int nch = (T + C - 1) / C;
@@ -290,12 +293,13 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     auto prefetch = [&](int c0n) __attribute__((always_inline)) {
       const int Ln = min(C, T - c0n);
       if (kFb && urole == 3) return;  // the z plane is z_low, fetched by prefetch_zlow
+      if (t < C) braw = x_b[(t0 + c0n + min(t, Ln - 1)) * H + h].bits;
+      if (urole == 0 && !write_out) return;  // the Transfer pass has no use for q
       const char* base = plane_base + (t0 + c0n) * Hd * 2;
       const int slice = opaque(2 * urole + hf);  // recomputed here, not kept live across the loop
 #pragma unroll
       for (int k = 0; k < 2; ++k)
         lds_dma16(base + min(8 * k + (lane >> 3), Ln - 1) * row_bytes, &raw_lds[slice >> 1][slice & 1][8 * k][0]);
-      if (t < C) braw = x_b[(t0 + c0n + min(t, Ln - 1)) * H + h].bits;
     };
     auto prefetch_gate = [&](int c0n, int buf) __attribute__((always_inline)) {
       if (uwave < 4) {
@@ -476,7 +480,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         // a sequence's last is full, and takes a path without per-row liveness tests so
         // that the rows' exp/rcp chains interleave.
         uint16_t xr[C];
-        if (!(kFb && urole == 3)) {
+        if (!(kFb && urole == 3) && !(urole == 0 && !write_out)) {
 #pragma unroll
           for (int r = 0; r < C; ++r) xr[r] = raw_lds[urole][hf][r][lane];
         }
@@ -485,6 +489,9 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           // the transfer matrix is the end state from the identity with v = 0
 #pragma unroll
           for (int r = 0; r < C; ++r) KN.V[r][ch] = 0.f;
+        } else if (urole == 0 && !write_out) {
+          // the Transfer pass forms end states only: q and everything built from it (Qa,
+          // P, the output rows) go unused, and their work is skipped
         } else if (urole < 3) {
           float(*dst)[LDP] = urole == 0 ? sm.aq : urole == 1 ? sm.ak : KN.V;
           if (full) {
@@ -563,7 +570,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       if (has_next) {
         // chunk i + 1's output gate, into the buffer of chunk i - 2, whose epilogue ran in
         // the previous interval 3
-        prefetch_gate((i + 1) * C, (i + 1) % 3);
+        if (write_out) prefetch_gate((i + 1) * C, (i + 1) % 3);
         // Every operand of chunk i + 1 for row r, channels c4 .. c4 + 3 (rows run fastest
         // across lanes, so the transposed Ka / Kl writes are 32 contiguous bytes per
         // channel).  With d = Gcum - Gcum_mid: Qp = a_q e^d, Kp = a_k e^d, Km = a_k e^-d;
@@ -610,8 +617,8 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           const int x1 = r & 7, x2 = ((r >> 3) << 2) + (r & 3);
           store4(&L1.h[late1 ? 8 + x1 : x1][c4], &L1.l[late1 ? 8 + x1 : x1][c4], x1k);
           store4(&L2.h[late2 ? 8 + x2 : x2][c4], &L2.l[late2 ? 8 + x2 : x2][c4], x2k);
-          if (late1) store4(&L1.h[16 + x1][c4], &L1.l[16 + x1][c4], x1q);
-          if (late2) store4(&L2.h[16 + x2][c4], &L2.l[16 + x2][c4], x2q);
+          if (late1 && write_out) store4(&L1.h[16 + x1][c4], &L1.l[16 + x1][c4], x1q);
+          if (late2 && write_out) store4(&L2.h[16 + x2][c4], &L2.l[16 + x2][c4], x2q);
         } else {
           const float4 g7 = ld<float4>(&sm.g7[c4]);
           const float4 e7 = ld<float4>(&sm.eg7[c4]);
@@ -632,7 +639,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
             sq = fmaf(q4[v], q4[v], sq);
             sk = fmaf(k4[v], k4[v], sk);
           }
-          store4(&sm.qp[0][r][c4], &sm.qp[1][r][c4], qp);
+          if (write_out) store4(&sm.qp[0][r][c4], &sm.qp[1][r][c4], qp);
           store4(&sm.kp[0][r][c4], &sm.kp[1][r][c4], kp);
           store4(&sm.km[0][r][c4], &sm.km[1][r][c4], km);
         }
@@ -641,7 +648,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         // Qa and Ka in the key order of the .S products: channels 32 kb + 4 m .. + 3 sit
         // at 32 kb + 8 (m % 4) + 4 (m / 4)
         const int pa = 32 * (c4 >> 5) + 8 * ((c4 >> 2) & 3) + 4 * ((c4 >> 4) & 1);
-        store4_f16(&KN.qa[r][pa], qa);
+        if (write_out) store4_f16(&KN.qa[r][pa], qa);
         store4_f16(&KN.ka[r][pa], ka);
 #pragma unroll
         for (int v = 0; v < 4; v += 2)
@@ -655,8 +662,8 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       if (kSp && !kFb && has_next && uwave < 4) pair_blocks((i + 1) & 1);
       // (softplus gate: level 1 of G and P on the Gram waves, level 2 on waves 7 and 6,
       // so that each SIMD issues one level tile)
-      if (has_next && (uwave == kGramAWave || uwave == kGramPWave || (kSp && uwave >= 6))) {
-        const bool gram_a = uwave == kGramAWave || uwave == 7;
+      const bool gram_a = uwave == kGramAWave || uwave == 7;
+      if (has_next && (uwave == kGramAWave || uwave == kGramPWave || (kSp && uwave >= 6)) && (gram_a || write_out)) {
         const int lv = kSp && uwave >= 6 ? 1 : 0;  // softplus gate: this wave's level
         // Gram tiles of chunk i + 1: G = Kp Km^T (strict lower; the elimination of consumer
         // waves kElimCwA/B in the next interval 1 scales its rows by beta') and
@@ -877,7 +884,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
             sf[s] = static_cast<_Float16>(S[2 * kb][s]);
             sf[4 + s] = static_cast<_Float16>(S[2 * kb + 1][s]);
           }
-          O = mma32h(ld<f16x8_t>(&K.qa[lm][32 * kb + 8 * lq]), sf, O);
+          if (write_out) O = mma32h(ld<f16x8_t>(&K.qa[lm][32 * kb + 8 * lq]), sf, O);
           X = mma32h(ld<f16x8_t>(&K.ka[lm][32 * kb + 8 * lq]), sf, X);
         }
       }
@@ -906,13 +913,15 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           split_vec<4>(u4, uh, ul);
           b_pair(uh, ul, u_l0, u_hh);
         }
-        // O += P U
-        O = mma16p(ld<bf16x8_t>(&K.p[lm][8 * lq]), u_l0, u_hh, O);
-        float ss[4];
+        // O += P U and the rows' partial sums of squares (not in the Transfer pass)
+        if (write_out) {
+          O = mma16p(ld<bf16x8_t>(&K.p[lm][8 * lq]), u_l0, u_hh, O);
+          float ss[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) ss[s] = row_sum16(O[s] * O[s]);
-        if (lm == 0)
-          *reinterpret_cast<float4*>(&sm.ss[cw][4 * lq]) = make_float4(ss[0], ss[1], ss[2], ss[3]);
+          for (int s = 0; s < 4; ++s) ss[s] = row_sum16(O[s] * O[s]);
+          if (lm == 0)
+            *reinterpret_cast<float4*>(&sm.ss[cw][4 * lq]) = make_float4(ss[0], ss[1], ss[2], ss[3]);
+        }
 
       }
       lds_barrier();
@@ -944,13 +953,14 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 
 }  // namespace
 
-// The kernel variant for the layer's decay gate: low-rank or full-rank pre-activation,
-// bounded or softplus gate.
+// The kernel variant for the layer's decay gate (low-rank or full-rank pre-activation,
+// bounded or softplus gate) and the pass (Transfer, or one with outputs).
 using PcKernel = void (*)(PrefillArgs, PcOrder, SplitPlan);
+template <bool kXfer>
 static PcKernel pc_kernel_for(const PrefillArgs& a) {
   const bool sp = a.L.gate_kind == KDA_GATE_SOFTPLUS;
-  if (a.L.f_b) return sp ? prefill_pc_kernel<true, true> : prefill_pc_kernel<true, false>;
-  return sp ? prefill_pc_kernel<false, true> : prefill_pc_kernel<false, false>;
+  if (a.L.f_b) return sp ? prefill_pc_kernel<true, true, kXfer> : prefill_pc_kernel<true, false, kXfer>;
+  return sp ? prefill_pc_kernel<false, true, kXfer> : prefill_pc_kernel<false, false, kXfer>;
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, const int32_t* order_host, hipStream_t stream) {
@@ -961,7 +971,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, const int32_t* order_host, 
   PrefillArgs w = a;
   w.pass = kPassWhole;
   const dim3 grid(static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.L.H));
-  hipLaunchKernelGGL(pc_kernel_for(a), grid, dim3(NT), 0, stream, w, ord, none);
+  hipLaunchKernelGGL(pc_kernel_for<false>(a), grid, dim3(NT), 0, stream, w, ord, none);
   return hipGetLastError();
 }
 
@@ -969,58 +979,114 @@ namespace {
 
 // S_{k+1} = M_k S_k + B_k over the segments of each sequence, for one 16-column block of
 // one head's state (value columns never mix, so the blocks are independent).  S_1 = B_0:
-// segment 0 started from the true state.  256 threads: thread t forms rows t / 2, columns
-// 8 (t % 2) .. + 7 of the block; the block itself sits in LDS.  fp32 FMAs in a fixed order.
-__global__ __launch_bounds__(256) void combine_kernel(PrefillArgs a, SplitPlan plan) {
+// segment 0 started from the true state.  The products run on fp32 MFMA (16x16x4): wave w
+// forms rows 32w .. 32w + 31 of the block as two 16-row tiles, and lane (lm, lq) feeds
+// M[row lm][32 lq + kk] and S[32 lq + kk][column lm] at step kk = 0..31, so the 128-long
+// contraction runs as four contiguous quarters, one per lane group; a lane's quarter-rows
+// of M and its entries of B are loaded one step ahead.  S_k sits in LDS.
+__global__ __launch_bounds__(256, 1) void combine_kernel(PrefillArgs a, SplitPlan plan) {
   constexpr int CB = 16;
-  __shared__ float sblk[kHeadDim][CB];
+  constexpr int SP = CB + 1;  // padded LDS row
+  __shared__ float sblk[kHeadDim][SP];
   const int H = a.L.H;
-  const int nb = kHeadDim / CB;
-  const int unit = blockIdx.x / nb;
-  const int cb = blockIdx.x - unit * nb;
+  constexpr int nb = kHeadDim / CB;
+  // The eight column blocks of a (sequence, head) go to one XCD (workgroups are dealt
+  // round-robin over the 8 XCDs), so that M_k comes from HBM once per unit and from that
+  // XCD's L2 for the other seven blocks.
+  int unit, cb;
+  const int nunits = static_cast<int>(gridDim.x) / nb;
+  if (nunits % 8 == 0) {
+    const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    unit = (slot / nb) * 8 + xcd;
+    cb = slot % nb;
+  } else {
+    unit = blockIdx.x / nb;
+    cb = blockIdx.x - unit * nb;
+  }
   const int n = unit / H;
   const int h = unit - n * H;
   const int t = threadIdx.x;
-  const int r = t >> 1, c0 = 8 * (t & 1);
+  const int wave = t >> 6, lane = t & 63, lm = lane & 15, lq = lane >> 4;
   const int first = plan.first[n], nsegs = plan.first[n + 1] - plan.first[n];
   if (nsegs < 2) return;
   constexpr int64_t kDD = kHeadDim * kHeadDim;
   auto plane = [&](float* base, int k) { return base + ((static_cast<int64_t>(first + k)) * H + h) * kDD; };
+  // this lane's output rows: 32 wave + 16 tile + 4 lq + s, column cb * 16 + lm
+  auto row_of = [&](int tile, int s) { return 32 * wave + 16 * tile + 4 * lq + s; };
+  const int col = cb * CB + lm;
   // S_1 = B_0
-  float acc[8];
   {
-    const float* b0 = plane(a.seg_b, 0) + r * kHeadDim + cb * CB + c0;
-    float* s1 = plane(a.seg_start, 1) + r * kHeadDim + cb * CB + c0;
+    const float* b0 = plane(a.seg_b, 0) + col;
+    float* s1 = plane(a.seg_start, 1) + col;
+    float v[2][4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      acc[j] = b0[j];
-      s1[j] = acc[j];
-      sblk[r][c0 + j] = acc[j];
-    }
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) v[tile][s] = b0[row_of(tile, s) * kHeadDim];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        s1[row_of(tile, s) * kHeadDim] = v[tile][s];
+        sblk[row_of(tile, s)][lm] = v[tile][s];
+      }
+  }
+  // M_k's quarter-rows of this lane: rows 32 wave + 16 tile + lm, columns 32 lq .. + 31
+  float4 mq[2][8];
+  auto load_m = [&](int k) __attribute__((always_inline)) {
+    const float* m = plane(a.seg_m, k) + 32 * lq;
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        mq[tile][q] = *reinterpret_cast<const float4*>(m + (32 * wave + 16 * tile + lm) * kHeadDim + 4 * q);
+  };
+  // B_k at this lane's output entries, also one step ahead
+  float bv[2][4];
+  auto load_b = [&](int k) __attribute__((always_inline)) {
+    const float* bk = plane(a.seg_b, k) + col;
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) bv[tile][s] = bk[row_of(tile, s) * kHeadDim];
+  };
+  if (nsegs > 2) {
+    load_m(1);
+    load_b(1);
   }
   for (int k = 1; k + 1 < nsegs; ++k) {
     __syncthreads();
-    const float* mrow = plane(a.seg_m, k) + r * kHeadDim;
-    const float* brow = plane(a.seg_b, k) + r * kHeadDim + cb * CB + c0;
+    // all 32 B operands from LDS first (one LDS round trip), then the MFMA chain
+    float bs[32];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-    for (int l = 0; l < kHeadDim; l += 4) {
-      const float4 m4 = *reinterpret_cast<const float4*>(mrow + l);
-      const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+    for (int kk = 0; kk < 32; ++kk) bs[kk] = sblk[32 * lq + kk][lm];
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+    for (int q = 0; q < 8; ++q) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = fmaf(mv[u], sblk[l + u][c0 + j], acc[j]);
+      for (int u = 0; u < 4; ++u) {
+        acc[0] = mma4(mq[0][q][u], bs[4 * q + u], acc[0]);
+        acc[1] = mma4(mq[1][q][u], bs[4 * q + u], acc[1]);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] += brow[j];
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc[tile][s] += bv[tile][s];
+    if (k + 2 < nsegs) {
+      load_m(k + 1);
+      load_b(k + 1);
+    }
     __syncthreads();
-    float* snext = plane(a.seg_start, k + 1) + r * kHeadDim + cb * CB + c0;
+    float* snext = plane(a.seg_start, k + 1) + col;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      sblk[r][c0 + j] = acc[j];
-      snext[j] = acc[j];
-    }
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        sblk[row_of(tile, s)][lm] = acc[tile][s];
+        snext[row_of(tile, s) * kHeadDim] = acc[tile][s];
+      }
   }
 }
 
@@ -1031,8 +1097,7 @@ hipError_t launch_prefill_bf16_split(const PrefillArgs& a, const SplitPlan& plan
   const unsigned H = static_cast<unsigned>(a.L.H);
   PrefillArgs w = a;
   w.pass = kPassTransfer;
-  const auto pass = pc_kernel_for(a);
-  hipLaunchKernelGGL(pass, dim3(2u * plan.nseg * H), dim3(NT), 0, stream, w, none, plan);
+  hipLaunchKernelGGL(pc_kernel_for<true>(a), dim3(2u * plan.nseg * H), dim3(NT), 0, stream, w, none, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(a.num_seqs) * H * (kHeadDim / 16)),
@@ -1040,7 +1105,7 @@ hipError_t launch_prefill_bf16_split(const PrefillArgs& a, const SplitPlan& plan
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   w.pass = kPassFinal;
-  hipLaunchKernelGGL(pass, dim3(plan.nseg * H), dim3(NT), 0, stream, w, none, plan);
+  hipLaunchKernelGGL(pc_kernel_for<false>(a), dim3(plan.nseg * H), dim3(NT), 0, stream, w, none, plan);
   return hipGetLastError();
 }
 
