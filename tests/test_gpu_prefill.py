@@ -117,6 +117,18 @@ def test_extreme_gates(zval, bval):
         _check(prob, _prefill(prob), _all_units(prob), f"extreme_{zval}_{io}")
 
 
+@pytest.mark.parametrize("gate_kind", [0, synthetic.GATE_SOFTPLUS])
+def test_many_short_sequences(gate_kind):
+    """600 packed sequences of 0..40 tokens (more than the 512 the launch orders longest
+    first, so the grid takes them in index order), carried state and ring, bf16: every
+    unit against the oracle, for both decay gates."""
+    rng = np.random.default_rng(206)
+    lens = [int(x) for x in rng.integers(0, 41, size=600)]
+    prob = synthetic.make_prefill(lens, H=2, io="bf16", seed=206, device=DEV, init_state=True,
+                                  init_ring=True, softplus_gate=gate_kind == synthetic.GATE_SOFTPLUS)
+    _check(prob, _prefill(prob), _all_units(prob), f"many_short_{gate_kind}")
+
+
 def test_prefill_t4096_h32():
     """1 sequence x 4096 tokens, 32 heads, bf16 io: every unit against the oracle.  With 32
     (sequence, head) units this runs the segment-parallel path (8 segments)."""
