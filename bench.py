@@ -47,6 +47,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+# Vector-ALU issue peak: 256 CUs x 4 SIMDs x 2.4 GHz, one wave64 fp32 instruction per SIMD
+# every 2 cycles (the 157.3 TFLOP/s fp32 vector peak is 32 FMA lanes per SIMD and cycle;
+# packed fp32 is not used).  Transcendentals (v_exp, v_rcp, ...) take 4 slots.
+VALU_PEAK_INSTS = 256 * 4 * 2.4e9 / 2
 D = 128
 
 # Algorithmic HBM bytes per (token, head) of the decode step, bf16 io: fp32 state read and
@@ -266,6 +270,12 @@ def bench_prefill(name: str, reps: int, warmup: int = 3):
     counters = prefill_counters(name)
     if counters:
         res["counters"] = counters
+        # the kernel's actual bound: vector-ALU issue, from the counted instructions
+        vi = counters.get("valu_insts_per_token_head")
+        if vi:
+            rate = vi * T * H / s
+            res["alu_roofline"] = dict(bound="alu", achieved=rate, peak=VALU_PEAK_INSTS,
+                                       unit="wave64 VALU instructions/s", frac=rate / VALU_PEAK_INSTS)
     if w.decode_after:
         res["decode_continuation"] = bench_decode_after(w, layer, st, rg, stream)
     del prob, out, flush
