@@ -163,6 +163,19 @@ def test_segment_parallel_path():
     _ring_exact(prob, _prefill(prob)[2])
 
 
+def test_segment_parallel_eight_units():
+    """Eight (sequence, head) units, a multiple of the eight XCDs, so the combine deals each
+    unit's column blocks to one XCD; the two sequences have different segment counts (8
+    and 4 segments of 256 tokens).  Every unit against the oracle."""
+    prob = synthetic.make_prefill([2000, 900], H=4, io="bf16", seed=208, device=DEV,
+                                  init_state=True, init_ring=True)
+    z = prob["z"].view(2900, 4, D)
+    z[:, :, ::4] = -1e4  # g = 0 on a quarter of the channels: state crosses every boundary
+    kda = _kda()
+    assert kda.prefill_workspace_bytes(kda.Layer(**prob["layer"]), torch.bfloat16, prob["cu_seqlens"]) > 0
+    _check(prob, _prefill(prob), _all_units(prob), "segment_parallel_8_units")
+
+
 def test_segment_parallel_matches_whole_path():
     """Both paths meet the oracle; with the same inputs their outputs differ only by
     rounding (the segment path forms start states as M S + B)."""

@@ -171,3 +171,24 @@ def test_softplus_low_rank_prefill_2x8192_h96():
     rng = np.random.default_rng(10)
     units = sorted({(0, 0), (1, 95)} | {(int(rng.integers(0, 2)), int(rng.integers(0, 96))) for _ in range(3)})
     _check(prob, res, units, "softplus_low_rank_2x8192_h96")
+
+
+@pytest.mark.parametrize("low_rank", [False, True])
+def test_softplus_prefill_fp32_runs_the_scan(low_rank):
+    """fp32 io with the softplus gate (and with the low-rank gate too): kda_prefill runs the
+    sequential scan, equal bit for bit to the explicit scan arm, and meets the oracle."""
+    kda = _kda()
+    lens = [45, 3, 0, 60]
+    prob = synthetic.make_prefill(lens, H=2, io="f32", seed=507, device=DEV, init_state=True,
+                                  init_ring=True, low_rank_gate=low_rank, softplus_gate=True)
+    res = _prefill(prob)
+    scan = _prefill(prob, scan=True)
+    for x, y in zip(res, scan):
+        assert torch.equal(x, y)
+    out, state, ring = res
+    cu = prob["cu_seqlens"].tolist()
+    for (n, h), (o_ref, s_ref, _) in zip(_all_units(prob), oracle_units(prob, _all_units(prob))):
+        got = out[cu[n]:cu[n + 1], h * D:(h + 1) * D].cpu().numpy()
+        if got.size:
+            assert_close(got, o_ref, False, f"softplus fp32 out (n={n}, h={h})")
+        assert_close(state[n, h].cpu().numpy(), s_ref, False, f"softplus fp32 state (n={n}, h={h})")
