@@ -176,6 +176,18 @@ def test_segment_parallel_eight_units():
     _check(prob, _prefill(prob), _all_units(prob), "segment_parallel_8_units")
 
 
+@pytest.mark.parametrize("gate_kind", [0, synthetic.GATE_SOFTPLUS])
+def test_single_head_long_sequence(gate_kind):
+    """One head, one 3,000-token sequence: the segment-parallel path with a single unit
+    (twelve 256-token segments, the last one short), carried state and ring, every output
+    row and the final state against the oracle."""
+    prob = synthetic.make_prefill([3000], H=1, io="bf16", seed=209, device=DEV, init_state=True,
+                                  init_ring=True, softplus_gate=gate_kind == synthetic.GATE_SOFTPLUS)
+    kda = _kda()
+    assert kda.prefill_workspace_bytes(kda.Layer(**prob["layer"]), torch.bfloat16, prob["cu_seqlens"]) > 0
+    _check(prob, _prefill(prob), _all_units(prob), f"single_head_{gate_kind}")
+
+
 def test_segment_parallel_matches_whole_path():
     """Both paths meet the oracle; with the same inputs their outputs differ only by
     rounding (the segment path forms start states as M S + B)."""
