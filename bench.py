@@ -59,13 +59,14 @@ D = 128
 DECODE_BYTES_PER_TOKEN_HEAD = 2 * D * D * 4 + 2 * 3 * D * 3 * 4 + 5 * D * 2 + 2 + D * 2
 # Prefill, bf16 io: q/k/v/z/gate in, beta in, out; state/ring in and out are added per sequence.
 PREFILL_BYTES_PER_TOKEN_HEAD = 5 * D * 2 + 2 + D * 2
+IO_BYTES = {"bf16": 2, "f32": 4}
 # Algorithmic prefill flops per (token, head) at chunk 64, the same count for every
 # prefill workload whatever chunk the kernel uses: 6 d^2 + 5 C d + C^2 / 3.
 PREFILL_FLOPS_PER_TOKEN_HEAD = 6 * D * D + 5 * 64 * D + 64 * 64 // 3
 METRIC = "KDA tokens/s per layer (chunked prefill, decode); % of MFMA / HBM roofline"
 DECODE_KERNEL = "decode_kernel"
 PREFILL_KERNEL = "prefill_pc_kernel"  # the bf16 prefill kernel
-PREFILL_WORKLOADS = ("prefill_t4096_h32", "prefill_2x8192_h96", "varlen16_h64", "prefill_2x8192_h96_lowrank",
+PREFILL_WORKLOADS = ("tiny_prefill_fp32", "prefill_t4096_h32", "prefill_2x8192_h96", "varlen16_h64", "prefill_2x8192_h96_lowrank",
                      "prefill_2x8192_h96_softplus", "prefill_2x8192_h96_softplus_lowrank")
 
 
@@ -82,11 +83,35 @@ def kernel_source_hash(name: str) -> str:
 
 
 def cpu_cores() -> int:
+    """Threads for the oracle baseline: the cores this process may run on (its affinity
+    mask), or fewer when the host's thread-count setting (OMP_NUM_THREADS) says so."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
+def cpu_info() -> dict:
+    """The host CPU: model name, logical CPUs online, and the affinity mask's size."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        aff = None
+    return dict(model=model, nproc=os.cpu_count(), affinity=aff,
+                omp_num_threads=os.environ.get("OMP_NUM_THREADS"))
 
 
 # --------------------------------------------------------------------------- decode
@@ -205,14 +230,15 @@ def prefill_algorithmic_bytes(w) -> int:
     with the low-rank gate, z_low [T, 128] (shared by the heads) and f_b [H*128, 128] in
     place of the full-rank z plane."""
     N, H, T = len(w.seqlens), w.heads, sum(w.seqlens)
-    nbytes = (PREFILL_BYTES_PER_TOKEN_HEAD * T * H + N * H * D * D * 4 * (2 if w.init_state else 1)
+    e = IO_BYTES[w.io]
+    nbytes = ((5 * D + 1 + D) * e * T * H + N * H * D * D * 4 * (2 if w.init_state else 1)
               + N * 3 * H * D * 3 * 4 * (2 if w.init_ring else 1))
     if w.low_rank_gate:
-        nbytes += -D * 2 * T * H + D * 2 * T + H * D * D * 2
+        nbytes += -D * e * T * H + D * e * T + H * D * D * e
     return nbytes
 
 
-def bench_prefill(name: str, reps: int, warmup: int = 3):
+def bench_prefill(name: str, reps: int, warmup: int = 3, cpu: bool = True):
     import torch
 
     import gated_delta_rule_05_amd as kda
@@ -225,12 +251,13 @@ def bench_prefill(name: str, reps: int, warmup: int = 3):
     cu_dev = prob["cu_seqlens"].to(dev)
     T = sum(w.seqlens)
     N = len(w.seqlens)
-    out = torch.empty((T, w.heads * D), dtype=torch.bfloat16, device=dev)
+    dt = synthetic.torch_io_dtype(w.io)
+    out = torch.empty((T, w.heads * D), dtype=dt, device=dev)
     st = torch.empty((N, w.heads, D, D), dtype=torch.float32, device=dev)
     rg = torch.empty((N, 3 * w.heads * D, 3), dtype=torch.float32, device=dev)
     flush = torch.empty(768 << 20, dtype=torch.uint8, device=dev)  # larger than the 256 MB MALL
     stream = torch.cuda.current_stream()
-    ws_bytes = kda.prefill_workspace_bytes(layer, torch.bfloat16, prob["cu_seqlens"])
+    ws_bytes = kda.prefill_workspace_bytes(layer, dt, prob["cu_seqlens"])
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
 
     def run():
@@ -257,7 +284,7 @@ def bench_prefill(name: str, reps: int, warmup: int = 3):
     nbytes = prefill_algorithmic_bytes(w)
     flops = PREFILL_FLOPS_PER_TOKEN_HEAD * T * H
     s = ms / 1e3
-    res = dict(workload=name, sequences=N, tokens=T, heads=H,
+    res = dict(workload=name, sequences=N, tokens=T, heads=H, io=w.io,
                path="segment-parallel" if ws_bytes else "whole-sequence", workspace_bytes=ws_bytes,
                decay_gate=(("softplus, " if w.softplus_gate else "") +
                            ("low-rank (z_low f_b^T in the kernel)" if w.low_rank_gate else "full-rank z")),
@@ -278,7 +305,10 @@ def bench_prefill(name: str, reps: int, warmup: int = 3):
                                        unit="wave64 VALU instructions/s", frac=rate / VALU_PEAK_INSTS)
     if w.decode_after:
         res["decode_continuation"] = bench_decode_after(w, layer, st, rg, stream)
-    del prob, out, flush
+    del out, flush
+    if cpu:
+        res["cpu_baseline"] = prefill_cpu_baseline(w, prob)
+    del prob
     return res
 
 
@@ -364,6 +394,41 @@ def prefill_counters(name: str):
 
 # --------------------------------------------------------------------------- CPU baseline
 
+PREFILL_CPU_SAMPLE = 2.0e6  # token-heads of oracle work per prefill workload (a few seconds)
+
+
+def prefill_cpu_baseline(w, prob):
+    """The fp64 oracle on the workload's own inputs, threaded over (sequence, head) units:
+    every unit when the workload has at most PREFILL_CPU_SAMPLE token-heads, otherwise the
+    first k heads of every sequence with k chosen to stay near that budget (all sequence
+    lengths are kept).  Tokens/s per layer = sampled token-heads / H / time, i.e. the time
+    scaled up from the sampled fraction of the units to the whole workload."""
+    import oracle
+
+    N, H, T = len(w.seqlens), w.heads, sum(w.seqlens)
+    k = H if T * H <= PREFILL_CPU_SAMPLE else max(1, int(-(-PREFILL_CPU_SAMPLE * H // (T * H))))
+    units = [(n, h) for n in range(N) for h in range(k)]
+    p = prob["layer"]
+    cpu = lambda x: None if x is None else x.detach().cpu()
+    lay = oracle.Layer(H, D, cpu(p["conv_w"]), cpu(p["dt_bias"]), cpu(p["A_log"]), cpu(p["norm_w"]),
+                       lower_bound=p["lower_bound"], l2_eps=p["l2_eps"], rms_eps=p["rms_eps"],
+                       gate_kind=p.get("gate_kind", 0), f_b=cpu(p.get("f_b")))
+    acts = {n: cpu(prob[n]) for n in ("q", "k", "v", "z", "beta", "gate")}
+    st = None if prob.get("state_in") is None else cpu(prob["state_in"]).double().numpy()
+    rg = None if prob.get("ring_in") is None else cpu(prob["ring_in"]).numpy()
+    io = oracle.BF16 if w.io == "bf16" else oracle.F32
+    cores = min(cpu_cores(), len(units))
+    t = time.perf_counter()
+    oracle.prefill_units(lay, io, prob["cu_seqlens"], acts["q"], acts["k"], acts["v"], acts["z"],
+                         acts["beta"], acts["gate"], st, rg, units=units, nthreads=cores)
+    el = time.perf_counter() - t
+    th = k * T
+    return {"value": th / H / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"all {N * H} units" if k == H else f"heads 0..{k - 1} of all {N} sequences "
+                       f"({k} of {H} heads, scaled by {H / k:.2f})") +
+                      f": {th} token-heads in {el:.2f} s"}
+
+
 def cpu_baseline(dec, target_s: float = 10.0):
     """The fp64 oracle on a bounded sample of the decode workload: all heads of the first
     u sequences over all 128 steps (each sequence's 128 steps as one oracle sequence, the
@@ -408,8 +473,10 @@ def cpu_baseline(dec, target_s: float = 10.0):
 # --------------------------------------------------------------------------- PMC summaries
 
 def _read_pmc(d: str, counter: str):
-    """(kernel name, grid size, value) for every dispatch row of one counter."""
+    """(kernel name, grid size, value) for every dispatch row of one counter, from
+    rocprofv3's CSV output (--output-format csv) or its default SQLite database."""
     import csv
+    import sqlite3
     rows = []
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         with open(f) as fh:
@@ -417,6 +484,15 @@ def _read_pmc(d: str, counter: str):
                 if r.get("Counter_Name") == counter:
                     rows.append((r["Kernel_Name"], int(r.get("Grid_Size", 0) or 0),
                                  float(r["Counter_Value"])))
+    if not rows:
+        for f in glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True):
+            con = sqlite3.connect(f)
+            try:
+                rows += [(k, int(g or 0), float(v)) for k, g, v in con.execute(
+                    "select kernel_name, grid_size, value from counters_collection where counter_name = ?",
+                    (counter,))]
+            finally:
+                con.close()
     return rows
 
 
@@ -428,8 +504,9 @@ def _copy_scale(rows):
 
 def summarize_pmc(fetch_dir: str, write_dir: str):
     """Reads two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) of
-    `bench.py --no-prefill --no-cpu-baseline --calibrate-copy`, scales each by the same
-    counter's reading on the 1 GiB copy kernel, and writes profiles/decode_b256_h32_pmc.json."""
+    `bench.py --decode-only --calibrate-copy` (decode steps only, so every decode-kernel
+    dispatch is a one-row step), scales each by the same counter's reading on the 1 GiB
+    copy kernel, and writes profiles/decode_b256_h32_pmc.json."""
     fetch = _read_pmc(fetch_dir, "FETCH_SIZE")
     write = _read_pmc(write_dir, "WRITE_SIZE")
 
@@ -520,6 +597,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="run only the timed decode steps (no verify, prefill, A/B or CPU "
+                         "baseline), so that a profile of the run holds decode steps alone")
     ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=3)
     ap.add_argument("--prefill-workloads", default=",".join(PREFILL_WORKLOADS))
@@ -555,11 +635,13 @@ def main():
     def prefill_list():
         pf = []
         for name in workloads:
-            pf.append(bench_prefill(name, args.prefill_reps, args.prefill_warmup))
+            pf.append(bench_prefill(name, args.prefill_reps, args.prefill_warmup,
+                                    cpu=not args.no_cpu_baseline))
             torch.cuda.empty_cache()
         return pf
 
     if args.only_prefill:
+        args.no_cpu_baseline = True
         pf = prefill_list()
         if args.calibrate_copy:
             copy_calibration()
@@ -591,12 +673,16 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": DECODE_KERNEL, "algorithmic_bytes_per_launch": bytes_launch},
     }
+    if args.decode_only:
+        print(json.dumps(line), flush=True)
+        return 0
     line["verify"] = bench_verify(dec)
     if not args.no_prefill:
         line["prefill"] = prefill_list()
         line["prefill_scan_ab"] = bench_scan_ab()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(dec)
+        line["cpu"] = cpu_info()
     print(json.dumps(line), flush=True)
     return 0
 

@@ -258,9 +258,21 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 #pragma unroll
         for (int j = 0; j < 3; ++j) hist[j] = bf16_to_f32(pl[(t0 - 3 + j) * Hd + c].bits);
       } else if (a.ring_in) {
-        const float* rin = a.ring_in + static_cast<int64_t>(n) * 3 * Hd * kRingTaps;
+        // segment 0 of a sequence cut into several: the Final pass reads the copy of the
+        // ring that the Transfer pass left in the unused M plane of segment 0, since the
+        // sequence's last segment may write ring_out == ring_in in the same launch
+        float* const copy = a.pass == kPassWhole ? nullptr
+                                                 : a.seg_m + (static_cast<int64_t>(seg) * H + h) * kHeadDim * kHeadDim +
+                                                       (role * kHeadDim + ch) * kRingTaps;
+        const float* const hp = (a.pass == kPassFinal && nsegs > 1)
+                                    ? copy
+                                    : a.ring_in + (static_cast<int64_t>(n) * 3 * Hd + role * Hd + c) * kRingTaps;
 #pragma unroll
-        for (int j = 0; j < 3; ++j) hist[j] = rin[(role * Hd + c) * kRingTaps + j];
+        for (int j = 0; j < 3; ++j) hist[j] = hp[j];
+        if (a.pass == kPassTransfer && !transfer_m) {
+#pragma unroll
+          for (int j = 0; j < 3; ++j) copy[j] = hist[j];
+        }
       }
     }
     // gate: g = lb sigmoid(e^A_log (z + dt_bias)) = lb / (1 + 2^(z ga + gb)); Gcum is kept
@@ -783,6 +795,10 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     const float* src = nullptr;
     if (a.pass == kPassFinal && kseg > 0)
       src = a.seg_start + sgbase;
+    else if (a.pass == kPassFinal && nsegs > 1)
+      // segment 0 of a sequence cut into several: the Transfer pass's copy of the start
+      // state (the sequence's last segment may write state_out == state_in in this launch)
+      src = a.state_in ? a.seg_start + sgbase : nullptr;
     else if (kseg == 0 && !transfer_m && a.state_in)
       src = a.state_in + nbase;
     if (src) {
@@ -791,6 +807,16 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
       for (int it = 0; it < 8; ++it)
 #pragma unroll
         for (int s = 0; s < 4; ++s) S[it][s] = sp[(16 * it + s) * kHeadDim];
+      if (a.pass == kPassTransfer && !transfer_m) {
+        // segment 0 (the Transfer pass skips a sequence's last segment, so the sequence
+        // has several): keep the start state where the Final pass reads it, in segment
+        // 0's start plane, which the combine never writes
+        float* cp = a.seg_start + sgbase + opaque(4 * lq * kHeadDim + col);
+#pragma unroll
+        for (int it = 0; it < 8; ++it)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) cp[(16 * it + s) * kHeadDim] = S[it][s];
+      }
     } else {
 #pragma unroll
       for (int it = 0; it < 8; ++it)

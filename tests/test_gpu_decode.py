@@ -1,10 +1,9 @@
 """GPU parity of kda_decode_step against the fp64 oracle (through the C ABI)."""
-import numpy as np
 import pytest
 import torch
 
 import synthetic
-from kda_testutil import D, assert_close, decode_as_prefill, oracle_units
+from kda_testutil import D, assert_close, check_all_units, decode_as_prefill, oracle_units
 
 pytestmark = pytest.mark.gpu
 
@@ -75,18 +74,23 @@ def test_decode_tiny_config_as_64_steps():
 
 
 def test_decode_b256_h32_128_steps():
-    """The batched decode workload at full size: 256 sequences x 32 heads, 128 steps.
-    Sampled units are checked against the oracle at every step; the ring is checked
+    """The batched decode workload at full size: 256 sequences x 32 heads, 128 steps.  Every
+    (sequence, head) unit's output at every step and its final state against the oracle,
+    which runs each sequence's 128 tokens as one sequence from the same initial state and
+    ring (prefill == repeated decode is pinned in the oracle tests); the ring is checked
     exactly for every channel."""
     w = synthetic.WORKLOADS["decode_b256_h32"]
     dec = synthetic.make_workload("decode_b256_h32", device=DEV)
     outs, state, ring = _run_decode(dec, w.steps)
     assert torch.isfinite(outs.float()).all() and torch.isfinite(state).all()
-    rng = np.random.default_rng(5)
-    units = [(0, 0), (255, 31), (17, 5)] + [(int(b), int(h)) for b, h in
-                                            zip(rng.integers(0, 256, 9), rng.integers(0, 32, 9))]
-    worst = _check_units(dec, outs, state, w.steps, units, True)
-    print(f"decode_b256_h32: worst error = {worst:.3f} x tolerance")
+    B, H, steps = w.batch, w.heads, w.steps
+    prob = {name: dec[name].transpose(0, 1).reshape(B * steps, -1).contiguous()
+            for name in ("q", "k", "v", "z", "beta", "gate")}
+    prob.update(layer=dec["layer"], cu_seqlens=synthetic.cu_seqlens([steps] * B),
+                state_in=dec["state"], ring_in=dec["ring"])
+    units = [(b, h) for b in range(B) for h in range(H)]
+    check_all_units(prob, outs.transpose(0, 1).reshape(B * steps, -1).cpu(), state.cpu(), units,
+                    "decode_b256_h32", batch=256)
     _ring_is_last_raw_inputs(dec, ring, w.steps)
 
 

@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import synthetic
-from kda_testutil import D, assert_close, head_layer, oracle_units
+from kda_testutil import D, assert_close, check_all_units, oracle_units
 
 pytestmark = pytest.mark.gpu
 
@@ -136,7 +136,9 @@ def test_prefill_t4096_h32():
     kda = _kda()
     layer = kda.Layer(**prob["layer"])
     assert kda.prefill_workspace_bytes(layer, torch.bfloat16, prob["cu_seqlens"]) > 0
-    _check(prob, _prefill(prob), _all_units(prob), "prefill_t4096_h32")
+    out, state, ring = _prefill(prob)
+    check_all_units(prob, out.cpu(), state.cpu(), _all_units(prob), "prefill_t4096_h32", batch=32,
+                    ring=ring.cpu())
 
 
 def _split_problem(seed):
@@ -161,6 +163,26 @@ def test_segment_parallel_path():
     assert kda.prefill_workspace_bytes(layer, torch.bfloat16, prob["cu_seqlens"]) > 0
     _check(prob, _prefill(prob), _all_units(prob), "segment_parallel")
     _ring_exact(prob, _prefill(prob)[2])
+
+
+def test_segment_parallel_in_place():
+    """The segment-parallel path with state_out == state_in and ring_out == ring_in: the
+    sequence's first segment reads its start state and ring in the same launch in which its
+    last segment writes the final ones, so it reads the copies the Transfer pass keeps in
+    the workspace.  Byte-identical to the run with separate output buffers."""
+    prob = _split_problem(210)
+    kda = _kda()
+    layer = kda.Layer(**prob["layer"])
+    assert kda.prefill_workspace_bytes(layer, torch.bfloat16, prob["cu_seqlens"]) > 0
+    ref = _prefill(prob)
+    st = prob["state_in"].clone()
+    rg = prob["ring_in"].clone()
+    out, st2, rg2 = kda.prefill(layer, prob["q"], prob["k"], prob["v"], prob["z"], prob["beta"],
+                                prob["gate"], prob["cu_seqlens"].to(DEV), prob["cu_seqlens"],
+                                state_in=st, ring_in=rg, state_out=st, ring_out=rg)
+    torch.cuda.synchronize()
+    assert st2.data_ptr() == st.data_ptr() and rg2.data_ptr() == rg.data_ptr()
+    assert torch.equal(out, ref[0]) and torch.equal(st, ref[1]) and torch.equal(rg, ref[2])
 
 
 def test_segment_parallel_eight_units():
@@ -201,21 +223,14 @@ def test_segment_parallel_matches_whole_path():
     assert d <= 0.05 * rms, (d, rms)
 
 
-def _sampled(N, H, extra, seed):
-    rng = np.random.default_rng(seed)
-    units = [(0, 0), (N - 1, H - 1)] + [(int(rng.integers(0, N)), int(rng.integers(0, H)))
-                                        for _ in range(extra)]
-    return sorted(set(units))
-
-
 def test_prefill_2x8192_h96():
-    """2 sequences x 8192 tokens, 96 heads, bf16 io, final states: sampled units against
-    the oracle; the ring of every channel checked exactly."""
+    """2 sequences x 8192 tokens, 96 heads, bf16 io, final states: every (sequence, head)
+    unit's output rows, final state and ring against the oracle."""
     prob = synthetic.make_workload("prefill_2x8192_h96", device=DEV)
-    res = _prefill(prob)
-    out, state, ring = res
+    out, state, ring = _prefill(prob)
     assert torch.isfinite(out.float()).all() and torch.isfinite(state).all()
-    _check(prob, res, _sampled(2, 96, 6, 7), "prefill_2x8192_h96")
+    check_all_units(prob, out.cpu(), state.cpu(), _all_units(prob), "prefill_2x8192_h96",
+                    ring=ring.cpu())
     _ring_exact(prob, ring)
 
 
@@ -232,19 +247,19 @@ def _ring_exact(prob, ring):
 
 def test_varlen16_h64_then_decode():
     """16 packed sequences with lengths ~ U[512, 16384], 64 heads, nonzero initial state
-    and ring; then 32 decode steps from the returned states and rings.  Sampled units of
-    both phases against the oracle."""
+    and ring; then 32 decode steps from the returned states and rings.  Every unit of both
+    phases against the oracle: the prefill's output rows, final states and rings; then the
+    decode outputs and final states against the oracle continued from its own prefill
+    states and rings (nothing of the GPU's prefill result enters the reference)."""
     kda = _kda()
     w = synthetic.WORKLOADS["varlen16_h64"]
     prob = synthetic.make_workload("varlen16_h64", device=DEV)
-    res = _prefill(prob)
-    out, state, ring = res
+    out, state, ring = _prefill(prob)
     N, H = len(w.seqlens), w.heads
     assert torch.isfinite(out.float()).all() and torch.isfinite(state).all()
-    longest = int(np.argmax(w.seqlens))
-    shortest = int(np.argmin(w.seqlens))
-    units = sorted(set(_sampled(N, H, 4, 11) + [(longest, 3), (shortest, 60)]))
-    _check(prob, res, units, "varlen16_h64")
+    units = _all_units(prob)
+    _, (s_ref, r_ref) = check_all_units(prob, out.cpu(), state.cpu(), units, "varlen16_h64",
+                                        ring=ring.cpu(), keep_final=True)
     _ring_exact(prob, ring)
     # decode continuation: 32 steps from the returned states and rings
     g = synthetic.gen(w.seed + 1, DEV)
@@ -258,40 +273,22 @@ def test_varlen16_h64_then_decode():
         outs.append(kda.decode_step(layer, acts["q"][s], acts["k"][s], acts["v"][s], acts["z"][s],
                                     acts["beta"][s], acts["gate"][s], st, rg))
     torch.cuda.synchronize()
-    outs = torch.stack(outs)
-    # Reference: the oracle runs each sampled unit's prefill tokens followed by its 32
-    # decode tokens as one sequence, from the original initial state and ring
-    # (prefill == repeated decode is pinned in the oracle tests); nothing of the GPU's
-    # prefill result enters the reference.
-    cu = prob["cu_seqlens"].tolist()
-    for (n, h) in [(longest, 3), (shortest, 60), (5, 17)]:
-        cols = slice(h * D, (h + 1) * D)
-        joined = {name: torch.cat([prob[name][cu[n]:cu[n + 1], cols], acts[name][:, n, cols]])
-                  for name in ("q", "k", "v", "z", "gate")}
-        joined["beta"] = torch.cat([prob["beta"][cu[n]:cu[n + 1], h:h + 1],
-                                    acts["beta"][:, n, h:h + 1]])
-        sub = dict(layer=prob["layer"], **joined)
-        p = decode_as_prefill_joined(sub, prob, n, h)
-        (o_ref, s_ref, _), = oracle_units(p, [(0, 0)], workers=1)
-        assert_close(outs[:, n, cols].float().cpu().numpy(), o_ref[-steps:], True,
-                     f"decode continuation out (n={n}, h={h})", stored_bf16=True)
-        assert_close(st[n, h].cpu().numpy(), s_ref, True,
-                     f"decode continuation state (n={n}, h={h})")
-
-
-def decode_as_prefill_joined(sub, prob, n, h):
-    """One-sequence, one-head problem over the joined tokens of unit (n, h)."""
-    T = sub["q"].shape[0]
-    H = prob["layer"]["num_heads"]
+    outs = torch.stack(outs)  # [steps, N, H*d]
+    # the reference: the decode tokens as a packed problem of N sequences x 32 tokens from
+    # the oracle's own final states and rings (prefill == repeated decode is pinned in the
+    # oracle tests)
     Hd = H * D
-    one = {name: sub[name].cpu() for name in ("q", "k", "v", "z", "gate", "beta")}
-    one["state_in"] = prob["state_in"][n:n + 1, h:h + 1].cpu()
-    r = prob["ring_in"][n].cpu()
-    one["ring_in"] = torch.cat([r[p * Hd + h * D:p * Hd + (h + 1) * D] for p in range(3)])[None]
-    one["cu_seqlens"] = torch.tensor([0, T], dtype=torch.int32)
-    lay = head_layer(prob["layer"], h)
-    one["layer"] = dict(num_heads=1, conv_w=torch.from_numpy(lay.conv_w),
-                        dt_bias=torch.from_numpy(lay.dt_bias), A_log=torch.from_numpy(lay.A_log),
-                        norm_w=torch.from_numpy(lay.norm_w), lower_bound=lay.lower_bound,
-                        l2_eps=lay.l2_eps, rms_eps=lay.rms_eps)
-    return one
+    dprob = {name: acts[name].transpose(0, 1).reshape(N * steps, -1).contiguous()
+             for name in ("q", "k", "v", "z", "beta", "gate")}
+    dprob["layer"] = prob["layer"]
+    dprob["cu_seqlens"] = synthetic.cu_seqlens([steps] * N)
+    sref = np.empty((N, H, D, D))
+    rref = np.empty((N, 3, H, D, 3))
+    for i, (n, h) in enumerate(units):
+        sref[n, h] = s_ref[i]
+        rref[n, :, h] = r_ref[i]
+    dprob["state_in"] = torch.from_numpy(sref)
+    dprob["ring_in"] = torch.from_numpy(rref.reshape(N, 3 * Hd, 3).astype(np.float32))
+    check_all_units(dprob, outs.transpose(0, 1).reshape(N * steps, Hd).cpu(), st.cpu(),
+                    _all_units(dprob), "varlen16_h64 decode continuation", batch=64)
+
