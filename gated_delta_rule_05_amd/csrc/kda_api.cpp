@@ -91,9 +91,9 @@ kda_status check_packed(int32_t num_seqs, const int32_t* cu_dev, const int32_t* 
     return fail(KDA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out)))
     return fail(KDA_ERR_INVALID_ARG, "state buffers must be 16-byte aligned");
-  if (total_tokens > 0 &&
-      (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(gate)))
-    return fail(KDA_ERR_INVALID_ARG, "q, k, v, z and gate must be 16-byte aligned");
+  if (total_tokens > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) ||
+                           !aligned16(gate) || !aligned16(out)))
+    return fail(KDA_ERR_INVALID_ARG, "q, k, v, z, gate and out must be 16-byte aligned");
   return KDA_OK;
 }
 

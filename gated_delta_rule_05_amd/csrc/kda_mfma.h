@@ -47,6 +47,16 @@ template <int N>
 __device__ __forceinline__ float row_bcast(float x) {
   return dpp<0x150 + N>(x);
 }
+// Multiplies the four key rows 16 IT + 4 lq + s (s = 0..3) of a state tile by their
+// factors, where lane n of each 16-lane row holds the factors of (it, s) = (n / 2,
+// 2 (n % 2)) in e0 and (n / 2, 2 (n % 2) + 1) in e1: row s takes lane 2 IT + s / 2's value.
+template <int IT, typename V4>
+__device__ __forceinline__ void decay_tile(V4& st, float e0, float e1) {
+  st[0] *= row_bcast<2 * IT>(e0);
+  st[1] *= row_bcast<2 * IT>(e1);
+  st[2] *= row_bcast<2 * IT + 1>(e0);
+  st[3] *= row_bcast<2 * IT + 1>(e1);
+}
 // Sum over the 16 lanes of a row, delivered to every lane of the row.
 __device__ __forceinline__ float row_sum16(float x) {
   x += dpp<0x128>(x);
@@ -55,9 +65,6 @@ __device__ __forceinline__ float row_sum16(float x) {
   x += dpp<0x121>(x);
   return x;
 }
-
-__device__ __forceinline__ float raw_to_f32(float x) { return x; }
-__device__ __forceinline__ float raw_to_f32(uint16_t b) { return bf16_to_f32(b); }
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() is also a fence on global
 // memory and waits for every outstanding global load, which would drain the next
@@ -157,26 +164,9 @@ __device__ __forceinline__ f32x4_t mma32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 __device__ __forceinline__ f32x4_t mma32h(f16x8_t a, f16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4_t mma16(bf16x4_t a, bf16x4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x4_t mma4(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
-// split products: (ah + al)(bh + bl) ~ ah bh + ah bl + al bh
-__device__ __forceinline__ f32x4_t mma32s(bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl,
-                                          f32x4_t c) {
-  c = mma32(al, bh, c);
-  c = mma32(ah, bl, c);
-  return mma32(ah, bh, c);
-}
-__device__ __forceinline__ f32x4_t mma16s(bf16x4_t ah, bf16x4_t al, bf16x4_t bh, bf16x4_t bl,
-                                          f32x4_t c) {
-  c = mma16(al, bh, c);
-  c = mma16(ah, bl, c);
-  return mma16(ah, bh, c);
-}
-
 // The same for a 16-long inner dimension on the 16x16x32 instruction, which issues in the
 // same time as the 16x16x16 one.  The A operand carries both halves, a = [ah | al] (slots
 // j < 4 of a lane hold ah, slots j >= 4 al, for the same four positions of the inner
@@ -203,35 +193,6 @@ __device__ __forceinline__ V ld(const E* p) {
   return *reinterpret_cast<const V*>(p);
 }
 
-// Stores 8 consecutive operand values at [row][col0..col0+7] of a (hi, lo) plane pair
-// (bf16) or of the single fp32 plane, as 16-byte writes.
-template <bool F32, typename Arr>
-__device__ __forceinline__ void store8(Arr& planes, int row, int col0, const float* x) {
-  if constexpr (F32) {
-    *reinterpret_cast<float4*>(&planes[0][row][col0]) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4*>(&planes[0][row][col0 + 4]) = make_float4(x[4], x[5], x[6], x[7]);
-  } else {
-    bf16x8_t hi, lo;
-    split_vec<8>(x, hi, lo);
-    *reinterpret_cast<bf16x8_t*>(&planes[0][row][col0]) = hi;
-    *reinterpret_cast<bf16x8_t*>(&planes[1][row][col0]) = lo;
-  }
-}
-
-// Same for a single plane rounded once (no lo part).
-template <bool F32, typename E>
-__device__ __forceinline__ void store8_hi(E* dst, const float* x) {
-  if constexpr (F32) {
-    *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4*>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
-  } else {
-    bf16x8_t hi;
-#pragma unroll
-    for (int v = 0; v < 8; ++v) hi[v] = static_cast<__bf16>(x[v]);
-    *reinterpret_cast<bf16x8_t*>(dst) = hi;
-  }
-}
-
 // 4 consecutive values as (hi, lo) bf16 at hi[0..3], lo[0..3] (8-byte writes), or hi only.
 __device__ __forceinline__ void store4(__bf16* hi, __bf16* lo, const float* x) {
   bf16x4_t h, l;
@@ -245,13 +206,6 @@ __device__ __forceinline__ void store4_f16(_Float16* dst, const float* x) {
   for (int v = 0; v < 4; ++v) h[v] = static_cast<_Float16>(x[v]);
   *reinterpret_cast<f16x4_t*>(dst) = h;
 }
-__device__ __forceinline__ void store4_hi(__bf16* hi, const float* x) {
-  bf16x4_t h;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) h[v] = static_cast<__bf16>(x[v]);
-  *reinterpret_cast<bf16x4_t*>(hi) = h;
-}
-
 // One elimination step per row j of the 16x16 unit-lower system: every lane of a 16-lane
 // row takes row j's values from lane j of its own row (DPP broadcast).
 template <int J>
@@ -260,18 +214,6 @@ __device__ __forceinline__ void eliminate(float* tt, const float* arow) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) tt[s] -= arow[J] * row_bcast<J>(tt[s]);
     eliminate<J + 1>(tt, arow);
-  }
-}
-
-// The same with lane (lm, lq) holding columns lq + 4 s (s = 0..3) of row lm.  Column c of
-// T is zero above row c, so step J can only change the values with lq + 4 s <= J: steps
-// 0..3 touch s = 0 only, 4..7 s <= 1, and so on (36 updates instead of 60).
-template <int J>
-__device__ __forceinline__ void eliminate_strided(float* tt, const float* arow) {
-  if constexpr (J < C - 1) {
-#pragma unroll
-    for (int s = 0; s <= J / 4; ++s) tt[s] -= arow[J] * row_bcast<J>(tt[s]);
-    eliminate_strided<J + 1>(tt, arow);
   }
 }
 

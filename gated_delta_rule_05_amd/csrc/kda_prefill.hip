@@ -23,16 +23,13 @@
 // in LDS for the next iteration):
 //   (1) q/k/v conv + SiLU (history in registers), gate, Gcum, sigmoid(gate), beta
 //   (2) q/k row norms
-//   (3) scaled operands, stored once in MFMA-ready form (bf16 hi/lo pairs)
+//   (3) scaled operands, stored once in MFMA-ready form
 //   (4) Gram tiles A and P (waves 0 and 1)
 //   (5) every wave: T by elimination across lanes (DPP broadcasts); W^T = Ka^T T^T lands directly in the
 //       A-operand layout of W.S; U~ = T V for its own value tile; the state pass
 //   (6) sigmoid-gated RMSNorm of each output row and the store
-// Precision (bf16 io): bf16 MFMA, fp32 accumulation; the operands of the Gram tiles,
-// U~ = T V, Qa.S, P.U and Kl^T.U are split into bf16 hi + lo (three MFMAs, about 16
-// significant bits); W and W.S use one bf16 rounding.  fp32 io runs the same data flow on
-// v_mfma_f32_16x16x4_f32.
-#include <type_traits>
+// This kernel serves fp32 io: every product runs on v_mfma_f32_16x16x4_f32 (fp32 operands,
+// fp32 accumulation).  bf16 io has its own producer/consumer kernel (kda_prefill_pc.hip).
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -52,35 +49,30 @@ struct SeqOrder {
   int32_t idx[kMaxOrdered];
 };
 
-// Operand storage: bf16 hi/lo planes, or one fp32 plane for fp32 io.
-template <bool F32>
+// MFMA operands, fp32.
 struct alignas(16) Ops {
-  using E = typename std::conditional<F32, float, __bf16>::type;
-  static constexpr int NP = F32 ? 1 : 2;
-  static constexpr int OPP = F32 ? 132 : 136;  // row stride of [16][128] operands
-  static constexpr int KTP = F32 ? 20 : 24;    // row stride of [128][16] operands
-  static constexpr int PPP = 20;               // row stride of the P tile
-  E qp[NP][C][OPP];    // Qp = q-hat exp(Gcum - Gref), natural key order
-  E qa[NP][C][OPP];    // Qa = q-hat exp(Gcum), key order of the .S products
-  E kp[NP][C][OPP];    // Kp = k-hat exp(Gcum - Gref)
-  E km[NP][C][OPP];    // Km = k-hat exp(Gref - Gcum)
-  E kat[kHeadDim][KTP];      // Ka^T, hi only
-  E klt[NP][kHeadDim][KTP];  // Kl^T
-  E p[NP][C][PPP];     // P tile (lower incl.)
+  static constexpr int OPP = 132;  // row stride of [16][128] operands
+  static constexpr int KTP = 20;   // row stride of [128][16] operands
+  static constexpr int PPP = 20;   // row stride of the P tile
+  float qp[C][OPP];         // Qp = q-hat exp(Gcum - Gref)
+  float qa[C][OPP];         // Qa = q-hat exp(Gcum)
+  float kp[C][OPP];         // Kp = k-hat exp(Gcum - Gref)
+  float km[C][OPP];         // Km = k-hat exp(Gref - Gcum)
+  float kat[kHeadDim][KTP];  // Ka^T
+  float klt[kHeadDim][KTP];  // Kl^T
+  float p[C][PPP];          // P tile (lower incl.)
 };
 
-template <bool F32>
 struct alignas(16) Smem {
-  using RawE = typename std::conditional<F32, float, uint16_t>::type;
-  static constexpr int RAWP = kHeadDim + (F32 ? 4 : 8);
-  RawE raw[5][C][RAWP];  // raw rows of q, k, v, z, gate (io type bits)
-  RawE braw[C];          // raw beta
+  static constexpr int RAWP = kHeadDim + 4;
+  float raw[5][C][RAWP];  // raw rows of q, k, v, z, gate
+  float braw[C];          // raw beta
   float aq[C][LDP];    // silu(conv q)
   float ak[C][LDP];    // silu(conv k)
   float va[C][LDP];    // silu(conv v) = V
   float gam[C][LDP];   // Gcum
   float sg[2][C][LDP];  // sigmoid(gate), double-buffered across chunks
-  Ops<F32> op;
+  Ops op;
   float A[C][AP];      // A tile times beta (strict lower), fp32
   float g7[kHeadDim];  // Gcum at the chunk midpoint (Gram reference)
   float g15[kHeadDim];  // Gcum at the chunk end
@@ -90,11 +82,9 @@ struct alignas(16) Smem {
   float ss[2][NWAVES][C];
 };
 
-template <typename IO>
 __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrder order) {
-  constexpr bool F32 = std::is_same<IO, float>::value;
-  using OP = Ops<F32>;
-  __shared__ Smem<F32> sm;
+  using OP = Ops;
+  __shared__ Smem sm;
 
   const int H = a.L.H;
   const int rank = blockIdx.x / H;
@@ -114,7 +104,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
   const int64_t c = static_cast<int64_t>(h) * kHeadDim + ch;
   const int col = 16 * wave + lm;  // value column this lane holds in the state pass
 
-  const IO* x_b = static_cast<const IO*>(a.beta);
+  const float* x_b = static_cast<const float*>(a.beta);
 
   // conv weights and history of the owned channel (roles 0-2: plane = role)
   float w[4] = {0.f, 0.f, 0.f, 0.f}, hist[3] = {0.f, 0.f, 0.f};
@@ -150,11 +140,10 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
   // registers while the chunk is processed, and parked in LDS just before the chunk's last
   // barrier.  Rows past the end of the sequence re-read its last row (always in bounds)
   // and are masked when used.
-  constexpr int E = sizeof(IO);
+  constexpr int E = sizeof(float);
   constexpr int SPR = kHeadDim * E / 16;  // 16-byte segments per row
   constexpr int NSEG = 5 * C * SPR;
   constexpr int NRND = (NSEG + NTHREADS - 1) / NTHREADS;
-  using Raw = typename std::conditional<F32, float, uint16_t>::type;
   uint4 seg0, seg1, seg2, seg3, seg4;
   // plane base pointers (uniform per wave: a wave's segments all fall in one plane)
   const char* const pq = static_cast<const char*>(a.q);
@@ -182,7 +171,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
     return reinterpret_cast<uint4*>(&sm.raw[pl][r][part * (16 / E)]);                      \
   }())
 #define KDA_SEG_OK(k) (NSEG % NTHREADS == 0 || t + (k) * NTHREADS < NSEG)
-  Raw braw = 0;
+  float braw = 0.f;
   auto prefetch = [&](int c0n) __attribute__((always_inline)) {
     const int Ln = min(C, T - c0n);
     if (KDA_SEG_OK(0)) seg0 = *KDA_SEG_SRC(0, c0n, Ln);
@@ -190,14 +179,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
     if (NRND > 2 && KDA_SEG_OK(2)) seg2 = *KDA_SEG_SRC(2, c0n, Ln);
     if (NRND > 3 && KDA_SEG_OK(3)) seg3 = *KDA_SEG_SRC(3, c0n, Ln);
     if (NRND > 4 && KDA_SEG_OK(4)) seg4 = *KDA_SEG_SRC(4, c0n, Ln);
-    if (t < C) {
-      const IO* pb = x_b + (t0 + c0n + min(t, Ln - 1)) * H + h;
-      if constexpr (F32) {
-        braw = *pb;
-      } else {
-        braw = pb->bits;
-      }
-    }
+    if (t < C) braw = x_b[(t0 + c0n + min(t, Ln - 1)) * H + h];
   };
   auto stage = [&]() __attribute__((always_inline)) {
     if (KDA_SEG_OK(0)) *KDA_SEG_DST(0) = seg0;
@@ -226,7 +208,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
       float(*dst)[LDP] = role == 0 ? sm.aq : role == 1 ? sm.ak : sm.va;
 #pragma unroll
       for (int r = 0; r < C; ++r) {
-        const float x = raw_to_f32(sm.raw[role][r][ch]);
+        const float x = sm.raw[role][r][ch];
         const float y = w[3] * x + w[0] * hist[0] + w[1] * hist[1] + w[2] * hist[2];
         const bool live = r < L;
         if (live) {
@@ -241,15 +223,15 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
 #pragma unroll
       for (int r = 0; r < C; ++r) {
         const bool live = r < L;
-        G += live ? lb * fsigmoid(ascale * (raw_to_f32(sm.raw[3][r][ch]) + dtb)) : 0.f;
+        G += live ? lb * fsigmoid(ascale * (sm.raw[3][r][ch] + dtb)) : 0.f;
         sm.gam[r][ch] = G;
-        sm.sg[buf][r][ch] = live ? fsigmoid(raw_to_f32(sm.raw[4][r][ch])) : 0.f;
+        sm.sg[buf][r][ch] = live ? fsigmoid(sm.raw[4][r][ch]) : 0.f;
         if (r == C / 2 - 1) sm.g7[ch] = G;
       }
       sm.g15[ch] = G;
       sm.eg15[ch] = fexp(G);
     }
-    if (t < C) sm.beta[t] = (t < L) ? fsigmoid(raw_to_f32(sm.braw[t])) : 0.f;
+    if (t < C) sm.beta[t] = (t < L) ? fsigmoid(sm.braw[t]) : 0.f;
     // next chunk's raw rows (the last chunk re-reads itself)
     prefetch(min(c0 + C, last_c0));
     lds_barrier();
@@ -298,9 +280,12 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
           kp[v] = k8[v] * rk * el;
           km[v] = k8[v] * rk * er;
         }
-        store8<F32>(sm.op.qp, r, c8, qp);
-        store8<F32>(sm.op.kp, r, c8, kp);
-        store8<F32>(sm.op.km, r, c8, km);
+        *reinterpret_cast<float4*>(&sm.op.qp[r][c8]) = make_float4(qp[0], qp[1], qp[2], qp[3]);
+        *reinterpret_cast<float4*>(&sm.op.qp[r][c8 + 4]) = make_float4(qp[4], qp[5], qp[6], qp[7]);
+        *reinterpret_cast<float4*>(&sm.op.kp[r][c8]) = make_float4(kp[0], kp[1], kp[2], kp[3]);
+        *reinterpret_cast<float4*>(&sm.op.kp[r][c8 + 4]) = make_float4(kp[4], kp[5], kp[6], kp[7]);
+        *reinterpret_cast<float4*>(&sm.op.km[r][c8]) = make_float4(km[0], km[1], km[2], km[3]);
+        *reinterpret_cast<float4*>(&sm.op.km[r][c8 + 4]) = make_float4(km[4], km[5], km[6], km[7]);
       } else {
         const int u = t - 256;
         {
@@ -318,13 +303,9 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
             qa[4 * half + 2] = qv.z * rq * fexp(gv.z);
             qa[4 * half + 3] = qv.w * rq * fexp(gv.w);
           }
-          if constexpr (F32) {
-            // fp32 operands keep the natural key order
-            *reinterpret_cast<float4*>(&sm.op.qa[0][r][k0]) = make_float4(qa[0], qa[1], qa[2], qa[3]);
-            *reinterpret_cast<float4*>(&sm.op.qa[0][r][k0 + 16]) = make_float4(qa[4], qa[5], qa[6], qa[7]);
-          } else {
-            store8<F32>(sm.op.qa, r, 32 * kb + 8 * g, qa);
-          }
+          // fp32 operands keep the natural key order
+          *reinterpret_cast<float4*>(&sm.op.qa[r][k0]) = make_float4(qa[0], qa[1], qa[2], qa[3]);
+          *reinterpret_cast<float4*>(&sm.op.qa[r][k0 + 16]) = make_float4(qa[4], qa[5], qa[6], qa[7]);
         }
         {
           // Ka^T and Kl^T: channel cc, rows 8 hf .. 8 hf + 7
@@ -339,8 +320,11 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
             ka[v] = kh * fexp(G);
             kl[v] = kh * fexp(gend - G);
           }
-          store8_hi<F32>(&sm.op.kat[cc][8 * hf], ka);
-          store8<F32>(sm.op.klt, cc, 8 * hf, kl);
+#pragma unroll
+          for (int v = 0; v < 8; v += 4) {
+            *reinterpret_cast<float4*>(&sm.op.kat[cc][8 * hf + v]) = make_float4(ka[v], ka[v + 1], ka[v + 2], ka[v + 3]);
+            *reinterpret_cast<float4*>(&sm.op.klt[cc][8 * hf + v]) = make_float4(kl[v], kl[v + 1], kl[v + 2], kl[v + 3]);
+          }
         }
       }
     }
@@ -349,34 +333,16 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
     // (4) Gram tiles: wave 0 -> A = Kp Km^T (strict lower, times beta_r); wave 1 -> P = Qp Km^T
     if (wave < 2) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (F32) {
-        const float(*X)[OP::OPP] = wave == 0 ? sm.op.kp[0] : sm.op.qp[0];
+      const float(*X)[OP::OPP] = wave == 0 ? sm.op.kp : sm.op.qp;
 #pragma unroll 8
-        for (int kk = 0; kk < kHeadDim / 4; ++kk)
-          acc = mma4(X[lm][4 * kk + lq], sm.op.km[0][lm][4 * kk + lq], acc);
-      } else {
-        const __bf16(*Xh)[OP::OPP] = wave == 0 ? sm.op.kp[0] : sm.op.qp[0];
-        const __bf16(*Xl)[OP::OPP] = wave == 0 ? sm.op.kp[1] : sm.op.qp[1];
-#pragma unroll
-        for (int kb = 0; kb < kHeadDim / 32; ++kb) {
-          const int o = 32 * kb + 8 * lq;
-          acc = mma32s(ld<bf16x8_t>(&Xh[lm][o]), ld<bf16x8_t>(&Xl[lm][o]),
-                       ld<bf16x8_t>(&sm.op.km[0][lm][o]), ld<bf16x8_t>(&sm.op.km[1][lm][o]), acc);
-        }
-      }
+      for (int kk = 0; kk < kHeadDim / 4; ++kk) acc = mma4(X[lm][4 * kk + lq], sm.op.km[lm][4 * kk + lq], acc);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int r = 4 * lq + s, j = lm;
-        if (wave == 0) {
+        if (wave == 0)
           sm.A[r][j] = (j < r) ? sm.beta[r] * acc[s] : 0.f;
-        } else {
-          const float pv = (j <= r) ? acc[s] : 0.f;
-          if constexpr (F32) {
-            sm.op.p[0][r][j] = pv;
-          } else {
-            split_store(&sm.op.p[0][r][j], &sm.op.p[1][r][j], pv);
-          }
-        }
+        else
+          sm.op.p[r][j] = (j <= r) ? acc[s] : 0.f;
       }
     }
     lds_barrier();
@@ -407,108 +373,40 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
       float v4[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) v4[s] = sm.va[4 * lq + s][col];
-      if constexpr (F32) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) Ut = mma4(tt[s], v4[s], Ut);
-      } else {
-        bf16x4_t th, tl, vh, vl;
-        split_vec<4>(tt, th, tl);
-        split_vec<4>(v4, vh, vl);
-        Ut = mma16s(th, tl, vh, vl, Ut);
-      }
+      for (int s = 0; s < 4; ++s) Ut = mma4(tt[s], v4[s], Ut);
     }
 
     // (5c) W^T = Ka^T T^T, tile nt holding W[lm][16 nt + 4 lq + s]: exactly the A operand
     // of W.S in the key order of the state tiles
     f32x4_t Wt[8];
-    {
-      bf16x4_t tb;
-      if constexpr (!F32) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) tb[s] = static_cast<__bf16>(tt[s]);
-      }
+    for (int nt = 0; nt < 8; ++nt) {
+      Wt[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        Wt[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if constexpr (F32) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) Wt[nt] = mma4(sm.op.kat[16 * nt + lm][4 * lq + s], tt[s], Wt[nt]);
-        } else {
-          Wt[nt] = mma16(ld<bf16x4_t>(&sm.op.kat[16 * nt + lm][4 * lq]), tb, Wt[nt]);
-        }
-      }
+      for (int s = 0; s < 4; ++s) Wt[nt] = mma4(sm.op.kat[16 * nt + lm][4 * lq + s], tt[s], Wt[nt]);
     }
 
     // (5d) the state pass on the wave's value tile
     f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (F32) {
+    {
       f32x4_t ws = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int it = 0; it < 8; ++it)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           ws = mma4(Wt[it][s], S[it][s], ws);
-          O = mma4(sm.op.qa[0][lm][16 * it + 4 * lq + s], S[it][s], O);
+          O = mma4(sm.op.qa[lm][16 * it + 4 * lq + s], S[it][s], O);
         }
       f32x4_t U = Ut - ws;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) O = mma4(sm.op.p[0][lm][4 * lq + s], U[s], O);
+      for (int s = 0; s < 4; ++s) O = mma4(sm.op.p[lm][4 * lq + s], U[s], O);
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) S[it][s] *= sm.eg15[16 * it + 4 * lq + s];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) S[it] = mma4(sm.op.klt[0][16 * it + lm][4 * lq + s], U[s], S[it]);
-      }
-    } else {
-      bf16x8_t sh[4], sl[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        float b8[8];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          b8[s] = S[2 * kb][s];
-          b8[4 + s] = S[2 * kb + 1][s];
-        }
-        split_vec<8>(b8, sh[kb], sl[kb]);
-      }
-      // U = U~ - W S
-      f32x4_t ws = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        bf16x8_t wb;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          wb[s] = static_cast<__bf16>(Wt[2 * kb][s]);
-          wb[4 + s] = static_cast<__bf16>(Wt[2 * kb + 1][s]);
-        }
-        ws = mma32(wb, sh[kb], ws);
-      }
-      const f32x4_t U = Ut - ws;
-      bf16x4_t uh, ul;
-      {
-        float u4[4] = {U[0], U[1], U[2], U[3]};
-        split_vec<4>(u4, uh, ul);
-      }
-      // O = Qa S + P U
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int o = 32 * kb + 8 * lq;
-        O = mma32s(ld<bf16x8_t>(&sm.op.qa[0][lm][o]), ld<bf16x8_t>(&sm.op.qa[1][lm][o]), sh[kb],
-                   sl[kb], O);
-      }
-      O = mma16s(ld<bf16x4_t>(&sm.op.p[0][lm][4 * lq]), ld<bf16x4_t>(&sm.op.p[1][lm][4 * lq]), uh,
-                 ul, O);
-      // S = Diag(exp(Gcum_C)) S + Kl^T U
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const float4 e4 = *reinterpret_cast<const float4*>(&sm.eg15[16 * it + 4 * lq]);
-        S[it][0] *= e4.x;
-        S[it][1] *= e4.y;
-        S[it][2] *= e4.z;
-        S[it][3] *= e4.w;
-        S[it] = mma16s(ld<bf16x4_t>(&sm.op.klt[0][16 * it + lm][4 * lq]),
-                       ld<bf16x4_t>(&sm.op.klt[1][16 * it + lm][4 * lq]), uh, ul, S[it]);
+        for (int s = 0; s < 4; ++s) S[it] = mma4(sm.op.klt[16 * it + lm][4 * lq + s], U[s], S[it]);
       }
     }
 
@@ -524,7 +422,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
     stage();  // the next chunk's raw rows, for the next iteration's prologue
     lds_barrier();
     {
-      IO* po = static_cast<IO*>(a.out) + (row0 + 4 * lq) * Hd + static_cast<int64_t>(h) * kHeadDim + col;
+      float* po = static_cast<float*>(a.out) + (row0 + 4 * lq) * Hd + static_cast<int64_t>(h) * kHeadDim + col;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int r = 4 * lq + s;
@@ -533,7 +431,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
 #pragma unroll
           for (int wv = 0; wv < NWAVES; ++wv) tot += sm.ss[buf][wv][r];
           const float rr = 1.0f / sqrtf(tot * (1.0f / kHeadDim) + a.L.rms_eps);
-          store_io(po, 0, nw * O[s] * rr * sm.sg[buf][r][col]);
+          *po = nw * O[s] * rr * sm.sg[buf][r][col];
         }
         po += Hd;
       }
@@ -568,7 +466,7 @@ hipError_t launch_prefill(const PrefillArgs& a, kda_dtype io, const int32_t* ord
   const int nord = a.num_seqs < kMaxOrdered ? a.num_seqs : kMaxOrdered;
   for (int i = 0; i < kMaxOrdered; ++i) ord.idx[i] = i < nord ? order_host[i] : 0;
   const dim3 grid(static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.L.H));
-  hipLaunchKernelGGL(prefill_kernel<float>, grid, dim3(NTHREADS), 0, stream, a, ord);
+  hipLaunchKernelGGL(prefill_kernel, grid, dim3(NTHREADS), 0, stream, a, ord);
   return hipGetLastError();
 }
 

@@ -105,6 +105,7 @@ struct alignas(16) PcSmem {
   float A[C][20];               // G = Kp Km^T (strict lower), for the elimination
   float ss[CWN][C];             // per consumer wave, per row: sum of O^2 over its columns
   float rr[2][C];               // per row: the RMSNorm factor, by chunk parity
+  float nw[kHeadDim];           // the RMSNorm weight (producer epilogue)
   float gbias[kHeadDim];        // low-rank gate: -log2 e exp(A_log) dt_bias per channel
   float eg15n[kHeadDim];        // low-rank gate: e^Gcum_end of the chunk formed ahead
 };
@@ -127,7 +128,8 @@ static_assert(offsetof(PcSmem, kb) % 16 == 0 && sizeof(KBuf) % 16 == 0 &&
                   offsetof(PcSmem, nsq) % 16 == 0 && offsetof(KBuf, beta) % 16 == 0 &&
                   offsetof(KBuf, vk) % 16 == 0 && offsetof(KBuf, rq) % 16 == 0 &&
                   offsetof(PcSmem, kp) % 16 == 0 && offsetof(PcSmem, km) % 16 == 0 &&
-                  offsetof(PcSmem, rr) % 16 == 0 && offsetof(PcSmem, gbias) % 16 == 0,
+                  offsetof(PcSmem, rr) % 16 == 0 && offsetof(PcSmem, gbias) % 16 == 0 &&
+                  offsetof(PcSmem, nw) % 16 == 0,
               "16-byte aligned LDS members");
 
 // Softplus gate: the Gram operands of one level, bf16 hi and lo, 24 rows each (the level's
@@ -223,6 +225,14 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     if (a.pass == kPassTransfer && (kseg == nsegs - 1 || (transfer_m && kseg == 0))) return;
   }
   constexpr bool write_out = !kXfer;  // a.pass == kPassTransfer exactly when kXfer
+  // Where the gated RMSNorm epilogue runs.  With the bounded full-rank gate it runs on the
+  // four q and k producer waves in interval 3, where they are otherwise idle: the consumers
+  // leave each chunk's O rows in the chunk's V buffer (each lane over the very elements of
+  // V it has just read) and go straight on to the state update.  With the softplus or the
+  // low-rank gate those waves have interval-3 work of their own (position pairs, gate
+  // tiles), and the consumers run the epilogue themselves, one chunk late, from per-wave
+  // partial sums of squares that the norm wave turns into row factors.
+  constexpr bool kProdEpi = !kSp && !kFb;
   const bool last_seg = kseg == nsegs - 1;
   const int64_t Hd = static_cast<int64_t>(H) * kHeadDim;
   const int nch = (T + C - 1) / C;
@@ -282,6 +292,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     const float lb2 = kLog2e * a.L.lower_bound;
     const float spb = kLog2e * a.L.dt_bias[c];  // softplus gate: (z + dt_bias) log2 e = z log2 e + spb
     if (kFb && urole == 3) sm.gbias[ch] = kSp ? spb : gb;
+    if (kProdEpi && write_out && urole == 3) sm.nw[ch] = a.L.norm_w[ch];  // both z waves: 128 channels
 
     // Raw rows of a chunk, straight into LDS.  Each wave fetches exactly the slice it reads
     // itself in interval 1 (plane urole, channels 64 hf .. + 63, all 16 rows) as two
@@ -454,6 +465,42 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         const float pv_ = b < a ? psel : (b == a ? dsel : 0.f);
         sm.A[r0 + a][r0 + b] = gv_;
         split_store(&KP.p[r0 + a][il16(r0 + b)], &KP.p[r0 + a][il16(r0 + b) + 4], pv_);
+      }
+    };
+
+    // The gated RMSNorm epilogue of chunk ic (kProdEpi) on the q and k waves in interval 3:
+    // wave w takes rows 4 w .. 4 w + 3, lane l row 4 w + l / 16 and channels 8 (l % 16) ..
+    // + 7.  The consumers left the chunk's rows of O = Qa S + P U in its V buffer; the true
+    // output row is rq O (rq the q row factor), and rq O / sqrt(mean (rq O)^2 + eps) = O rr
+    // with rr = rq / sqrt(rq^2 mean O^2 + eps), the sum of squares taken over the 16 lanes
+    // of a DPP row.  Then times the norm weight and sigmoid(gate), rounded to bf16 and
+    // stored as one 16-byte piece per lane.
+    auto epilogue = [&](int ic) __attribute__((always_inline)) {
+      const KBuf& K = sm.kb[ic & 1];
+      const int r = 4 * uwave + (lane >> 4), c8 = 8 * (lane & 15);
+      const float4 o0 = ld<float4>(&K.V[r][c8]), o1 = ld<float4>(&K.V[r][c8 + 4]);
+      const float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+      const uint4 gr = ld<uint4>(&graw_lds[ic % 3][r][c8]);
+      const float4 w0 = ld<float4>(&sm.nw[c8]), w1 = ld<float4>(&sm.nw[c8 + 4]);
+      const float nw8[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      const uint32_t g2[4] = {gr.x, gr.y, gr.z, gr.w};
+      float ss = 0.f;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) ss = fmaf(o[v], o[v], ss);
+      ss = row_sum16(ss);
+      const float rq = K.rq[r];
+      const float rr = rq * __builtin_amdgcn_rsqf(rq * rq * ss * (1.0f / kHeadDim) + a.L.rms_eps);
+      uint32_t packed[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float ga0 = __uint_as_float(g2[j] << 16), ga1 = __uint_as_float(g2[j] & 0xffff0000u);
+        const float y0 = nw8[2 * j] * o[2 * j] * rr * fsigmoid(ga0);
+        const float y1 = nw8[2 * j + 1] * o[2 * j + 1] * rr * fsigmoid(ga1);
+        packed[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){y0, y1}, bf16x2_t));
+      }
+      if (r < min(C, T - ic * C)) {
+        char* po = static_cast<char*>(a.out) + ((t0 + ic * C + r) * Hd + static_cast<int64_t>(h) * kHeadDim + c8) * 2;
+        *reinterpret_cast<uint4*>(po) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
       }
     };
 
@@ -672,6 +719,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 
       // ---------------------------------------------------------- interval 3
       if (kSp && !kFb && has_next && uwave < 4) pair_blocks((i + 1) & 1);
+      if (kProdEpi && write_out && i >= 0 && uwave < 4) epilogue(i);
       // (softplus gate: level 1 of G and P on the Gram waves, level 2 on waves 7 and 6,
       // so that each SIMD issues one level tile)
       const bool gram_a = uwave == kGramAWave || uwave == 7;
@@ -755,7 +803,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
             }
           }
         } else if (lane < 3 * C) {
-          if (i >= 0 && write_out) {
+          if (!kProdEpi && i >= 0 && write_out) {
             // RMSNorm factor of chunk i's output row r from the consumers' partial sums:
             // the true row is rq O, and rq O / sqrt(mean (rq O)^2 + eps) = O rr with
             // rr = rq / sqrt(rq^2 mean O^2 + eps)
@@ -826,19 +874,34 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     lds_barrier();
     if (kFb) lds_barrier();  // the producers' low-rank gate of chunk 0
 
-    const float nw = a.L.norm_w[col];
+    const float nw = kProdEpi ? 0.f : a.L.norm_w[col];
     bf16x8_t u_l0 = {}, u_hh = {};  // U as the B operands of mma16p
-    // S = Diag(exp(Gcum_C)) S + Kl^T U, once chunk i's U is known
+    // S = Diag(exp(Gcum_C)) S + Kl^T U, once chunk i's U is known.  The factors of key rows
+    // 16 it + 4 lq + s (it = 0..7, s = 0..3) are the same for the 16 lanes of a DPP row:
+    // lane lm reads those of (it, s) = (lm / 2, 2 (lm % 2)) and (lm / 2, 2 (lm % 2) + 1)
+    // (one 8-byte LDS read instead of eight 16-byte ones), and every lane takes each factor
+    // from its owner by row_newbcast inside the multiply.
     auto update_state = [&](const KBuf& K) __attribute__((always_inline)) {
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const float4 e4 = ld<float4>(&K.eg15[16 * it + 4 * lq]);
-        S[it][0] *= e4.x;
-        S[it][1] *= e4.y;
-        S[it][2] *= e4.z;
-        S[it][3] *= e4.w;
+      const float2 e2 = ld<float2>(&K.eg15[16 * (lm >> 1) + 4 * lq + 2 * (lm & 1)]);
+      auto mm = [&](int it) __attribute__((always_inline)) {
         S[it] = mma16p(ld<bf16x8_t>(&K.klt[16 * it + lm][8 * lq]), u_l0, u_hh, S[it]);
-      }
+      };
+      decay_tile<0>(S[0], e2.x, e2.y);
+      mm(0);
+      decay_tile<1>(S[1], e2.x, e2.y);
+      mm(1);
+      decay_tile<2>(S[2], e2.x, e2.y);
+      mm(2);
+      decay_tile<3>(S[3], e2.x, e2.y);
+      mm(3);
+      decay_tile<4>(S[4], e2.x, e2.y);
+      mm(4);
+      decay_tile<5>(S[5], e2.x, e2.y);
+      mm(5);
+      decay_tile<6>(S[6], e2.x, e2.y);
+      mm(6);
+      decay_tile<7>(S[7], e2.x, e2.y);
+      mm(7);
     };
 
     // Gated RMSNorm of chunk ic's output rows O and the store, with the row factors rr
@@ -939,28 +1002,42 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           split_vec<4>(u4, uh, ul);
           b_pair(uh, ul, u_l0, u_hh);
         }
-        // O += P U and the rows' partial sums of squares (not in the Transfer pass)
+        // O += P U and the rows' partial sums of squares (not in the Transfer pass).
+        // Accumulator hand-off between opcodes: O was last written by the fp16 16x16x32
+        // MFMA of interval 1 and is accumulated here by the bf16 16x16x32 one.  The rule
+        // this kernel keeps (see mma16p) is that a dependent accumulation chain never mixes
+        // instructions of different shapes (a 16x16x16 result taken as the accumulator of a
+        // 16x16x32 a few instructions later gave wrong rows); these two have the same shape
+        // and pass count, and a barrier and the U product lie between them.  Every other
+        // chain in the kernel uses a single opcode.
         if (write_out) {
           O = mma16p(ld<bf16x8_t>(&K.p[lm][8 * lq]), u_l0, u_hh, O);
-          float ss[4];
+          if constexpr (kProdEpi) {
+            // the O rows go to the producers' epilogue, over the elements of V this lane
+            // read above (no other lane touches them)
 #pragma unroll
-          for (int s = 0; s < 4; ++s) ss[s] = row_sum16(O[s] * O[s]);
-          if (lm == 0)
-            *reinterpret_cast<float4*>(&sm.ss[cw][4 * lq]) = make_float4(ss[0], ss[1], ss[2], ss[3]);
+            for (int s = 0; s < 4; ++s) K.V[4 * lq + s][col] = O[s];
+          } else {
+            float ss[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) ss[s] = row_sum16(O[s] * O[s]);
+            if (lm == 0)
+              *reinterpret_cast<float4*>(&sm.ss[cw][4 * lq]) = make_float4(ss[0], ss[1], ss[2], ss[3]);
+          }
         }
 
       }
       lds_barrier();
 
       // ---------------------------------------------------------- interval 3
-      if (i >= 1 && write_out) emit(i - 1, Oprev);
+      if (!kProdEpi && i >= 1 && write_out) emit(i - 1, Oprev);
       if (i >= 0) {
         update_state(K);
       }
       lds_barrier();
       Oprev = O;
     }
-    if (nch > 0 && write_out) emit(nch - 1, Oprev);
+    if (!kProdEpi && nch > 0 && write_out) emit(nch - 1, Oprev);
 
     float* dst = nullptr;
     if (a.pass == kPassTransfer)

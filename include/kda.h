@@ -140,7 +140,15 @@ size_t kda_prefill_workspace_bytes(const kda_layer* layer, kda_dtype io, int32_t
  *             with less, the whole-sequence path runs (same results up to rounding).  The
  *             library keeps nothing in it after the call's work completes.
  * Partial overlap between inputs and outputs is invalid.  State pointers and q, k, v, z,
- * gate must be 16-byte aligned (the kernel reads activation rows in 16-byte pieces).
+ * gate and out must be 16-byte aligned (the kernels move activation rows in 16-byte
+ * pieces).
+ * Range (bf16 io): the state pass multiplies fp16 operands, so every state entry (start,
+ * intermediate and final) and log2(e) times every SiLU conv output of q and k must stay
+ * below 65504 in magnitude -- about 45,000 for the conv outputs themselves.  Past that
+ * the outputs and the final state are not finite (inf or NaN, never finite wrong
+ * values); nothing is checked on the host.  State entries are bounded by about
+ * sqrt(d) * max |v| plus the start state's, since the keys are unit vectors and beta <= 1.
+ * fp32 io and the decode entry points compute in fp32 throughout and have fp32's range.
  */
 kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
                        const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,

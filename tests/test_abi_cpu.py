@@ -145,10 +145,10 @@ def test_prefill_scan_validation():
     kda, lib = _lib()
     lay = _layer(kda)
 
-    def scan(cu, total, q=FAKE, lb_layer=None):
+    def scan(cu, total, q=FAKE, lb_layer=None, out=FAKE):
         cu = np.ascontiguousarray(cu, dtype=np.int32)
         return lib.kda_prefill_scan(ctypes.byref(lb_layer or lay), 1, len(cu) - 1, FAKE,
-                                    cu.ctypes.data, total, q, *([FAKE] * 5), None, None, FAKE,
+                                    cu.ctypes.data, total, q, *([FAKE] * 5), None, None, out,
                                     None, None, None)
 
     assert scan([0, 5, 3], 3) == 1             # decreasing
@@ -156,6 +156,7 @@ def test_prefill_scan_validation():
     assert scan([0, 5], 6) == 1                # total mismatch
     assert scan([0, 5], 5, q=0) == 1           # null activation
     assert scan([0, 5], 5, q=FAKE + 2) == 1    # misaligned activation
+    assert scan([0, 5], 5, out=FAKE + 2) == 1  # misaligned output
     assert lib.kda_prefill_scan(ctypes.byref(lay), 1, 0, None, None, 0, *([None] * 11), None) == 0
 
 

@@ -3,8 +3,9 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synthetic
-from kda_testutil import D, assert_close, check_all_units, oracle_units
+from kda_testutil import D, assert_close, check_all_units, head_layer, io_code, oracle_units, unit_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -292,3 +293,34 @@ def test_varlen16_h64_then_decode():
     check_all_units(dprob, outs.transpose(0, 1).reshape(N * steps, Hd).cpu(), st.cpu(),
                     _all_units(dprob), "varlen16_h64 decode continuation", batch=64)
 
+
+def test_fp16_operand_range():
+    """Activations 8192x larger than the configs' (raw q, k, v and the ring scaled up) and a
+    quarter of the channels at g = 0, so that the state accumulates: the state pass's fp16
+    operands -- the state itself and log2(e) times the SiLU conv outputs of q and k -- reach
+    over half of fp16's largest finite value 65504 (asserted below from the oracle's trace)
+    while staying under it.  Whole-sequence and segment-parallel paths, every unit against
+    the oracle."""
+    scale = 8192.0
+    prob = synthetic.make_prefill([600, 300], H=2, io="bf16", seed=302, device=DEV,
+                                  init_state=True, init_ring=True)
+    for name in ("q", "k", "v"):
+        prob[name] = (prob[name].float() * scale).to(torch.bfloat16)
+    prob["ring_in"] *= scale
+    z = prob["z"].view(900, 2, D)
+    z[:, :, ::4] = -1e4
+    # the regime, from the oracle's trace of one unit: SiLU outputs (v, whose distribution
+    # q and k share) and state entries
+    acts, st, rg = unit_inputs(prob, 0, 0)
+    tr = oracle.prefill_units(head_layer(prob["layer"], 0), io_code(torch.bfloat16), [0, 600],
+                              acts["q"], acts["k"], acts["v"], acts["z"], acts["beta"], acts["gate"],
+                              st, rg, units=[(0, 0)], nthreads=1, trace=True)["trace"]
+    assert np.abs(tr["v"]).max() * 1.4426950408889634 > 0.5 * 65504
+    assert np.abs(tr["S"]).max() > 8000
+    kda = _kda()
+    assert kda.prefill_workspace_bytes(kda.Layer(**prob["layer"]), torch.bfloat16, prob["cu_seqlens"]) > 0
+    for split in (False, True):
+        out, state, ring = _prefill(prob, allow_split=split)
+        assert torch.isfinite(out.float()).all() and torch.isfinite(state).all()
+        check_all_units(prob, out.cpu(), state.cpu(), _all_units(prob),
+                        f"fp16_range ({'segment-parallel' if split else 'whole-sequence'})", ring=ring.cpu())
