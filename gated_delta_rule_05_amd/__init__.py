@@ -9,9 +9,9 @@ is the thin Python binding used by the tests and the benchmark.
     out = decode_multi(layer, q, k, v, z, beta, gate, state_in, ring_in, state_out, ring_out, ntok)
 """
 from ._binding import (ABI_VERSION, EXPORTED, GATE_BOUNDED, GATE_SOFTPLUS, HEAD_DIM, CONV_KERNEL,
-                       KdaError, Layer, LIB_PATH,
+                       KdaError, Layer, LIB_PATH, NOALLOC_SCRATCH_BYTES,
                        decode_multi, decode_step, load, prefill, prefill_workspace_bytes)
 
 __all__ = ["ABI_VERSION", "EXPORTED", "GATE_BOUNDED", "GATE_SOFTPLUS", "HEAD_DIM", "CONV_KERNEL",
-           "KdaError", "Layer", "LIB_PATH", "decode_multi", "decode_step", "load", "prefill",
+           "KdaError", "Layer", "LIB_PATH", "NOALLOC_SCRATCH_BYTES", "decode_multi", "decode_step", "load", "prefill",
            "prefill_workspace_bytes"]

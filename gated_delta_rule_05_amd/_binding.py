@@ -20,10 +20,11 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP
 KDA_F32, KDA_BF16 = 0, 1
 ABI_VERSION = 5
 HEAD_DIM = 128
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 CONV_KERNEL = 4
 
-EXPORTED = ("kda_prefill_workspace_bytes", "kda_prefill", "kda_prefill_scan", "kda_decode_step",
-            "kda_decode_multi",
+EXPORTED = ("kda_prefill_workspace_bytes", "kda_prefill", "kda_prefill_noalloc", "kda_prefill_scan",
+            "kda_decode_step", "kda_decode_multi",
             "kda_status_string", "kda_last_error", "kda_abi_version")
 
 
@@ -70,6 +71,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.kda_prefill_workspace_bytes.argtypes = [lp, ctypes.c_int, i32, vp, i64]
         lib.kda_prefill.restype = ctypes.c_int
         lib.kda_prefill.argtypes = [lp, ctypes.c_int, i32, vp, vp, i64] + [vp] * 11 + [vp, sz, vp]
+        lib.kda_prefill_noalloc.restype = ctypes.c_int
+        lib.kda_prefill_noalloc.argtypes = [lp, ctypes.c_int, i32, vp, vp, i64] + [vp] * 11 + [vp]
         lib.kda_decode_step.restype = ctypes.c_int
         lib.kda_decode_step.argtypes = [lp, ctypes.c_int, i32] + [vp] * 9 + [vp]
         lib.kda_prefill_scan.restype = ctypes.c_int
@@ -165,7 +168,7 @@ def prefill_workspace_bytes(layer: Layer, io_dtype: torch.dtype, cu_seqlens_host
 def prefill(layer: Layer, q, k, v, z, beta, gate, cu_seqlens, cu_seqlens_host=None,
             state_in=None, ring_in=None, out=None, state_out=None, ring_out=None,
             final_state: bool = True, workspace=None, allow_split: bool = True, scan: bool = False,
-            stream=None):
+            noalloc: bool = False, stream=None):
     """Chunked prefill over packed sequences (see kda_prefill in include/kda.h).
 
     q, k, v, z, gate: [T, H*128] io (fp32 or bf16); beta: [T, H] io.  cu_seqlens: int32
@@ -175,7 +178,8 @@ def prefill(layer: Layer, q, k, v, z, beta, gate, cu_seqlens, cu_seqlens_host=No
     (segment-parallel path for few (sequence, head) units) is allocated when not given;
     allow_split=False passes none, so the whole-sequence path runs.  scan=True runs the
     sequential-scan arm instead (kda_prefill_scan: token by token, bit-identical to decode
-    steps).
+    steps).  noalloc=True calls kda_prefill_noalloc: no workspace; the segment-parallel path
+    uses the library's own scratch array.
     """
     lib = load()
     dev = layer.device
@@ -208,6 +212,12 @@ def prefill(layer: Layer, q, k, v, z, beta, gate, cu_seqlens, cu_seqlens_host=No
         _need(state_out, "state_out", (N, H, HEAD_DIM, HEAD_DIM), torch.float32, dev)
     if ring_out is not None:
         _need(ring_out, "ring_out", (N, 3 * Hd, CONV_KERNEL - 1), torch.float32, dev)
+    if noalloc:
+        _check(lib.kda_prefill_noalloc(ctypes.byref(layer.c), io, N, _ptr(cu_seqlens), _ptr(cu_h), T,
+                                       _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(gate),
+                                       _ptr(state_in), _ptr(ring_in), _ptr(out), _ptr(state_out),
+                                       _ptr(ring_out), _stream_handle(stream)))
+        return out, state_out, ring_out
     if scan:
         _check(lib.kda_prefill_scan(ctypes.byref(layer.c), io, N, _ptr(cu_seqlens), _ptr(cu_h), T,
                                     _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(gate),

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_pc.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_pc.hip", "kda_noalloc.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-munsafe-fp-atomics"]

@@ -4,9 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <numeric>
 #include <string>
-#include <vector>
 
 #include "kda_internal.h"
 
@@ -131,6 +129,93 @@ bool make_split_plan(const kda_layer* L, kda_dtype io, int32_t N, const int32_t*
   return true;
 }
 
+// kda_prefill and kda_prefill_noalloc: the same checks and launches; they differ only in
+// where the segment-parallel path's workspace comes from (the caller's buffer, or the
+// library's scratch array).  No device memory is allocated, and on success no host heap
+// memory either (the launch order lives on the stack).
+kda_status prefill_impl(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
+                        const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                        int64_t total_tokens, const void* q, const void* k, const void* v,
+                        const void* z, const void* beta, const void* gate, const float* state_in,
+                        const float* ring_in, void* out, float* state_out, float* ring_out,
+                        void* workspace, size_t workspace_bytes, bool noalloc, hipStream_t stream) {
+  kda_status st = check_layer(layer, true);
+  if (st != KDA_OK) return st;
+  if (!io_ok(io)) return fail(KDA_ERR_INVALID_ARG, "unknown io dtype %d", static_cast<int>(io));
+  if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (num_seqs == 0) {
+    if (total_tokens != 0) return fail(KDA_ERR_INVALID_ARG, "no sequences but total_tokens != 0");
+    return ok();
+  }
+  st = check_packed(num_seqs, cu_seqlens_dev, cu_seqlens_host, total_tokens, q, k, v, z, beta,
+                    gate, out, state_in, state_out);
+  if (st != KDA_OK) return st;
+  if (workspace_bytes > 0 && !workspace)
+    return fail(KDA_ERR_WORKSPACE, "workspace is NULL but workspace_bytes = %zu", workspace_bytes);
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (static_cast<int64_t>(num_seqs) * layer->num_heads > 0x7fffffffLL)
+    return fail(KDA_ERR_INVALID_ARG, "num_seqs * num_heads exceeds the grid limit");
+
+  kda::PrefillArgs a;
+  a.L = layer_params(layer);
+  a.num_seqs = num_seqs;
+  a.cu_seqlens = cu_seqlens_dev;
+  a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.gate = gate;
+  a.state_in = state_in;
+  a.ring_in = ring_in;
+  a.out = out;
+  a.state_out = state_out;
+  a.ring_out = ring_out;
+  // The fp32-io chunked kernel has neither the softplus gate nor the low-rank gate: with
+  // either, fp32 io runs the scan.
+  if (io == KDA_F32 && (layer->gate_kind == KDA_GATE_SOFTPLUS || layer->f_b))
+    return kda_prefill_scan(layer, io, num_seqs, cu_seqlens_dev, cu_seqlens_host, total_tokens,
+                            q, k, v, z, beta, gate, state_in, ring_in, out, state_out, ring_out,
+                            stream);
+  a.pass = kda::kPassWhole;
+  a.seg_b = a.seg_m = a.seg_start = nullptr;
+
+  kda::SplitPlan plan;
+  size_t need = 0;
+  hipError_t e;
+  bool split = make_split_plan(layer, io, num_seqs, cu_seqlens_host, &plan, &need);
+  if (split && noalloc) {
+    if (need > kda::kNoAllocScratchBytes)
+      return fail(KDA_ERR_WORKSPACE, "the segment-parallel plan needs %zu bytes of scratch, more than the %zu "
+                  "bytes kda_prefill_noalloc holds", need, kda::kNoAllocScratchBytes);
+    e = kda::noalloc_scratch(stream, &workspace);
+    if (e != hipSuccess)
+      return fail(KDA_ERR_HIP, "scratch lookup failed: %s", hipGetErrorString(e));
+    workspace_bytes = kda::kNoAllocScratchBytes;
+  }
+  split = split && workspace_bytes >= need;
+  if (split) {
+    const size_t plane = static_cast<size_t>(plan.nseg) * layer->num_heads * kda::kHeadDimHost *
+                         kda::kHeadDimHost;
+    float* ws = static_cast<float*>(workspace);
+    a.seg_b = ws;
+    a.seg_m = ws + plane;
+    a.seg_start = ws + 2 * plane;
+    e = kda::launch_prefill_bf16_split(a, plan, stream);
+  } else {
+    // Longest sequences first, so the long serial chains start early (the launch orders
+    // at most kMaxOrdered of them; ties keep their index order).
+    int32_t order[kda::kMaxOrdered];
+    const int32_t nord = std::min<int32_t>(num_seqs, kda::kMaxOrdered);
+    for (int32_t i = 0; i < nord; ++i) order[i] = i;
+    if (num_seqs <= kda::kMaxOrdered)
+      std::sort(order, order + nord, [&](int32_t x, int32_t y) {
+        const int32_t lx = cu_seqlens_host[x + 1] - cu_seqlens_host[x];
+        const int32_t ly = cu_seqlens_host[y + 1] - cu_seqlens_host[y];
+        return lx != ly ? lx > ly : x < y;
+      });
+    e = kda::launch_prefill(a, io, order, stream);
+  }
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -223,67 +308,20 @@ kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
                        const void* z, const void* beta, const void* gate, const float* state_in,
                        const float* ring_in, void* out, float* state_out, float* ring_out,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  kda_status st = check_layer(layer, true);
-  if (st != KDA_OK) return st;
-  if (!io_ok(io)) return fail(KDA_ERR_INVALID_ARG, "unknown io dtype %d", static_cast<int>(io));
-  if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 0");
-  if (num_seqs == 0) {
-    if (total_tokens != 0) return fail(KDA_ERR_INVALID_ARG, "no sequences but total_tokens != 0");
-    return ok();
-  }
-  st = check_packed(num_seqs, cu_seqlens_dev, cu_seqlens_host, total_tokens, q, k, v, z, beta,
-                    gate, out, state_in, state_out);
-  if (st != KDA_OK) return st;
-  if (workspace_bytes > 0 && !workspace)
-    return fail(KDA_ERR_WORKSPACE, "workspace is NULL but workspace_bytes = %zu", workspace_bytes);
-  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
-    return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (static_cast<int64_t>(num_seqs) * layer->num_heads > 0x7fffffffLL)
-    return fail(KDA_ERR_INVALID_ARG, "num_seqs * num_heads exceeds the grid limit");
+  return prefill_impl(layer, io, num_seqs, cu_seqlens_dev, cu_seqlens_host, total_tokens, q, k, v, z,
+                      beta, gate, state_in, ring_in, out, state_out, ring_out, workspace,
+                      workspace_bytes, false, stream);
+}
 
-  // Longest sequences first, so the long serial chains start early.
-  std::vector<int32_t> order(num_seqs);
-  std::iota(order.begin(), order.end(), 0);
-  if (num_seqs <= kda::kMaxOrdered)
-    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
-      return cu_seqlens_host[x + 1] - cu_seqlens_host[x] > cu_seqlens_host[y + 1] - cu_seqlens_host[y];
-    });
-
-  kda::PrefillArgs a;
-  a.L = layer_params(layer);
-  a.num_seqs = num_seqs;
-  a.cu_seqlens = cu_seqlens_dev;
-  a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.gate = gate;
-  a.state_in = state_in;
-  a.ring_in = ring_in;
-  a.out = out;
-  a.state_out = state_out;
-  a.ring_out = ring_out;
-  // The fp32-io chunked kernel has neither the softplus gate nor the low-rank gate: with
-  // either, fp32 io runs the scan.
-  if (io == KDA_F32 && (layer->gate_kind == KDA_GATE_SOFTPLUS || layer->f_b))
-    return kda_prefill_scan(layer, io, num_seqs, cu_seqlens_dev, cu_seqlens_host, total_tokens,
-                            q, k, v, z, beta, gate, state_in, ring_in, out, state_out, ring_out,
-                            stream);
-  a.pass = kda::kPassWhole;
-  a.seg_b = a.seg_m = a.seg_start = nullptr;
-
-  kda::SplitPlan plan;
-  size_t need = 0;
-  hipError_t e;
-  if (make_split_plan(layer, io, num_seqs, cu_seqlens_host, &plan, &need) && workspace_bytes >= need) {
-    const size_t plane = static_cast<size_t>(plan.nseg) * layer->num_heads * kda::kHeadDimHost *
-                         kda::kHeadDimHost;
-    float* ws = static_cast<float*>(workspace);
-    a.seg_b = ws;
-    a.seg_m = ws + plane;
-    a.seg_start = ws + 2 * plane;
-    e = kda::launch_prefill_bf16_split(a, plan, stream);
-  } else {
-    e = kda::launch_prefill(a, io, order.data(), stream);
-  }
-  if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
-  return ok();
+kda_status kda_prefill_noalloc(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
+                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                               int64_t total_tokens, const void* q, const void* k, const void* v,
+                               const void* z, const void* beta, const void* gate,
+                               const float* state_in, const float* ring_in, void* out,
+                               float* state_out, float* ring_out, hipStream_t stream) {
+  return prefill_impl(layer, io, num_seqs, cu_seqlens_dev, cu_seqlens_host, total_tokens, q, k, v, z,
+                      beta, gate, state_in, ring_in, out, state_out, ring_out, nullptr, 0, true,
+                      stream);
 }
 
 kda_status kda_prefill_scan(const kda_layer* layer, kda_dtype io, int32_t num_seqs,

@@ -79,6 +79,15 @@ struct SplitPlan {
   int32_t first[kMaxSplitSeqs + 1];  // first segment of each sequence; first[N] = nseg
 };
 
+// The scratch array of kda_prefill_noalloc: the largest workspace any segment-parallel
+// plan needs (3 states of 64 KiB for at most 340 (segment, head) pairs, since the plan
+// only applies below 96 (sequence, head) units and cuts each into ceil(256 / units)
+// segments at most), rounded up.
+constexpr size_t kNoAllocScratchBytes = size_t{64} << 20;
+static_assert(kNoAllocScratchBytes == KDA_NOALLOC_SCRATCH_BYTES, "the header's figure");
+// Device address of the calling stream's GPU's copy of that array (looked up once per device).
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
+
 hipError_t launch_decode(const DecodeArgs& a, kda_dtype io, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, kda_dtype io, const int32_t* order_host,
                           hipStream_t stream);

@@ -158,6 +158,29 @@ kda_status kda_prefill(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kda_prefill for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, checks
+ * and results as kda_prefill, without the workspace: when the segment-parallel path
+ * applies, its per-segment states live in a device array the library holds, of
+ * KDA_NOALLOC_SCRATCH_BYTES per GPU (allocated when the library's code is loaded on that
+ * GPU, kept until the process ends; every plan of the path fits in it, and a plan that
+ * would need more -- none does -- returns KDA_ERR_WORKSPACE with nothing written).
+ * Results are bit-identical to kda_prefill given a large enough workspace.  The call
+ * makes no device allocation; its first call on each GPU looks up that GPU's array
+ * (hipGetSymbolAddress), which must not happen during graph capture, so make one
+ * call per GPU before capturing.  All calls on one GPU share its array: calls that
+ * overlap on one GPU (concurrent streams, or host threads) race and must be serialised
+ * by the caller.  The stream's device is the GPU used.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+kda_status kda_prefill_noalloc(const kda_layer* layer, kda_dtype io, int32_t num_seqs,
+                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                               int64_t total_tokens, const void* q, const void* k, const void* v,
+                               const void* z, const void* beta, const void* gate,
+                               const float* state_in, const float* ring_in, void* out,
+                               float* state_out, float* ring_out, hipStream_t stream);
+
+/*
  * Sequential-scan prefill: the same packed problem and buffers as kda_prefill (no
  * workspace), run token by token by the decode kernel over register-resident state
  * (memra_engine::kda's prefill arrangement, memra_kda_scan_s128, which serves prefill and

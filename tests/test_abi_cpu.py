@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    assert names == sorted(["kda_prefill_workspace_bytes", "kda_prefill", "kda_prefill_scan",
+    assert names == sorted(["kda_prefill_workspace_bytes", "kda_prefill", "kda_prefill_noalloc", "kda_prefill_scan",
                             "kda_decode_step", "kda_decode_multi", "kda_status_string",
                             "kda_last_error", "kda_abi_version"])
 
@@ -131,6 +131,24 @@ def test_prefill_validation():
     assert _prefill(lib, _layer(kda, head_dim=256), [0, 4], 4) == 2
     # zero sequences is a no-op
     assert lib.kda_prefill(ctypes.byref(L), 1, 0, None, None, 0, *([None] * 11), None, 0, None) == 0
+
+
+def test_prefill_noalloc_validation():
+    """kda_prefill_noalloc checks its arguments like kda_prefill, before any launch or
+    scratch lookup."""
+    kda, lib = _lib()
+    L = _layer(kda)
+
+    def call(cu, total, layer=L, out=FAKE):
+        cu = np.ascontiguousarray(cu, dtype=np.int32)
+        return lib.kda_prefill_noalloc(ctypes.byref(layer), 1, len(cu) - 1, FAKE, cu.ctypes.data,
+                                       total, *([FAKE] * 6), None, None, out, None, None, None)
+
+    assert call([0, 5, 3], 3) == 1                      # decreasing
+    assert call([0, 5, 9], 8) == 1                      # total mismatch
+    assert call([0, 4], 4, out=FAKE + 2) == 1           # misaligned output
+    assert call([0, 4], 4, layer=_layer(kda, lb=-6.0)) == 2  # beyond the tile bound
+    assert lib.kda_prefill_noalloc(ctypes.byref(L), 1, 0, None, None, 0, *([None] * 11), None) == 0
 
 
 def test_workspace_query_is_host_only():
