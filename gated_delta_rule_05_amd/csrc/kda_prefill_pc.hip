@@ -34,6 +34,8 @@
 // Three LDS barriers per chunk.  With 16 waves per workgroup each SIMD holds two producer
 // and two consumer waves, so the VALU-heavy and MFMA-heavy halves hide each other's
 // latencies.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_mfma.h"
@@ -59,6 +61,18 @@ constexpr int kGramPWave = 5;
 // low-rank gate, where every producer wave forms a tile of the gate in interval 3).
 constexpr int kNormWave = 6;
 constexpr int NT = 64 * (PW + CWN);
+// With the bounded full-rank gate the state pass runs on 4 consumer waves of two 16-column
+// value tiles each (12 waves per workgroup): every A operand a consumer reads from LDS (Qa,
+// Ka, T, P, Kl^T) then serves two tiles, which halves those reads, and with 3 waves per
+// SIMD a wave may hold 168 registers, room for the 64 state values.  The other variants
+// keep 8 consumer waves of one tile (16 waves).
+template <bool kSp, bool kFb>
+struct PcShape {
+  static constexpr bool kWide = !kSp && !kFb;
+  static constexpr int kCT = kWide ? 2 : 1;        // value tiles per consumer wave
+  static constexpr int kCwn = CWN / kCT;           // consumer waves
+  static constexpr int kNt = 64 * (PW + kCwn);     // threads per workgroup
+};
 constexpr int LDP = 132;               // fp32 row stride of [16][128] arrays
 constexpr int OPP = 136;               // bf16 row stride of [16][128] operands
 constexpr int ILP = 40;                // bf16 row stride of interleaved hi/lo [.][16] operands
@@ -181,7 +195,9 @@ __device__ __forceinline__ float softplus_gate2(float z, float spb, float ascale
 // kXfer: the Transfer pass of the segment-parallel path, which forms end states only: the
 // q plane and everything built from it (Qa, P, O, the output rows) are left out.
 template <bool kFb, bool kSp, bool kXfer>
-__global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder order, SplitPlan plan) {
+__global__ __launch_bounds__((PcShape<kSp, kFb>::kNt)) void prefill_pc_kernel(PrefillArgs a, PcOrder order, SplitPlan plan) {
+  using Shape = PcShape<kSp, kFb>;
+  constexpr int kCT = Shape::kCT;
   __shared__ PcSmem sm;
   // raw rows of q, k, v, z of the next chunk, as [plane][channel half][row][64]: producer
   // wave w reads and refills slice [w / 2][w % 2] only
@@ -250,7 +266,8 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
   const int64_t c = static_cast<int64_t>(h) * kHeadDim + ch;
   // consumers: value tile cw, column col
   const int cw = wave - PW;
-  const int col = 16 * (cw & (CWN - 1)) + lm;
+  // (value column of tile j: col + 16 j)
+  const int col = 16 * kCT * (cw & (Shape::kCwn - 1)) + lm;
 
   if (producer) {
     // ============================================================== producer waves
@@ -543,6 +560,14 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
 #pragma unroll
           for (int r = 0; r < C; ++r) xr[r] = raw_lds[urole][hf][r][lane];
         }
+        if (t < C) KN.beta[t] = (t < Ln) ? fsigmoid(bf16_to_f32(braw)) : 0.f;
+        // this wave's raw slice is read: refill it with chunk i + 2 at once (the reads are
+        // complete before the transfer is issued), so that the transfer's issue overlaps
+        // the arithmetic below instead of following it
+        if (i + 2 < nch && !(kFb && urole == 3)) {
+          lds_wait();
+          prefetch((i + 2) * C);
+        }
         const bool full = Ln == C;
         if (urole == 2 && transfer_m) {
           // the transfer matrix is the end state from the identity with v = 0
@@ -554,15 +579,27 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         } else if (urole < 3) {
           float(*dst)[LDP] = urole == 0 ? sm.aq : urole == 1 ? sm.ak : KN.V;
           if (full) {
+            // Staged over the 16 rows: every conv sum, then every exponential, then every
+            // reciprocal, then the products.  The history is a pure shift, so the rows are
+            // independent and 16 chains interleave instead of the few a row-by-row loop
+            // leaves the scheduler.
+            float xs[C + 3], ys[C], ev[C];
+            xs[0] = hist[0];
+            xs[1] = hist[1];
+            xs[2] = hist[2];
 #pragma unroll
-            for (int r = 0; r < C; ++r) {
-              const float x = bf16_to_f32(xr[r]);
-              const float ys = w[3] * x + w[0] * hist[0] + w[1] * hist[1] + w[2] * hist[2];
-              hist[0] = hist[1];
-              hist[1] = hist[2];
-              hist[2] = x;
-              dst[r][ch] = ys * frcp(1.0f + fexp2(ys));
-            }
+            for (int r = 0; r < C; ++r) xs[r + 3] = bf16_to_f32(xr[r]);
+#pragma unroll
+            for (int r = 0; r < C; ++r) ys[r] = w[3] * xs[r + 3] + w[0] * xs[r] + w[1] * xs[r + 1] + w[2] * xs[r + 2];
+            hist[0] = xs[C];
+            hist[1] = xs[C + 1];
+            hist[2] = xs[C + 2];
+#pragma unroll
+            for (int r = 0; r < C; ++r) ev[r] = fexp2(ys[r]);
+#pragma unroll
+            for (int r = 0; r < C; ++r) ev[r] = frcp(1.0f + ev[r]);
+#pragma unroll
+            for (int r = 0; r < C; ++r) dst[r][ch] = ys[r] * ev[r];
           } else {
 #pragma unroll
             for (int r = 0; r < C; ++r) {
@@ -589,9 +626,13 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
           };
           float G = 0.f, G7 = 0.f;
           if (full) {
+            // every row's decay first (independent chains), then the running sum
+            float gv[C];
+#pragma unroll
+            for (int r = 0; r < C; ++r) gv[r] = gate2(xr[r]);
 #pragma unroll
             for (int r = 0; r < C; ++r) {
-              G += gate2(xr[r]);
+              G += gv[r];
               sm.gam[r][ch] = G;
               if (r == C / 2 - 1) G7 = G;
             }
@@ -610,13 +651,6 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
             sm.eg7[ch] = fexp2(G7);
             sm.e157[ch] = fexp2(G - G7);
           }
-        }
-        if (t < C) KN.beta[t] = (t < Ln) ? fsigmoid(bf16_to_f32(braw)) : 0.f;
-        // this wave's raw slice is consumed: refill it with chunk i + 2 (the reads are
-        // complete before the transfer is issued)
-        if (i + 2 < nch && !(kFb && urole == 3)) {
-          lds_wait();
-          prefetch((i + 2) * C);
         }
         // low-rank gate: chunk i + 3's z_low rows (their buffer's chunk i + 1 was read in the
         // previous interval 3), waited for with this wave's other transfers
@@ -836,7 +870,9 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     }
   } else {
     // ============================================================== consumer waves
-    f32x4_t S[8];
+    // kCT value tiles of 16 columns per wave (tile j: columns col + 16 j), each the fp32
+    // 128 x 16 block of the state as 8 MFMA accumulator tiles
+    f32x4_t S[kCT][8];
     constexpr int64_t kDD = kHeadDim * kHeadDim;
     const int64_t nbase = (static_cast<int64_t>(n) * H + h) * kDD;    // [N][H] planes
     const int64_t sgbase = (static_cast<int64_t>(seg) * H + h) * kDD; // [segments][H] planes
@@ -852,60 +888,68 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     if (src) {
       const float* sp = src + opaque(4 * lq * kHeadDim + col);
 #pragma unroll
-      for (int it = 0; it < 8; ++it)
+      for (int j = 0; j < kCT; ++j)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) S[it][s] = sp[(16 * it + s) * kHeadDim];
+        for (int it = 0; it < 8; ++it)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) S[j][it][s] = sp[(16 * it + s) * kHeadDim + 16 * j];
       if (a.pass == kPassTransfer && !transfer_m) {
         // segment 0 (the Transfer pass skips a sequence's last segment, so the sequence
         // has several): keep the start state where the Final pass reads it, in segment
         // 0's start plane, which the combine never writes
         float* cp = a.seg_start + sgbase + opaque(4 * lq * kHeadDim + col);
 #pragma unroll
-        for (int it = 0; it < 8; ++it)
+        for (int j = 0; j < kCT; ++j)
 #pragma unroll
-          for (int s = 0; s < 4; ++s) cp[(16 * it + s) * kHeadDim] = S[it][s];
+          for (int it = 0; it < 8; ++it)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) cp[(16 * it + s) * kHeadDim + 16 * j] = S[j][it][s];
       }
     } else {
 #pragma unroll
-      for (int it = 0; it < 8; ++it)
+      for (int j = 0; j < kCT; ++j)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) S[it][s] = (transfer_m && 16 * it + 4 * lq + s == col) ? 1.f : 0.f;
+        for (int it = 0; it < 8; ++it)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) S[j][it][s] = (transfer_m && 16 * it + 4 * lq + s == col + 16 * j) ? 1.f : 0.f;
     }
     lds_barrier();
     if (kFb) lds_barrier();  // the producers' low-rank gate of chunk 0
 
     const float nw = kProdEpi ? 0.f : a.L.norm_w[col];
-    bf16x8_t u_l0 = {}, u_hh = {};  // U as the B operands of mma16p
+    bf16x8_t u_l0[kCT] = {}, u_hh[kCT] = {};  // U of each tile as the B operands of mma16p
     // S = Diag(exp(Gcum_C)) S + Kl^T U, once chunk i's U is known.  The factors of key rows
     // 16 it + 4 lq + s (it = 0..7, s = 0..3) are the same for the 16 lanes of a DPP row:
     // lane lm reads those of (it, s) = (lm / 2, 2 (lm % 2)) and (lm / 2, 2 (lm % 2) + 1)
     // (one 8-byte LDS read instead of eight 16-byte ones), and every lane takes each factor
-    // from its owner by row_newbcast inside the multiply.
+    // from its owner by row_newbcast inside the multiply.  Each Kl^T operand serves every
+    // tile of the wave.
     auto update_state = [&](const KBuf& K) __attribute__((always_inline)) {
       const float2 e2 = ld<float2>(&K.eg15[16 * (lm >> 1) + 4 * lq + 2 * (lm & 1)]);
       auto mm = [&](int it) __attribute__((always_inline)) {
-        S[it] = mma16p(ld<bf16x8_t>(&K.klt[16 * it + lm][8 * lq]), u_l0, u_hh, S[it]);
+        const bf16x8_t kl = ld<bf16x8_t>(&K.klt[16 * it + lm][8 * lq]);
+#pragma unroll
+        for (int j = 0; j < kCT; ++j) S[j][it] = mma16p(kl, u_l0[j], u_hh[j], S[j][it]);
       };
-      decay_tile<0>(S[0], e2.x, e2.y);
-      mm(0);
-      decay_tile<1>(S[1], e2.x, e2.y);
-      mm(1);
-      decay_tile<2>(S[2], e2.x, e2.y);
-      mm(2);
-      decay_tile<3>(S[3], e2.x, e2.y);
-      mm(3);
-      decay_tile<4>(S[4], e2.x, e2.y);
-      mm(4);
-      decay_tile<5>(S[5], e2.x, e2.y);
-      mm(5);
-      decay_tile<6>(S[6], e2.x, e2.y);
-      mm(6);
-      decay_tile<7>(S[7], e2.x, e2.y);
-      mm(7);
+      auto dec = [&](auto tag) __attribute__((always_inline)) {
+        constexpr int IT = decltype(tag)::value;
+#pragma unroll
+        for (int j = 0; j < kCT; ++j) decay_tile<IT>(S[j][IT], e2.x, e2.y);
+        mm(IT);
+      };
+      dec(std::integral_constant<int, 0>{});
+      dec(std::integral_constant<int, 1>{});
+      dec(std::integral_constant<int, 2>{});
+      dec(std::integral_constant<int, 3>{});
+      dec(std::integral_constant<int, 4>{});
+      dec(std::integral_constant<int, 5>{});
+      dec(std::integral_constant<int, 6>{});
+      dec(std::integral_constant<int, 7>{});
     };
 
     // Gated RMSNorm of chunk ic's output rows O and the store, with the row factors rr
-    // that the norm wave formed from every consumer wave's partial sums.
+    // that the norm wave formed from every consumer wave's partial sums (the variants
+    // whose epilogue runs on the consumers; one tile per wave there).
     auto emit = [&](int ic, const f32x4_t& Oc) __attribute__((always_inline)) {
       const int L = min(C, T - ic * C);
       const float4 r4 = ld<float4>(&sm.rr[ic & 1][4 * lq]);
@@ -931,8 +975,9 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     f32x4_t Oprev = {0.f, 0.f, 0.f, 0.f};
     for (int i = -1; i < nch; ++i) {
       KBuf& K = sm.kb[i & 1];
-      f32x4_t O = {0.f, 0.f, 0.f, 0.f};  // Qa S + P U
-      f32x4_t X = {0.f, 0.f, 0.f, 0.f};  // Ka S
+      f32x4_t O[kCT], X[kCT];  // Qa S + P U, and Ka S, per tile
+#pragma unroll
+      for (int j = 0; j < kCT; ++j) O[j] = X[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
       // ---------------------------------------------------------- interval 1
       if (i >= 0) {
@@ -964,43 +1009,48 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
                        &K.tm[lm][il16(lq + 4 * s1) + 4], tt[0], tt[1]);
         }
         // O = Qa S (rows still to be scaled by the q scale rq) and X = Ka S, with S as
-        // fp16 B operands (per 32 keys: 4 lq + s, then 16 + 4 lq + s)
+        // fp16 B operands (per 32 keys: 4 lq + s, then 16 + 4 lq + s); each Qa and Ka
+        // operand serves every tile
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          f16x8_t sf;
+          const f16x8_t qa = write_out ? ld<f16x8_t>(&K.qa[lm][32 * kb + 8 * lq]) : f16x8_t{};
+          const f16x8_t ka = ld<f16x8_t>(&K.ka[lm][32 * kb + 8 * lq]);
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            sf[s] = static_cast<_Float16>(S[2 * kb][s]);
-            sf[4 + s] = static_cast<_Float16>(S[2 * kb + 1][s]);
+          for (int j = 0; j < kCT; ++j) {
+            f16x8_t sf;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              sf[s] = static_cast<_Float16>(S[j][2 * kb][s]);
+              sf[4 + s] = static_cast<_Float16>(S[j][2 * kb + 1][s]);
+            }
+            if (write_out) O[j] = mma32h(qa, sf, O[j]);
+            X[j] = mma32h(ka, sf, X[j]);
           }
-          if (write_out) O = mma32h(ld<f16x8_t>(&K.qa[lm][32 * kb + 8 * lq]), sf, O);
-          X = mma32h(ld<f16x8_t>(&K.ka[lm][32 * kb + 8 * lq]), sf, X);
         }
       }
       lds_barrier();
 
       // ---------------------------------------------------------- interval 2
       if (i >= 0) {
-        // U = U~ - W S = T (V' - Ka S) for this wave's value tile, V' = |a_k|' V by rows
+        // U = U~ - W S = T (V' - Ka S) for each value tile, V' = |a_k|' V by rows
         const bf16x8_t tq = ld<bf16x8_t>(&K.tm[lm][8 * lq]);
-        f32x4_t U = {0.f, 0.f, 0.f, 0.f};
-        {
-          const float4 k4 = ld<float4>(&K.vk[4 * lq]);
-          const float vk[4] = {k4.x, k4.y, k4.z, k4.w};
+        const float4 k4 = ld<float4>(&K.vk[4 * lq]);
+        const float vk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+        for (int j = 0; j < kCT; ++j) {
+          f32x4_t U = {0.f, 0.f, 0.f, 0.f};
           float y4[4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) y4[s] = fmaf(K.V[4 * lq + s][col], vk[s], -X[s]);
+          for (int s = 0; s < 4; ++s) y4[s] = fmaf(K.V[4 * lq + s][col + 16 * j], vk[s], -X[j][s]);
           bf16x4_t yh, yl;
           split_vec<4>(y4, yh, yl);
           bf16x8_t y_l0, y_hh;
           b_pair(yh, yl, y_l0, y_hh);
           U = mma16p(tq, y_l0, y_hh, U);
-        }
-        {
           float u4[4] = {U[0], U[1], U[2], U[3]};
           bf16x4_t uh, ul;
           split_vec<4>(u4, uh, ul);
-          b_pair(uh, ul, u_l0, u_hh);
+          b_pair(uh, ul, u_l0[j], u_hh[j]);
         }
         // O += P U and the rows' partial sums of squares (not in the Transfer pass).
         // Accumulator hand-off between opcodes: O was last written by the fp16 16x16x32
@@ -1011,16 +1061,20 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         // and pass count, and a barrier and the U product lie between them.  Every other
         // chain in the kernel uses a single opcode.
         if (write_out) {
-          O = mma16p(ld<bf16x8_t>(&K.p[lm][8 * lq]), u_l0, u_hh, O);
+          const bf16x8_t pp = ld<bf16x8_t>(&K.p[lm][8 * lq]);
+#pragma unroll
+          for (int j = 0; j < kCT; ++j) O[j] = mma16p(pp, u_l0[j], u_hh[j], O[j]);
           if constexpr (kProdEpi) {
             // the O rows go to the producers' epilogue, over the elements of V this lane
             // read above (no other lane touches them)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) K.V[4 * lq + s][col] = O[s];
+            for (int j = 0; j < kCT; ++j)
+#pragma unroll
+              for (int s = 0; s < 4; ++s) K.V[4 * lq + s][col + 16 * j] = O[j][s];
           } else {
             float ss[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) ss[s] = row_sum16(O[s] * O[s]);
+            for (int s = 0; s < 4; ++s) ss[s] = row_sum16(O[0][s] * O[0][s]);
             if (lm == 0)
               *reinterpret_cast<float4*>(&sm.ss[cw][4 * lq]) = make_float4(ss[0], ss[1], ss[2], ss[3]);
           }
@@ -1035,7 +1089,7 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
         update_state(K);
       }
       lds_barrier();
-      Oprev = O;
+      Oprev = O[0];
     }
     if (!kProdEpi && nch > 0 && write_out) emit(nch - 1, Oprev);
 
@@ -1047,9 +1101,11 @@ __global__ __launch_bounds__(NT) void prefill_pc_kernel(PrefillArgs a, PcOrder o
     if (dst) {
       float* sp = dst + opaque(4 * lq * kHeadDim + col);
 #pragma unroll
-      for (int it = 0; it < 8; ++it)
+      for (int j = 0; j < kCT; ++j)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) sp[(16 * it + s) * kHeadDim] = S[it][s];
+        for (int it = 0; it < 8; ++it)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) sp[(16 * it + s) * kHeadDim + 16 * j] = S[j][it][s];
     }
   }
 }
@@ -1065,6 +1121,11 @@ static PcKernel pc_kernel_for(const PrefillArgs& a) {
   if (a.L.f_b) return sp ? prefill_pc_kernel<true, true, kXfer> : prefill_pc_kernel<true, false, kXfer>;
   return sp ? prefill_pc_kernel<false, true, kXfer> : prefill_pc_kernel<false, false, kXfer>;
 }
+// Threads per workgroup of the variant pc_kernel_for picks.
+static unsigned pc_threads(const PrefillArgs& a) {
+  const bool sp = a.L.gate_kind == KDA_GATE_SOFTPLUS, fb = a.L.f_b != nullptr;
+  return static_cast<unsigned>(sp || fb ? PcShape<true, true>::kNt : PcShape<false, false>::kNt);
+}
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, const int32_t* order_host, hipStream_t stream) {
   PcOrder ord;
@@ -1074,7 +1135,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, const int32_t* order_host, 
   PrefillArgs w = a;
   w.pass = kPassWhole;
   const dim3 grid(static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.L.H));
-  hipLaunchKernelGGL(pc_kernel_for<false>(a), grid, dim3(NT), 0, stream, w, ord, none);
+  hipLaunchKernelGGL(pc_kernel_for<false>(a), grid, dim3(pc_threads(a)), 0, stream, w, ord, none);
   return hipGetLastError();
 }
 
@@ -1200,7 +1261,7 @@ hipError_t launch_prefill_bf16_split(const PrefillArgs& a, const SplitPlan& plan
   const unsigned H = static_cast<unsigned>(a.L.H);
   PrefillArgs w = a;
   w.pass = kPassTransfer;
-  hipLaunchKernelGGL(pc_kernel_for<true>(a), dim3(2u * plan.nseg * H), dim3(NT), 0, stream, w, none, plan);
+  hipLaunchKernelGGL(pc_kernel_for<true>(a), dim3(2u * plan.nseg * H), dim3(pc_threads(a)), 0, stream, w, none, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(a.num_seqs) * H * (kHeadDim / 16)),
@@ -1208,7 +1269,7 @@ hipError_t launch_prefill_bf16_split(const PrefillArgs& a, const SplitPlan& plan
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   w.pass = kPassFinal;
-  hipLaunchKernelGGL(pc_kernel_for<false>(a), dim3(plan.nseg * H), dim3(NT), 0, stream, w, none, plan);
+  hipLaunchKernelGGL(pc_kernel_for<false>(a), dim3(plan.nseg * H), dim3(pc_threads(a)), 0, stream, w, none, plan);
   return hipGetLastError();
 }
 
