@@ -13,27 +13,31 @@
 // output rows.
 //
 //   * 8 producer waves build everything chunk c+1 needs from its raw rows alone: short
-//     conv + SiLU, gate and Gcum (interval 1); the MFMA-ready operands (bf16 hi/lo, fp16)
-//     and partial sums of squares of the q and k rows (interval 2); the Gram tiles
-//     G = Kp Km^T and P = Qp Km^T, and on a third wave the row norms (interval 3).  Each
-//     wave streams the next-but-one chunk's raw rows of its own slice from HBM straight
-//     into LDS.  In interval 3 the norm wave also turns the consumers' partial sums of
-//     squares of chunk c's output rows into the RMSNorm row factors.
-//   * 8 consumer waves run chunk c's state pass, one 16-column value tile of the fp32
-//     128x128 state each, held in MFMA accumulators for the whole sequence: O = Qa S and
+//     conv + SiLU (two waves per plane of q, k, v, one channel per lane over the 16 rows),
+//     gate and Gcum (two z waves) (interval 1); the MFMA-ready operands (bf16 hi/lo,
+//     fp16) and partial sums of squares of the q and k rows (interval 2); the Gram tiles
+//     G = Kp Km^T and P = Qp Km^T on two waves and the row norms on a third (interval 3).
+//     Each wave reads its own slice of the chunk's raw rows from LDS at the start of
+//     interval 1 and at once refills it with the chunk after, straight from HBM.
+//   * The consumer waves run chunk c's state pass on the fp32 128x128 state, held in MFMA
+//     accumulators for the whole sequence, 16 value columns per tile: O = Qa S and
 //     X = Ka S, beside which two of them form T = (I + A)^-1 Diag(beta') with
 //     A = Diag(beta') G (DPP elimination, once per chunk) (interval 1); then
-//     U = U~ - W S = T (V' - X) (with U~ = T V' and W = T Ka), O += P U and the rows'
-//     partial sums of squares (interval 2); then the gated RMSNorm epilogue of chunk
-//     c-1's rows and S <- Diag(e^Gcum_C) S + Kl^T U (interval 3).
+//     U = U~ - W S = T (V' - X) (with U~ = T V' and W = T Ka) and O += P U (interval 2);
+//     then S <- Diag(e^Gcum_C) S + Kl^T U (interval 3).
+//   * The gated RMSNorm epilogue of chunk c: with the bounded full-rank gate on the four
+//     q and k producer waves in interval 3 (the consumers leave O in the chunk's V buffer;
+//     4 consumer waves of two tiles each, 12 waves per workgroup); with the softplus or
+//     the low-rank gate, whose producers have interval-3 work of their own, on the
+//     consumers one chunk late, from row factors the norm wave forms (8 consumer waves of
+//     one tile each, 16 waves per workgroup).
 //
 // With the low-rank decay gate (kFb below) every producer wave also forms one 16-channel
 // tile of chunk c+2's gate in interval 3.
 //
 // Operands that cross from producers to consumers are double-buffered by chunk parity.
-// Three LDS barriers per chunk.  With 16 waves per workgroup each SIMD holds two producer
-// and two consumer waves, so the VALU-heavy and MFMA-heavy halves hide each other's
-// latencies.
+// Three LDS barriers per chunk.  Each SIMD holds two producer waves and one or two
+// consumer waves, so the VALU-heavy and MFMA-heavy work hide each other's latencies.
 #include <type_traits>
 
 #include "kda_device.h"
