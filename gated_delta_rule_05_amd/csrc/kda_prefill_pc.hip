@@ -70,12 +70,17 @@ constexpr int NT = 64 * (PW + CWN);
 // Ka, T, P, Kl^T) then serves two tiles, which halves those reads, and with 3 waves per
 // SIMD a wave may hold 168 registers, room for the 64 state values.  The other variants
 // keep 8 consumer waves of one tile (16 waves).
-template <bool kSp, bool kFb>
+// The Transfer pass of that variant forms both end states of a segment in one workgroup
+// (kMerged): a second set of 4 consumer waves runs M (identity start, v = 0) beside the
+// first set's B, on the same operands, so each segment's rows are read and its operands
+// built once (16 waves).
+template <bool kSp, bool kFb, bool kXfer = false>
 struct PcShape {
   static constexpr bool kWide = !kSp && !kFb;
-  static constexpr int kCT = kWide ? 2 : 1;        // value tiles per consumer wave
-  static constexpr int kCwn = CWN / kCT;           // consumer waves
-  static constexpr int kNt = 64 * (PW + kCwn);     // threads per workgroup
+  static constexpr int kCT = kWide ? 2 : 1;                // value tiles per consumer wave
+  static constexpr int kCwn = CWN / kCT;                   // consumer waves per state
+  static constexpr bool kMerged = kWide && kXfer;
+  static constexpr int kNt = 64 * (PW + (kMerged ? 2 : 1) * kCwn);  // threads per workgroup
 };
 constexpr int LDP = 132;               // fp32 row stride of [16][128] arrays
 constexpr int OPP = 136;               // bf16 row stride of [16][128] operands
@@ -199,8 +204,8 @@ __device__ __forceinline__ float softplus_gate2(float z, float spb, float ascale
 // kXfer: the Transfer pass of the segment-parallel path, which forms end states only: the
 // q plane and everything built from it (Qa, P, O, the output rows) are left out.
 template <bool kFb, bool kSp, bool kXfer>
-__global__ __launch_bounds__((PcShape<kSp, kFb>::kNt)) void prefill_pc_kernel(PrefillArgs a, PcOrder order, SplitPlan plan) {
-  using Shape = PcShape<kSp, kFb>;
+__global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_kernel(PrefillArgs a, PcOrder order, SplitPlan plan) {
+  using Shape = PcShape<kSp, kFb, kXfer>;
   constexpr int kCT = Shape::kCT;
   __shared__ PcSmem sm;
   // raw rows of q, k, v, z of the next chunk, as [plane][channel half][row][64]: producer
@@ -218,7 +223,7 @@ __global__ __launch_bounds__((PcShape<kSp, kFb>::kNt)) void prefill_pc_kernel(Pr
   // segment kseg of nsegs (see the passes in kda_internal.h).
   const int H = a.L.H;
   int n, h, seg = 0, kseg = 0, nsegs = 1;
-  bool transfer_m = false;  // Transfer pass, M half: identity start, v = 0
+  bool transfer_m = false;  // Transfer pass, M half: identity start, v = 0 (not kMerged)
   int64_t t0;
   int T;
   if (a.pass == kPassWhole) {
@@ -875,7 +880,9 @@ __global__ __launch_bounds__((PcShape<kSp, kFb>::kNt)) void prefill_pc_kernel(Pr
   } else {
     // ============================================================== consumer waves
     // kCT value tiles of 16 columns per wave (tile j: columns col + 16 j), each the fp32
-    // 128 x 16 block of the state as 8 MFMA accumulator tiles
+    // 128 x 16 block of the state as 8 MFMA accumulator tiles.  mstate: this wave forms a
+    // transfer matrix M (the M half of the Transfer pass, or its second wave set)
+    const bool mstate = Shape::kMerged ? cw >= Shape::kCwn : transfer_m;
     f32x4_t S[kCT][8];
     constexpr int64_t kDD = kHeadDim * kHeadDim;
     const int64_t nbase = (static_cast<int64_t>(n) * H + h) * kDD;    // [N][H] planes
@@ -887,7 +894,7 @@ __global__ __launch_bounds__((PcShape<kSp, kFb>::kNt)) void prefill_pc_kernel(Pr
       // segment 0 of a sequence cut into several: the Transfer pass's copy of the start
       // state (the sequence's last segment may write state_out == state_in in this launch)
       src = a.state_in ? a.seg_start + sgbase : nullptr;
-    else if (kseg == 0 && !transfer_m && a.state_in)
+    else if (kseg == 0 && !mstate && a.state_in)
       src = a.state_in + nbase;
     if (src) {
       const float* sp = src + opaque(4 * lq * kHeadDim + col);
@@ -897,7 +904,7 @@ __global__ __launch_bounds__((PcShape<kSp, kFb>::kNt)) void prefill_pc_kernel(Pr
         for (int it = 0; it < 8; ++it)
 #pragma unroll
           for (int s = 0; s < 4; ++s) S[j][it][s] = sp[(16 * it + s) * kHeadDim + 16 * j];
-      if (a.pass == kPassTransfer && !transfer_m) {
+      if (a.pass == kPassTransfer && !mstate) {
         // segment 0 (the Transfer pass skips a sequence's last segment, so the sequence
         // has several): keep the start state where the Final pass reads it, in segment
         // 0's start plane, which the combine never writes
@@ -915,7 +922,7 @@ __global__ __launch_bounds__((PcShape<kSp, kFb>::kNt)) void prefill_pc_kernel(Pr
 #pragma unroll
         for (int it = 0; it < 8; ++it)
 #pragma unroll
-          for (int s = 0; s < 4; ++s) S[j][it][s] = (transfer_m && 16 * it + 4 * lq + s == col + 16 * j) ? 1.f : 0.f;
+          for (int s = 0; s < 4; ++s) S[j][it][s] = (mstate && 16 * it + 4 * lq + s == col + 16 * j) ? 1.f : 0.f;
     }
     lds_barrier();
     if (kFb) lds_barrier();  // the producers' low-rank gate of chunk 0
@@ -1045,7 +1052,8 @@ __global__ __launch_bounds__((PcShape<kSp, kFb>::kNt)) void prefill_pc_kernel(Pr
           f32x4_t U = {0.f, 0.f, 0.f, 0.f};
           float y4[4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) y4[s] = fmaf(K.V[4 * lq + s][col + 16 * j], vk[s], -X[j][s]);
+          for (int s = 0; s < 4; ++s)
+            y4[s] = fmaf(Shape::kMerged && mstate ? 0.f : K.V[4 * lq + s][col + 16 * j], vk[s], -X[j][s]);
           bf16x4_t yh, yl;
           split_vec<4>(y4, yh, yl);
           bf16x8_t y_l0, y_hh;
@@ -1098,10 +1106,12 @@ __global__ __launch_bounds__((PcShape<kSp, kFb>::kNt)) void prefill_pc_kernel(Pr
     if (!kProdEpi && nch > 0 && write_out) emit(nch - 1, Oprev);
 
     float* dst = nullptr;
-    if (a.pass == kPassTransfer)
-      dst = (transfer_m ? a.seg_m : a.seg_b) + sgbase;
-    else if (last_seg && a.state_out)
+    if (a.pass == kPassTransfer) {
+      // (segment 0 needs no M, and its M plane holds the Transfer pass's copy of the ring)
+      if (!(mstate && kseg == 0)) dst = (mstate ? a.seg_m : a.seg_b) + sgbase;
+    } else if (last_seg && a.state_out) {
       dst = a.state_out + nbase;
+    }
     if (dst) {
       float* sp = dst + opaque(4 * lq * kHeadDim + col);
 #pragma unroll
@@ -1126,9 +1136,14 @@ static PcKernel pc_kernel_for(const PrefillArgs& a) {
   return sp ? prefill_pc_kernel<false, true, kXfer> : prefill_pc_kernel<false, false, kXfer>;
 }
 // Threads per workgroup of the variant pc_kernel_for picks.
-static unsigned pc_threads(const PrefillArgs& a) {
+static unsigned pc_threads(const PrefillArgs& a, bool xfer) {
   const bool sp = a.L.gate_kind == KDA_GATE_SOFTPLUS, fb = a.L.f_b != nullptr;
-  return static_cast<unsigned>(sp || fb ? PcShape<true, true>::kNt : PcShape<false, false>::kNt);
+  if (sp || fb) return static_cast<unsigned>(PcShape<true, true>::kNt);
+  return static_cast<unsigned>(xfer ? PcShape<false, false, true>::kNt : PcShape<false, false>::kNt);
+}
+// Whether the Transfer pass forms B and M in one workgroup (kMerged) for this layer.
+static bool pc_merged(const PrefillArgs& a) {
+  return a.L.gate_kind != KDA_GATE_SOFTPLUS && a.L.f_b == nullptr;
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, const int32_t* order_host, hipStream_t stream) {
@@ -1139,7 +1154,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, const int32_t* order_host, 
   PrefillArgs w = a;
   w.pass = kPassWhole;
   const dim3 grid(static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.L.H));
-  hipLaunchKernelGGL(pc_kernel_for<false>(a), grid, dim3(pc_threads(a)), 0, stream, w, ord, none);
+  hipLaunchKernelGGL(pc_kernel_for<false>(a), grid, dim3(pc_threads(a, false)), 0, stream, w, ord, none);
   return hipGetLastError();
 }
 
@@ -1265,7 +1280,9 @@ hipError_t launch_prefill_bf16_split(const PrefillArgs& a, const SplitPlan& plan
   const unsigned H = static_cast<unsigned>(a.L.H);
   PrefillArgs w = a;
   w.pass = kPassTransfer;
-  hipLaunchKernelGGL(pc_kernel_for<true>(a), dim3(2u * plan.nseg * H), dim3(pc_threads(a)), 0, stream, w, none, plan);
+  const unsigned halves = pc_merged(a) ? 1u : 2u;  // B and M in one workgroup, or in two
+  hipLaunchKernelGGL(pc_kernel_for<true>(a), dim3(halves * plan.nseg * H), dim3(pc_threads(a, true)), 0, stream, w,
+                     none, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(a.num_seqs) * H * (kHeadDim / 16)),
@@ -1273,7 +1290,8 @@ hipError_t launch_prefill_bf16_split(const PrefillArgs& a, const SplitPlan& plan
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   w.pass = kPassFinal;
-  hipLaunchKernelGGL(pc_kernel_for<false>(a), dim3(plan.nseg * H), dim3(pc_threads(a)), 0, stream, w, none, plan);
+  hipLaunchKernelGGL(pc_kernel_for<false>(a), dim3(plan.nseg * H), dim3(pc_threads(a, false)), 0, stream, w, none,
+                     plan);
   return hipGetLastError();
 }
 
