@@ -92,6 +92,28 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_wave_base)
                : "v"(gsrc), "s"(lds)
                : "memory", "m0");
 }
+// The same through a buffer resource (base and size in SGPRs, a 32-bit lane offset and a
+// scalar offset): the per-lane address costs no 64-bit arithmetic, and lanes past the
+// resource's size read zeros instead of touching memory.  The resource is built from
+// wave-uniform values taken through readfirstlane (uniform_rsrc), so that it is in SGPRs
+// whatever the compiler's divergence analysis concludes about where they came from.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+  const uint64_t b = reinterpret_cast<uintptr_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+  const void* u = reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return buffer_rsrc(u, __builtin_amdgcn_readfirstlane(bytes));
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff, uint32_t lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_wave_base);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds), "s"(soff)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Waits for this wave's outstanding LDS operations (e.g. reads of a buffer it refills next).
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }

@@ -327,7 +327,10 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
     // raw_lds[urole][hf][8 k].  No other wave touches the slice, so the wave orders its
     // reads and refills by itself.  The output-gate plane goes to the consumers'
     // double-buffered copy: four waves, piece s = 64 wave + lane is row s / 16, bytes
-    // 16 (s % 16).  Rows past the end of a sequence re-read its last row.
+    // 16 (s % 16).  Both go through a buffer resource that starts at the chunk's first row
+    // and spans its rows within the sequence: the lane offsets stay the same from chunk to
+    // chunk (only the resource's SGPRs move), and rows past the end of a sequence read
+    // zeros, which no arithmetic of a ragged chunk uses.
     const char* const pq = static_cast<const char*>(a.q);
     const char* const pk = static_cast<const char*>(a.k);
     const char* const pv = static_cast<const char*>(a.v);
@@ -335,28 +338,31 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
     const char* const pgt = static_cast<const char*>(a.gate);
     const bf16_t* const x_b = static_cast<const bf16_t*>(a.beta);
     const int row_bytes = static_cast<int>(Hd) * 2;
-    const int64_t head_bytes = static_cast<int64_t>(h) * kHeadDim * 2;
-    const char* const plane_base = (urole == 0 ? pq : urole == 1 ? pk : urole == 2 ? pv : pz) +
-                                   head_bytes + (kHeadDim / 2) * 2 * hf + 16 * (lane & 7);
+    const int head_bytes = h * kHeadDim * 2;
+    const char* const plane = urole == 0 ? pq : urole == 1 ? pk : urole == 2 ? pv : pz;
     uint16_t braw = 0;  // raw beta of row t (threads t < C), one chunk ahead
+    // this wave's slice of raw_lds (wave-uniform)
+    const uint32_t raw_slice = lds_addr(&raw_lds[0][0][0][0]) + (2 * urole + hf) * (C * kHeadDim);
     auto prefetch = [&](int c0n) __attribute__((always_inline)) {
       const int Ln = min(C, T - c0n);
       if (kFb && urole == 3) return;  // the z plane is z_low, fetched by prefetch_zlow
-      if (t < C) braw = x_b[(t0 + c0n + min(t, Ln - 1)) * H + h].bits;
+      if (t < C) {
+        const __amdgpu_buffer_rsrc_t rb = uniform_rsrc(x_b + (t0 + c0n) * H, Ln * H * 2);
+        braw = __builtin_amdgcn_raw_buffer_load_b16(rb, (t * H + h) * 2, 0, 0);
+      }
       if (urole == 0 && !write_out) return;  // the Transfer pass has no use for q
-      const char* base = plane_base + (t0 + c0n) * Hd * 2;
-      const int slice = opaque(2 * urole + hf);  // recomputed here, not kept live across the loop
+      const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(plane + (t0 + c0n) * row_bytes, Ln * row_bytes);
+      const int vo = opaque((lane >> 3) * row_bytes + head_bytes + (kHeadDim / 2) * 2 * hf + 16 * (lane & 7));
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
-        lds_dma16(base + min(8 * k + (lane >> 3), Ln - 1) * row_bytes, &raw_lds[slice >> 1][slice & 1][8 * k][0]);
+      for (int k = 0; k < 2; ++k) lds_dma16_buf(rs, vo, 8 * k * row_bytes, raw_slice + 8 * k * kHeadDim);
     };
     auto prefetch_gate = [&](int c0n, int buf) __attribute__((always_inline)) {
       if (uwave < 4) {
         const int Ln = min(C, T - c0n);
         const int sg = 64 * uwave + lane;
-        const char* base = pgt + (t0 + c0n) * Hd * 2 + head_bytes;
-        lds_dma16(base + min(sg >> 4, Ln - 1) * row_bytes + 16 * (sg & 15),
-                  &graw_lds[buf][0][0] + 8 * 64 * uwave);
+        const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(pgt + (t0 + c0n) * row_bytes, Ln * row_bytes);
+        lds_dma16_buf(rs, (sg >> 4) * row_bytes + head_bytes + 16 * (sg & 15), 0,
+                      lds_addr(&graw_lds[buf][0][0]) + 2 * 8 * 64 * uwave);
       }
     };
 
