@@ -506,7 +506,7 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
     // output row is rq O (rq the q row factor), and rq O / sqrt(mean (rq O)^2 + eps) = O rr
     // with rr = rq / sqrt(rq^2 mean O^2 + eps), the sum of squares taken over the 16 lanes
     // of a DPP row.  Then times the norm weight and sigmoid(gate), rounded to bf16 and
-    // stored as one 16-byte piece per lane.
+    // stored as one 16-byte piece per lane through a buffer resource over the chunk's rows.
     auto epilogue = [&](int ic) __attribute__((always_inline)) {
       const KBuf& K = sm.kb[ic & 1];
       const int r = 4 * uwave + (lane >> 4), c8 = 8 * (lane & 15);
@@ -530,10 +530,11 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
         const float y1 = nw8[2 * j + 1] * o[2 * j + 1] * rr * fsigmoid(ga1);
         packed[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){y0, y1}, bf16x2_t));
       }
-      if (r < min(C, T - ic * C)) {
-        char* po = static_cast<char*>(a.out) + ((t0 + ic * C + r) * Hd + static_cast<int64_t>(h) * kHeadDim + c8) * 2;
-        *reinterpret_cast<uint4*>(po) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      }
+      // rows past the end of the sequence fall outside the resource and are not written
+      const __amdgpu_buffer_rsrc_t ro =
+          uniform_rsrc(static_cast<char*>(a.out) + (t0 + ic * C) * row_bytes, min(C, T - ic * C) * row_bytes);
+      const u32x4_raw pk4 = {packed[0], packed[1], packed[2], packed[3]};
+      __builtin_amdgcn_raw_buffer_store_b128(pk4, ro, r * row_bytes + head_bytes + 2 * c8, 0, 0);
     };
 
     if (T > 0) {
