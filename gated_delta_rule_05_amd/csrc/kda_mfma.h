@@ -74,29 +74,20 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane
-// l's bytes land at lds_wave_base + 16 l, so one wave fills 1 KiB.  lds_wave_base must be
-// wave-uniform (it goes to M0).  Completion is counted by vmcnt, not lgkmcnt: the issuing
+// 16 bytes per lane from global memory straight into LDS (buffer_load_dwordx4 ... lds):
+// lane l's bytes land at lds_wave_base + 16 l, so one wave fills 1 KiB.  lds_wave_base is
+// an LDS byte address, wave-uniform (it goes to M0).  The source is a buffer resource
+// (base and size in SGPRs) with a 32-bit lane offset and a scalar offset, so the per-lane
+// address costs no 64-bit arithmetic, and lanes past the resource's size read zeros
+// instead of touching memory.  Completion is counted by vmcnt, not lgkmcnt: the issuing
 // wave waits with wait_vm() before the barrier that publishes the data.  The instruction
 // is issued from inline assembly so that the compiler does not track it: it would
 // otherwise wait for the transfer before LDS accesses it cannot prove disjoint from the
 // target, which stalls on HBM latency.  The vmcnt waits the compiler does compute for its
 // own loads stay correct (vector memory operations complete in issue order, so extra
-// ones in flight only make those waits longer).
-// The LDS address is the low half of the pointer's flat address (the LDS aperture puts
-// the offset there), taken without an address-space cast and its null test.
-__device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_wave_base)));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gsrc), "s"(lds)
-               : "memory", "m0");
-}
-// The same through a buffer resource (base and size in SGPRs, a 32-bit lane offset and a
-// scalar offset): the per-lane address costs no 64-bit arithmetic, and lanes past the
-// resource's size read zeros instead of touching memory.  The resource is built from
-// wave-uniform values taken through readfirstlane (uniform_rsrc), so that it is in SGPRs
-// whatever the compiler's divergence analysis concludes about where they came from.
+// ones in flight only make those waits longer).  The resource must be in SGPRs: build it
+// with uniform_rsrc, which takes its wave-uniform inputs through readfirstlane whatever
+// the compiler's divergence analysis concludes about where they came from.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
   const uint64_t b = reinterpret_cast<uintptr_t>(base);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
@@ -104,10 +95,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
   const void* u = reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
   return buffer_rsrc(u, __builtin_amdgcn_readfirstlane(bytes));
 }
+// The LDS byte address of a __shared__ object: the low half of its flat address (the LDS
+// aperture puts the offset there), taken without an address-space cast and its null test.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
-__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff, uint32_t lds_wave_base) {
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff, uint32_t lds_wave_base) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_wave_base);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
                :

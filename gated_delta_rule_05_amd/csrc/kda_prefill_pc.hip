@@ -354,14 +354,14 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
       const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(plane + (t0 + c0n) * row_bytes, Ln * row_bytes);
       const int vo = opaque((lane >> 3) * row_bytes + head_bytes + (kHeadDim / 2) * 2 * hf + 16 * (lane & 7));
 #pragma unroll
-      for (int k = 0; k < 2; ++k) lds_dma16_buf(rs, vo, 8 * k * row_bytes, raw_slice + 8 * k * kHeadDim);
+      for (int k = 0; k < 2; ++k) lds_dma16(rs, vo, 8 * k * row_bytes, raw_slice + 8 * k * kHeadDim);
     };
     auto prefetch_gate = [&](int c0n, int buf) __attribute__((always_inline)) {
       if (uwave < 4) {
         const int Ln = min(C, T - c0n);
         const int sg = 64 * uwave + lane;
         const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(pgt + (t0 + c0n) * row_bytes, Ln * row_bytes);
-        lds_dma16_buf(rs, (sg >> 4) * row_bytes + head_bytes + 16 * (sg & 15), 0,
+        lds_dma16(rs, (sg >> 4) * row_bytes + head_bytes + 16 * (sg & 15), 0,
                       lds_addr(&graw_lds[buf][0][0]) + 2 * 8 * 64 * uwave);
       }
     };
@@ -372,13 +372,14 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
     // across the loop)
     auto prefetch_zlow = [&](int c0n) __attribute__((always_inline)) {
       const int Ln = min(C, T - c0n);
-      const char* zb = pz + (t0 + c0n) * (kHeadDim * 2);
+      // rows past the end of the sequence read zeros (their gate is masked)
+      const __amdgpu_buffer_rsrc_t rz = uniform_rsrc(pz + (t0 + c0n) * (kHeadDim * 2), Ln * (kHeadDim * 2));
       const int ln = opaque(lane);
       const int buf = (c0n / C) & 1;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int row = 8 * hf + 4 * j + (ln >> 4);
-        lds_dma16(zb + min(row, Ln - 1) * (kHeadDim * 2) + 16 * ((ln & 15) ^ row), &zlow_lds[buf][8 * hf + 4 * j][0]);
+        lds_dma16(rz, row * (kHeadDim * 2) + 16 * ((ln & 15) ^ row), 0, lds_addr(&zlow_lds[buf][8 * hf + 4 * j][0]));
       }
     };
 
