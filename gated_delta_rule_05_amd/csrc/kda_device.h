@@ -54,7 +54,9 @@ __device__ __forceinline__ void store_io<bf16_t>(bf16_t* p, int64_t i, float x) 
 // Raw buffer access (CDNA buffer instructions): a resource of `bytes` bytes at `base` in
 // four SGPRs, one 32-bit VGPR offset per lane and a scalar offset per access, so a
 // thread's 16 rows of state cost one address register instead of 16 64-bit pointers.
-// Accesses past `bytes` read 0 and are dropped on write.
+// Accesses past `bytes` read 0 and are dropped on write; the check covers the lane (VGPR)
+// offset, not the scalar one, so code that relies on it keeps the checked part in the
+// lane offset.
 typedef float f32x4_raw __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_raw __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {

@@ -79,7 +79,9 @@ __device__ __forceinline__ void lds_barrier() {
 // an LDS byte address, wave-uniform (it goes to M0).  The source is a buffer resource
 // (base and size in SGPRs) with a 32-bit lane offset and a scalar offset, so the per-lane
 // address costs no 64-bit arithmetic, and lanes past the resource's size read zeros
-// instead of touching memory.  Completion is counted by vmcnt, not lgkmcnt: the issuing
+// instead of touching memory.  The range check covers the lane offset only, not the
+// scalar one: an offset that must stay within the resource belongs in voff.  Completion
+// is counted by vmcnt, not lgkmcnt: the issuing
 // wave waits with wait_vm() before the barrier that publishes the data.  The instruction
 // is issued from inline assembly so that the compiler does not track it: it would
 // otherwise wait for the transfer before LDS accesses it cannot prove disjoint from the

@@ -354,7 +354,7 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
       const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(plane + (t0 + c0n) * row_bytes, Ln * row_bytes);
       const int vo = opaque((lane >> 3) * row_bytes + head_bytes + (kHeadDim / 2) * 2 * hf + 16 * (lane & 7));
 #pragma unroll
-      for (int k = 0; k < 2; ++k) lds_dma16(rs, vo, 8 * k * row_bytes, raw_slice + 8 * k * kHeadDim);
+      for (int k = 0; k < 2; ++k) lds_dma16(rs, vo + 8 * k * row_bytes, 0, raw_slice + 8 * k * kHeadDim);
     };
     auto prefetch_gate = [&](int c0n, int buf) __attribute__((always_inline)) {
       if (uwave < 4) {
