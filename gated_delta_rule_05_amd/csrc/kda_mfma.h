@@ -78,8 +78,8 @@ __device__ __forceinline__ void lds_barrier() {
 // lane l's bytes land at lds_wave_base + 16 l, so one wave fills 1 KiB.  lds_wave_base is
 // an LDS byte address, wave-uniform (it goes to M0).  The source is a buffer resource
 // (base and size in SGPRs) with a 32-bit lane offset and a scalar offset, so the per-lane
-// address costs no 64-bit arithmetic, and lanes past the resource's size read zeros
-// instead of touching memory.  The range check covers the lane offset only, not the
+// address costs no 64-bit arithmetic, and lanes past the resource's size touch no memory
+// (what their LDS bytes then hold is not to be used).  The range check covers the lane offset only, not the
 // scalar one: an offset that must stay within the resource belongs in voff.  Completion
 // is counted by vmcnt, not lgkmcnt: the issuing
 // wave waits with wait_vm() before the barrier that publishes the data.  The instruction

@@ -329,8 +329,8 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
     // double-buffered copy: four waves, piece s = 64 wave + lane is row s / 16, bytes
     // 16 (s % 16).  Both go through a buffer resource that starts at the chunk's first row
     // and spans its rows within the sequence: the lane offsets stay the same from chunk to
-    // chunk (only the resource's SGPRs move), and rows past the end of a sequence read
-    // zeros, which no arithmetic of a ragged chunk uses.
+    // chunk (only the resource's SGPRs move), and rows past the end of a sequence are not
+    // fetched; no arithmetic of a ragged chunk uses their slots.
     const char* const pq = static_cast<const char*>(a.q);
     const char* const pk = static_cast<const char*>(a.k);
     const char* const pv = static_cast<const char*>(a.v);
@@ -372,7 +372,7 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
     // across the loop)
     auto prefetch_zlow = [&](int c0n) __attribute__((always_inline)) {
       const int Ln = min(C, T - c0n);
-      // rows past the end of the sequence read zeros (their gate is masked)
+      // rows past the end of the sequence are not fetched (their gate is masked)
       const __amdgpu_buffer_rsrc_t rz = uniform_rsrc(pz + (t0 + c0n) * (kHeadDim * 2), Ln * (kHeadDim * 2));
       const int ln = opaque(lane);
       const int buf = (c0n / C) & 1;
