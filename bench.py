@@ -618,8 +618,8 @@ def main():
         summarize_prefill_pmc(args.summarize_prefill_pmc)
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the KDA core shards by head or sequence with no exchange; see the design notes)",
+        print(f"bench.py: the KDA core runs on one GPU here; --gpus {args.gpus} is not supported "
+              "(it shards by head or by sequence with no exchange between GPUs)",
               file=sys.stderr)
         return 2
 

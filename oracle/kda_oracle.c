@@ -20,7 +20,7 @@
  * fusion or reordering beyond what the definitions state.  io inputs arrive either as
  * fp32 or as bf16 bit patterns (uint16); both convert to double exactly.
  *
- * Readings taken where the pages are silent (each is listed in the design notes):
+ * Readings taken where the pages are silent:
  *   - conv taps: cross-correlation with left zero padding of kernel-1, tap index
  *     kernel-1 multiplies the current token (PyTorch Conv1d semantics, [p1]);
  *   - the conv history ("ring") holds the kernel-1 most recent raw inputs, oldest first;
