@@ -19,6 +19,12 @@ SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_pc.h
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-munsafe-fp-atomics"]
+# Per-source additions.  The chunked prefill is scheduled with no weight on occupancy in
+# the scheduler's occupancy/latency metric: its occupancy is fixed by the workgroup shape
+# (one workgroup per CU), and the latency-first schedule measured about 1.5% faster on
+# 2 x 8192 tokens x 96 heads (the max-ilp, memory-clause and iterative-ilp strategies were
+# slower).
+EXTRA = {"kda_prefill_pc.hip": ["-mllvm", "-amdgpu-schedule-metric-bias=0"]}
 
 
 def hipcc() -> str:
@@ -33,7 +39,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(build_dir, exist_ok=True)
     for src in SOURCES:
         obj = os.path.join(build_dir, src.rsplit(".", 1)[0] + ".o")
-        cmd = [hipcc()] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc()] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".hip"):
             cmd[1:1] = ["-x", "hip"]
         if verbose:
