@@ -262,7 +262,14 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
   const int64_t Hd = static_cast<int64_t>(H) * kHeadDim;
   const int nch = (T + C - 1) / C;
 
-  const int t = threadIdx.x;
+  // With the softplus gate alone, the v and z producer waves (logical waves 4..7) are
+  // dispatched first, so that they are the oldest waves in each SIMD's issue arbitration
+  // (measured 3% faster there; the other variants gain nothing or lose); t and wave below
+  // are the logical numbering.  The swap moves waves by 4, so every wave keeps its SIMD.
+  constexpr bool kVzFirst = kSp && !kFb;
+  const int pwave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int t = kVzFirst ? ((pwave < 4 ? pwave + 4 : pwave < 8 ? pwave - 4 : pwave) << 6) | (threadIdx.x & 63)
+                         : static_cast<int>(threadIdx.x);
   const int wave = t >> 6;
   const int lane = t & 63;
   const int lm = lane & 15;
