@@ -224,25 +224,38 @@ __device__ __forceinline__ void store4_f16(_Float16* dst, const float* x) {
   *reinterpret_cast<f16x4_t*>(dst) = h;
 }
 // One elimination step per row j of the 16x16 unit-lower system: every lane of a 16-lane
-// row takes row j's values from lane j of its own row (DPP broadcast).
+// row takes row j's values from lane j of its own row (DPP broadcast).  The row's
+// coefficients come negated (nrow = -A[row]), so that a step is one multiply-add with the
+// broadcast as its DPP source (v_fmac_f32_dpp) instead of a DPP move and a negated fma.
 template <int J>
-__device__ __forceinline__ void eliminate(float* tt, const float* arow) {
+__device__ __forceinline__ void eliminate(float* tt, const float* nrow) {
   if constexpr (J < C - 1) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) tt[s] -= arow[J] * row_bcast<J>(tt[s]);
-    eliminate<J + 1>(tt, arow);
+    for (int s = 0; s < 4; ++s) tt[s] = fmaf(row_bcast<J>(tt[s]), nrow[J], tt[s]);
+    eliminate<J + 1>(tt, nrow);
   }
 }
 
 // The same for two of the four strided slots (SA, SB) only: columns never mix in the
 // elimination, so two waves can share it, one taking slots {0, 3} and the other {1, 2}
 // (18 updates each).
+//
+// A step is one v_fmac_f32_dpp, t += bcast_J(t) * nrow[J], issued from inline assembly
+// (the compiler keeps a separate DPP move in front of the multiply-add, which doubles the
+// dependency chain).  The s_nop in front of it provides the two wait states a DPP read
+// needs after the VALU write of its source.
+template <int J>
+__device__ __forceinline__ void elim_step(float& t, float nr) {
+  asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf"
+               : "+v"(t)
+               : "v"(nr), "i"(J));
+}
 template <int J, int SA, int SB>
-__device__ __forceinline__ void eliminate_strided2(float* tt, const float* arow) {
+__device__ __forceinline__ void eliminate_strided2(float* tt, const float* nrow) {
   if constexpr (J < C - 1) {
-    if constexpr (SA <= J / 4) tt[0] -= arow[J] * row_bcast<J>(tt[0]);
-    if constexpr (SB <= J / 4) tt[1] -= arow[J] * row_bcast<J>(tt[1]);
-    eliminate_strided2<J + 1, SA, SB>(tt, arow);
+    if constexpr (SA <= J / 4) elim_step<J>(tt[0], nrow[J]);
+    if constexpr (SB <= J / 4) elim_step<J>(tt[1], nrow[J]);
+    eliminate_strided2<J + 1, SA, SB>(tt, nrow);
   }
 }
 

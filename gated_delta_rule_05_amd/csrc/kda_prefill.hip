@@ -356,10 +356,10 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(PrefillArgs a, SeqOrd
 #pragma unroll
       for (int j = 0; j < C; j += 4) {
         const float4 v4 = *reinterpret_cast<const float4*>(&sm.A[lm][j]);
-        arow[j] = v4.x;
-        arow[j + 1] = v4.y;
-        arow[j + 2] = v4.z;
-        arow[j + 3] = v4.w;
+        arow[j] = -v4.x;  // negated: the elimination takes -A[row]
+        arow[j + 1] = -v4.y;
+        arow[j + 2] = -v4.z;
+        arow[j + 3] = -v4.w;
       }
       const float bl = sm.beta[lm];
 #pragma unroll

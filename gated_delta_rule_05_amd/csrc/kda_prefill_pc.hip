@@ -1012,16 +1012,16 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
           // broadcasts inside each 16-lane row); A[r][j] = 0 for j >= r, so the update
           // is unconditional.  Lane (lm, lq) holds T[lm][lq + 4 s]; wave kElimCwA takes
           // slots s = 0, 3 and wave kElimCwB slots 1, 2.
-          // A = Diag(beta') G, row lm
+          // -A = -Diag(beta') G, row lm (the elimination takes the row negated)
           float arow[C], tt[2];
-          const float bl = K.beta[lm];
+          const float bl = K.beta[lm], nbl = -bl;
 #pragma unroll
           for (int j = 0; j < C; j += 4) {
             const float4 v4 = *reinterpret_cast<const float4*>(&sm.A[lm][j]);
-            arow[j] = bl * v4.x;
-            arow[j + 1] = bl * v4.y;
-            arow[j + 2] = bl * v4.z;
-            arow[j + 3] = bl * v4.w;
+            arow[j] = nbl * v4.x;
+            arow[j + 1] = nbl * v4.y;
+            arow[j + 2] = nbl * v4.z;
+            arow[j + 3] = nbl * v4.w;
           }
           const bool wa = cw == kElimCwA;
           const int s0 = wa ? 0 : 1, s1 = wa ? 3 : 2;
