@@ -567,6 +567,14 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
       lds_barrier();
     }
 
+    // With two value tiles per consumer wave (the 12-wave layout, which has registers to
+    // spare), the raw rows are read straight into the high halves of registers whose low
+    // halves stay zero from one chunk to the next (ds_read_u16_d16_hi): each value is then
+    // already the fp32 of its bf16, and the 16 shifts per chunk and wave are saved.
+    uint32_t xw[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) xw[r] = 0u;
+
     // iteration i: producers build chunk i + 1
     for (int i = -1; i < nch; ++i) {
       const bool has_next = i + 1 < nch;
@@ -581,9 +589,21 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
         // that the rows' exp/rcp chains interleave.
         uint16_t xr[C];
         if (!(kFb && urole == 3) && !(urole == 0 && !write_out)) {
+          if constexpr (Shape::kWide) {
+            const uint32_t ra = lds_addr(&raw_lds[urole][hf][0][lane]);
 #pragma unroll
-          for (int r = 0; r < C; ++r) xr[r] = raw_lds[urole][hf][r][lane];
+            for (int r = 0; r < C; ++r)
+              asm volatile("ds_read_u16_d16_hi %0, %1 offset:%2" : "+v"(xw[r]) : "v"(ra), "i"(r * kHeadDim) : "memory");
+            lds_wait();  // the compiler does not track these reads
+          } else {
+#pragma unroll
+            for (int r = 0; r < C; ++r) xr[r] = raw_lds[urole][hf][r][lane];
+          }
         }
+        // raw value of row r as fp32
+        auto raw = [&](int r) __attribute__((always_inline)) {
+          return Shape::kWide ? __uint_as_float(xw[r]) : bf16_to_f32(xr[r]);
+        };
         if (t < C) KN.beta[t] = (t < Ln) ? fsigmoid(bf16_to_f32(braw)) : 0.f;
         // this wave's raw slice is read: refill it with chunk i + 2 at once (the reads are
         // complete before the transfer is issued), so that the transfer's issue overlaps
@@ -612,7 +632,7 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
             xs[1] = hist[1];
             xs[2] = hist[2];
 #pragma unroll
-            for (int r = 0; r < C; ++r) xs[r + 3] = bf16_to_f32(xr[r]);
+            for (int r = 0; r < C; ++r) xs[r + 3] = raw(r);
 #pragma unroll
             for (int r = 0; r < C; ++r) ys[r] = w[3] * xs[r + 3] + w[0] * xs[r] + w[1] * xs[r + 1] + w[2] * xs[r + 2];
             hist[0] = xs[C];
@@ -627,7 +647,7 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
           } else {
 #pragma unroll
             for (int r = 0; r < C; ++r) {
-              const float x = bf16_to_f32(xr[r]);
+              const float x = raw(r);
               const float ys = w[3] * x + w[0] * hist[0] + w[1] * hist[1] + w[2] * hist[2];
               const bool live = r < Ln;
               if (live) {
@@ -644,16 +664,15 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
           KN.eg15[cc] = sm.eg15n[cc];
         } else {
           // the per-token log2 decay of either gate
-          auto gate2 = [&](uint16_t xz) __attribute__((always_inline)) {
-            return kSp ? softplus_gate2(bf16_to_f32(xz), spb, ascale)
-                       : lb2 * frcp(1.0f + fexp2(fmaf(bf16_to_f32(xz), ga, gb)));
+          auto gate2 = [&](float xz) __attribute__((always_inline)) {
+            return kSp ? softplus_gate2(xz, spb, ascale) : lb2 * frcp(1.0f + fexp2(fmaf(xz, ga, gb)));
           };
           float G = 0.f, G7 = 0.f;
           if (full) {
             // every row's decay first (independent chains), then the running sum
             float gv[C];
 #pragma unroll
-            for (int r = 0; r < C; ++r) gv[r] = gate2(xr[r]);
+            for (int r = 0; r < C; ++r) gv[r] = gate2(raw(r));
 #pragma unroll
             for (int r = 0; r < C; ++r) {
               G += gv[r];
@@ -664,7 +683,7 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
 #pragma unroll
             for (int r = 0; r < C; ++r) {
               const bool live = r < Ln;
-              G += live ? gate2(xr[r]) : 0.f;
+              G += live ? gate2(raw(r)) : 0.f;
               sm.gam[r][ch] = G;
               if (r == C / 2 - 1) G7 = G;
             }
