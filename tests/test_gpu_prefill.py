@@ -72,6 +72,19 @@ def test_varlen_ragged_with_state_and_ring(io):
     _check(prob, _prefill(prob), _all_units(prob), f"varlen_{io}")
 
 
+@pytest.mark.parametrize("softplus,low_rank", [(False, False), (True, False), (False, True), (True, True)])
+def test_chunk_boundary_lengths(softplus, low_rank):
+    """Sequence lengths on either side of one, two and three 16-token chunks, and just past
+    the conv window: the pipelined kernel's first and last iterations (prefetch two chunks
+    ahead, ragged last chunk with 1..15 live rows, the ring taken from the last chunk or
+    from the history before it), with carried state and ring."""
+    lens = [3, 4, 15, 16, 17, 18, 31, 32, 33, 47, 48, 49]
+    prob = synthetic.make_prefill(lens, H=2, io="bf16", seed=211, device=DEV, init_state=True,
+                                  init_ring=True, softplus_gate=softplus, low_rank_gate=low_rank)
+    label = ("softplus" if softplus else "bounded") + ("_low_rank" if low_rank else "")
+    _check(prob, _prefill(prob), _all_units(prob), f"chunk_boundaries_{label}")
+
+
 def test_in_place_state_and_ring():
     """state_out may equal state_in and ring_out may equal ring_in."""
     prob = synthetic.make_prefill([40, 19], H=2, io="bf16", seed=202, device=DEV,
