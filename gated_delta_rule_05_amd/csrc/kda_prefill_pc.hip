@@ -1046,6 +1046,9 @@ __global__ __launch_bounds__((PcShape<kSp, kFb, kXfer>::kNt)) void prefill_pc_ke
           const int s0 = wa ? 0 : 1, s1 = wa ? 3 : 2;
           tt[0] = (lq + 4 * s0 == lm) ? bl : 0.f;
           tt[1] = (lq + 4 * s1 == lm) ? bl : 0.f;
+          // five wait states ahead of the first DPP step, whatever the compiler placed
+          // before it (a VALU write of EXEC needs five; a VGPR write two)
+          asm volatile("s_nop 4" ::: "memory");
           if (wa)
             eliminate_strided2<0, 0, 3>(tt, arow);
           else
