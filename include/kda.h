@@ -186,8 +186,9 @@ kda_status kda_prefill_noalloc(const kda_layer* layer, kda_dtype io, int32_t num
  * (memra_engine::kda's prefill arrangement, memra_kda_scan_s128, which serves prefill and
  * decode alike).  An A/B comparator for the chunked path (which measures faster on this
  * hardware even for 64-token prompts), and the path kda_prefill takes for fp32 io with the
- * softplus or the low-rank gate.  Each sequence's outputs, final state and ring are bit-identical to running its
- * tokens through kda_decode_step one at a time.  Any lower_bound <= 0 is accepted (there
+ * softplus or the low-rank gate.  Each sequence's outputs, final state and ring are
+ * bit-identical to running its tokens through kda_decode_step one at a time.  Any
+ * lower_bound <= 0 is accepted (there
  * is no tile bound).  state_in / ring_in may be NULL (zeros), state_out / ring_out NULL
  * (not written); state_out may equal state_in and ring_out ring_in.
  */
