@@ -23,8 +23,9 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
 # the scheduler's occupancy/latency metric: its occupancy is fixed by the workgroup shape
 # (one workgroup per CU), and the latency-first schedule measured about 1.5% faster on
 # 2 x 8192 tokens x 96 heads (the max-ilp, memory-clause and iterative-ilp strategies were
-# slower).
-EXTRA = {"kda_prefill_pc.hip": ["-mllvm", "-amdgpu-schedule-metric-bias=0"]}
+# slower).  Without memory-operation clustering the scheduler spreads the LDS accesses
+# among the arithmetic: a further 0.7% on every prefill workload in a same-box A/B.
+EXTRA = {"kda_prefill_pc.hip": ["-mllvm", "-amdgpu-schedule-metric-bias=0", "-mllvm", "-misched-cluster=false"]}
 
 
 def hipcc() -> str:
