@@ -44,10 +44,12 @@ def _chain(layer, dec, t, state, ring, ntok=None):
     return outs, st, rg
 
 
+@pytest.mark.parametrize("t", [4, 6])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_multi_is_bit_identical_to_chained_steps(io):
+def test_multi_is_bit_identical_to_chained_steps(io, t):
+    """Ping-pong and in place, at the speculative verify's 4 tokens and at 6."""
     kda = _kda()
-    B, H, t = 5, 3, 6
+    B, H = 5, 3
     dec = synthetic.make_decode(B=B, H=H, io=io, steps=t, seed=301, device=DEV)
     layer = kda.Layer(**dec["layer"])
     ref_out, ref_st, ref_rg = _chain(layer, dec, t, dec["state"], dec["ring"])
@@ -68,15 +70,15 @@ def test_multi_is_bit_identical_to_chained_steps(io):
     assert torch.equal(out2, ref_out) and torch.equal(st_in, ref_st) and torch.equal(rg_in, ref_rg)
 
 
-def test_multi_against_oracle_with_ragged_counts():
+@pytest.mark.parametrize("t,counts", [(7, [7, 0, 1, 4, 3, 7]), (4, [4, 0, 1, 2, 3, 4])])
+def test_multi_against_oracle_with_ragged_counts(t, counts):
     """bf16, per-sequence token counts 0..t: outputs of the run rows and final states match
     the oracle over each sequence's own prefix; rows past the count are not written; a
     sequence with 0 rows passes its state and ring through."""
     kda = _kda()
-    B, H, t = 6, 2, 7
+    B, H = 6, 2
     dec = synthetic.make_decode(B=B, H=H, io="bf16", steps=t, seed=302, device=DEV)
     layer = kda.Layer(**dec["layer"])
-    counts = [7, 0, 1, 4, 3, 7]
     ntok = torch.tensor(counts, dtype=torch.int32, device=DEV)
     rows = _rows(dec, t)
     sentinel = torch.full((B, t, H * D), 7.0, dtype=torch.bfloat16, device=DEV)
@@ -148,12 +150,13 @@ def test_zero_tokens_copies_through():
     assert torch.equal(s1, dec["state"]) and torch.equal(r1, dec["ring"])
 
 
+@pytest.mark.parametrize("t", [3, 5])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_multi_softplus_gate_is_bit_identical_to_chained_steps(io):
+def test_multi_softplus_gate_is_bit_identical_to_chained_steps(io, t):
     """The same per-row bit-identity with the unbounded softplus gate (its fast decays make
     the state forget within a few rows, so every row's own arithmetic shows)."""
     kda = _kda()
-    B, H, t = 4, 2, 5
+    B, H = 4, 2
     dec = synthetic.make_decode(B=B, H=H, io=io, steps=t, seed=307, device=DEV)
     dec["layer"]["gate_kind"] = synthetic.GATE_SOFTPLUS
     layer = kda.Layer(**dec["layer"])
