@@ -10,10 +10,11 @@
 // 4*(t%32) .. +3 and key rows (t/32) + 8m, m = 0..15: 64 fp32 of state in registers,
 // loaded and stored 16 bytes at a time (buffer instructions: one offset register) so each
 // wave moves two whole 512-byte rows per access.
-// The first token's prologue (conv, L2 norms, gate, beta) runs while those loads are in
-// flight; the epilogue is the sigmoid-gated RMSNorm over the head's 128 outputs.  State
-// stores are non-temporal: on MI355X that lifts the read+write stream from about 5.0 to
-// about 6.6 TB/s for this kernel (measured), with identical results.
+// The first token's activations and the conv history are loaded right behind the state
+// (vector memory completes in order, so the first prologue starts as the state arrives);
+// the epilogue is the sigmoid-gated RMSNorm over the head's 128 outputs.  State stores
+// are non-temporal: on MI355X that lifts the read+write stream from about 5.0 to about
+// 6.6 TB/s for this kernel (measured), with identical results.
 //
 // Several tokens per launch (the batched verify of speculative decoding, docs.rs
 // "memra_engine::kda" kda_verify_rows_cached): the token loop runs over the
